@@ -1,0 +1,165 @@
+"""Seeded synthetic attention inputs, shared bit-for-bit by the GPU path and the oracle.
+
+This module holds no attention arithmetic: it only draws numbers.  Every tensor is
+a deterministic function of (seed, element index), so any subset of it can be
+regenerated independently of the rest:
+
+* uniform bits: SplitMix64 used as a counter-based generator.  Output n of the
+  stream for ``seed`` is ``mix64(seed + (n + 1) * 0x9E3779B97F4A7C15)`` with the
+  published SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable
+  pseudorandom number generators", OOPSLA 2014; constants as in Vigna's
+  reference code).  This is exactly the sequence the stateful SplitMix64 gives
+  when seeded with ``seed``.
+* normals: Box-Muller on consecutive output pairs (2p, 2p+1), with
+  u = (x >> 11) * 2**-53, r = sqrt(-2 ln(1 - u1)), theta = 2 pi u2,
+  z[2p] = r cos theta, z[2p+1] = r sin theta, evaluated in float64.
+* storage: float64 -> float32 (round to nearest even) -> bfloat16 (round to
+  nearest even on the float32 bit pattern).  Optional multiplier applied in
+  float64 before the float32 rounding (the "x3" peaky-row workload).
+
+Workloads follow the shapes the pages benchmark: d=128, 16 heads, 4K-32K tokens
+(page "AVO算法优化Transformer注意力机制性能解析", section 1 and 4.1), and d=128,
+N=2048, batch 8, 16 heads with MQA and GQA (page "GPU注意力算子性能优化"
+(QiMeng-Attention), section 4.1).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_CHUNK = 1 << 22
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    z = (z ^ (z >> np.uint64(30))) * _M1
+    z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def splitmix64(seed: int, start: int, count: int) -> np.ndarray:
+    """Outputs ``start .. start+count-1`` of the SplitMix64 stream seeded with ``seed``."""
+    n = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + n * GAMMA
+        return _mix64(z)
+
+
+def normal_f64(seed: int, start_pair: int, n_pairs: int) -> np.ndarray:
+    """2*n_pairs standard normals (float64), pairs ``start_pair ..`` of the stream."""
+    x = splitmix64(seed, 2 * start_pair, 2 * n_pairs)
+    u = (x >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    u1 = u[0::2]
+    u2 = u[1::2]
+    r = np.sqrt(-2.0 * np.log1p(-u1))
+    th = (2.0 * math.pi) * u2
+    out = np.empty(2 * n_pairs, dtype=np.float64)
+    out[0::2] = r * np.cos(th)
+    out[1::2] = r * np.sin(th)
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    NaN inputs are not produced by this module and are not handled specially.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 values (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(seed: int, shape, mult: float = 1.0) -> np.ndarray:
+    """bf16 bits of ``bf16(f32(mult * z))`` for iid standard normals z, C-order ``shape``."""
+    total = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(total, dtype=np.uint16)
+    pos = 0
+    while pos < total:
+        cnt = min(_CHUNK, total - pos)
+        # pairs cover elements [pos, pos+cnt); pos is kept even so pairs align.
+        p0 = pos // 2
+        npairs = (cnt + 1) // 2
+        z = normal_f64(seed, p0, npairs)[:cnt]
+        if mult != 1.0:
+            z = z * mult
+        out[pos:pos + cnt] = f32_to_bf16_bits(z.astype(np.float32))
+        pos += cnt
+    return out.reshape(shape)
+
+
+# --------------------------------------------------------------------------
+# Workload catalogue.  Each workload has its own seed block; the Q, K and V
+# tensors use seed_base + 0, + 1 and + 2.
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H_q: int
+    H_kv: int
+    N: int
+    D: int = 128
+    causal: bool = False
+    qk_mult: float = 1.0
+    seed_base: int = 0
+    scale: float = field(default=float(np.float32(1.0 / math.sqrt(128.0))))
+
+    @property
+    def flops(self) -> float:
+        """4*B*H_q*N^2*D, halved for causal (the counting convention of the metric)."""
+        f = 4.0 * self.B * self.H_q * self.N * self.N * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def pairs(self) -> int:
+        """Number of allowed (query, key) pairs, exact."""
+        per_head = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return self.B * self.H_q * per_head
+
+    def shapes(self):
+        return ((self.B, self.H_q, self.N, self.D), (self.B, self.H_kv, self.N, self.D))
+
+    def generate(self):
+        """(q, k, v) as uint16 bf16 bit arrays in [B, H, N, D] layout."""
+        qs, ks = self.shapes()
+        q = normal_bf16(self.seed_base + 0, qs, self.qk_mult)
+        k = normal_bf16(self.seed_base + 1, ks, self.qk_mult)
+        v = normal_bf16(self.seed_base + 2, ks, 1.0)
+        return q, k, v
+
+
+def _sweep(base: int, causal: bool):
+    out = []
+    tag = "causal" if causal else "noncausal"
+    for i, (b, n) in enumerate(((8, 4096), (4, 8192), (2, 16384), (1, 32768))):
+        out.append(Workload(f"mha_{tag}_b{b}_h16_n{n}", b, 16, 16, n, causal=causal,
+                            seed_base=base + 10 * i))
+    return out
+
+
+WORKLOADS = {w.name: w for w in [
+    # tiny MHA, the size the oracle finishes in well under a second
+    Workload("mha_tiny_b1_h2_n256", 1, 2, 2, 256, seed_base=1000),
+    # the pages' mid shape (d=128, N=2048, batch 8, 16 heads): GQA with 8 query
+    # heads per KV head, and MQA
+    Workload("gqa_b8_hq16_hkv2_n2048", 8, 16, 2, 2048, seed_base=2000),
+    Workload("mqa_b8_hq16_hkv1_n2048", 8, 16, 1, 2048, seed_base=2010),
+    # 32768 tokens per step split as (batch, length), 16 heads, both mask modes
+    *_sweep(3000, False),
+    *_sweep(4000, True),
+    # causal long-context MQA with Q and K scaled x3 before rounding: peaky rows
+    Workload("mqa_causal_peaky_b1_hq16_n32768", 1, 16, 1, 32768, causal=True, qk_mult=3.0,
+             seed_base=5000),
+]}
+
+# The headline workload: non-causal MHA, B=2, N=16384, 16 heads, d=128.
+HEADLINE = "mha_noncausal_b2_h16_n16384"

@@ -1,0 +1,60 @@
+"""The seeded input generator (CPU)."""
+import numpy as np
+import torch
+
+import synth
+
+
+def test_splitmix64_published_sequence():
+    # First outputs of SplitMix64 seeded with 0, as produced by the published
+    # reference implementation (Vigna, splitmix64.c).
+    got = [int(x) for x in synth.splitmix64(0, 0, 3)]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_counter_based_slices_agree():
+    full = synth.splitmix64(1234, 0, 100)
+    assert np.array_equal(full[37:61], synth.splitmix64(1234, 37, 24))
+    z = synth.normal_f64(9, 0, 50)
+    assert np.array_equal(z[20:40], synth.normal_f64(9, 10, 10))
+
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.standard_normal(100000).astype(np.float32) * 7,
+                        np.array([1.00390625, 1.01171875, -1.00390625, 3.0e-39, 65504.0,
+                                  1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], np.float32)])
+    mine = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    assert np.array_equal(synth.bf16_bits_to_f32(mine),
+                          torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_normal_statistics_and_determinism():
+    a = synth.normal_bf16(77, (4, 300, 128))
+    b = synth.normal_bf16(77, (4, 300, 128))
+    assert np.array_equal(a, b)
+    f = synth.bf16_bits_to_f32(a).astype(np.float64)
+    assert abs(f.mean()) < 0.01 and abs(f.std() - 1.0) < 0.01
+    assert abs(np.mean(f ** 4) - 3.0) < 0.1          # Gaussian kurtosis
+    c = synth.normal_bf16(78, (4, 300, 128))
+    assert not np.array_equal(a, c)
+
+
+def test_multiplier_applied_before_rounding():
+    z = synth.normal_f64(5, 0, 8)
+    got = synth.bf16_bits_to_f32(synth.normal_bf16(5, (16,), 3.0))
+    want = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((3.0 * z).astype(np.float32)))
+    assert np.array_equal(got, want)
+
+
+def test_workload_catalogue():
+    w = synth.WORKLOADS[synth.HEADLINE]
+    assert (w.B, w.H_q, w.H_kv, w.N, w.D, w.causal) == (2, 16, 16, 16384, 128, False)
+    assert abs(w.flops - 4 * 2 * 16 * 16384 ** 2 * 128) < 1
+    c = synth.WORKLOADS["mha_causal_b2_h16_n16384"]
+    assert c.flops == w.flops / 2
+    assert all(x.H_q % x.H_kv == 0 for x in synth.WORKLOADS.values())
+    seeds = [s for x in synth.WORKLOADS.values() for s in (x.seed_base, x.seed_base + 2)]
+    assert len(set(seeds)) == len(seeds)
