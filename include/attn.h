@@ -1,0 +1,91 @@
+/*
+ * attn.h: C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The operation.  Scaled dot-product attention forward with the log-sum-exp
+ * of every score row:
+ *
+ *     O   = softmax(scale * Q K^T  [+ causal mask]) V
+ *     LSE = ln( sum_j exp(scale * q_i . k_j) )      over the allowed keys j
+ *
+ * as defined on page "GPU注意力算子性能优化" (QiMeng-Attention), section 1
+ * (softmax(Q K^T / sqrt(d_k)) V, scores of shape [batch, heads, seq, seq]) and
+ * page "注意力机制的本质与计算挑战", section 1 (scores, softmax, weighted sum of
+ * V).  The mask is the causal one of page "AVO算法优化Transformer注意力机制性能
+ * 解析", section 2.2: query i sees keys 0..i.  K/V heads are shared by
+ * contiguous groups of query heads (GQA; MQA when H_kv = 1, MHA when
+ * H_kv = H_q), per the QiMeng page, section 3.2.  The score matrix is never
+ * written to memory: scores live in registers and an online softmax merges
+ * key tiles (page "从硬件视角看注意力机制优化", section 2.1; the QiMeng page,
+ * section 3.1.1: local computation plus a global reduction).
+ *
+ * Everything here is plain C: no HIP, torch or vendor bf16 types.  bf16 data
+ * is passed as raw 16-bit storage behind void pointers.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every argument error is reported synchronously, before any
+ * work is enqueued; nothing is launched when the status is not ATTN_OK. */
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,      /* a required pointer is NULL                              */
+    ATTN_ERR_SHAPE = 2,     /* B, H_q, H_kv, N or D <= 0, or a size overflows         */
+    ATTN_ERR_GQA = 3,       /* H_q is not a multiple of H_kv                          */
+    ATTN_ERR_HEAD_DIM = 4,  /* D is not a supported head size (this build: 128)        */
+    ATTN_ERR_SCALE = 5,     /* scale is NaN or infinite                               */
+    ATTN_ERR_ALIGN = 6,     /* a pointer is not 16-byte aligned                        */
+    ATTN_ERR_ALIAS = 7,     /* an output range overlaps an input or the other output   */
+    ATTN_ERR_LAUNCH = 8,    /* the HIP runtime rejected the kernel launch              */
+    ATTN_ERR_DEVICE = 9     /* the current device is not a gfx950 (MI350-series) GPU   */
+} attn_status;
+
+/*
+ * attn_fwd: enqueue the attention forward pass on `stream`.
+ *
+ * q    device pointer, bf16 [B, H_q, N, D], contiguous row-major (D fastest).
+ * k, v device pointers, bf16 [B, H_kv, N, D], contiguous row-major.
+ * o    device pointer, bf16 [B, H_q, N, D], written: O rounded to nearest even.
+ * lse  device pointer, fp32 [B, H_q, N], written: natural-log LSE of each
+ *      score row (scale included, masked keys excluded).  May be NULL when
+ *      the caller does not need it.
+ * B, H_q, H_kv, N, D   sizes; N is both the query and the key length.
+ *      Query head h reads K/V head h / (H_q / H_kv).
+ * causal   0: every query sees all N keys.  Non-zero: query i sees keys 0..i.
+ * scale    multiplies the scores (1/sqrt(D) for the standard attention).
+ * stream   a hipStream_t, or NULL for the default stream of the current
+ *          device.  The pointers must belong to that device.
+ *
+ * Ownership: the caller allocates and frees every buffer; the library keeps no
+ * pointer after the call returns, allocates no memory and keeps no global
+ * state beyond a per-process cache of the device architecture check.  It does
+ * not synchronise: the work runs in stream order and its results are visible
+ * after the caller synchronises with the stream.  o and lse must not overlap
+ * q, k, v or each other.  Results are bitwise reproducible for identical
+ * inputs.  Thread-safe.
+ *
+ * Errors: returns a status code (see above).  A fault inside the kernel (for
+ * example a pointer to too little memory) is reported by the HIP runtime at
+ * the caller's next synchronisation, not by this call.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H_q, int H_kv, int N, int D, int causal, float scale,
+                     void* stream);
+
+/* attn_status_string: a static, human-readable description of a status code. */
+const char* attn_status_string(int status);
+
+/*
+ * attn_fwd_flops: the throughput convention of the benchmarks,
+ * 4 * B * H_q * N^2 * D, halved when causal.  Host-only arithmetic.
+ */
+double attn_fwd_flops(int B, int H_q, int N, int D, int causal);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -25,6 +25,8 @@ N=2048, batch 8, 16 heads with MQA and GQA (page "GPU注意力算子性能优化
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -32,7 +34,7 @@ import numpy as np
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22
+_CHUNK = 1 << 21
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -78,21 +80,38 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _fill(out: np.ndarray, seed: int, pos: int, cnt: int, mult: float) -> None:
+    # pairs cover elements [pos, pos+cnt); chunk starts are even so pairs align.
+    z = normal_f64(seed, pos // 2, (cnt + 1) // 2)[:cnt]
+    if mult != 1.0:
+        z = z * mult
+    out[pos:pos + cnt] = f32_to_bf16_bits(z.astype(np.float32))
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def normal_bf16(seed: int, shape, mult: float = 1.0) -> np.ndarray:
-    """bf16 bits of ``bf16(f32(mult * z))`` for iid standard normals z, C-order ``shape``."""
+    """bf16 bits of ``bf16(f32(mult * z))`` for iid standard normals z, C-order ``shape``.
+
+    Element e is always drawn from stream outputs 2*(e//2) and 2*(e//2)+1, so the
+    result does not depend on how the work is chunked or threaded.
+    """
     total = int(np.prod(shape, dtype=np.int64))
     out = np.empty(total, dtype=np.uint16)
-    pos = 0
-    while pos < total:
-        cnt = min(_CHUNK, total - pos)
-        # pairs cover elements [pos, pos+cnt); pos is kept even so pairs align.
-        p0 = pos // 2
-        npairs = (cnt + 1) // 2
-        z = normal_f64(seed, p0, npairs)[:cnt]
-        if mult != 1.0:
-            z = z * mult
-        out[pos:pos + cnt] = f32_to_bf16_bits(z.astype(np.float32))
-        pos += cnt
+    starts = list(range(0, total, _CHUNK))
+    jobs = [(p, min(_CHUNK, total - p)) for p in starts]
+    if len(jobs) <= 1:
+        for p, c in jobs:
+            _fill(out, seed, p, c, mult)
+    else:
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(lambda j: _fill(out, seed, j[0], j[1], mult), jobs))
     return out.reshape(shape)
 
 

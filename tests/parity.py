@@ -1,0 +1,85 @@
+"""Parity metrics between the GPU output and the fp64 oracle.
+
+The bar (max-abs <= 1e-2, mean-abs <= 1e-3 on O, max-abs <= 1e-3 on LSE, for
+unit-normal inputs) is a stated tolerance for a bf16 output.  Where the exact
+result itself is farther than 1e-2 from every bf16 value (|O| >= 4 has bf16
+spacing 1/32), no bf16 output can meet the max-abs bound; such an element also
+passes when it is one of the two bf16 values bracketing the exact result (a
+faithful rounding).  Mean-abs and LSE bounds apply as stated.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from synth import bf16_bits_to_f32, f32_to_bf16_bits
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+LSE_ABS = 1e-3
+
+
+def _bf16_succ_pred(bits: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """bf16 neighbour of each finite value: toward +inf where ``up`` else toward -inf."""
+    b = bits.astype(np.int32)
+    neg = (b & 0x8000) != 0
+    mag = b & 0x7FFF
+    # moving away from zero increments the magnitude; toward zero decrements it
+    away = np.where(neg, ~up, up)
+    mag2 = np.where(away, mag + 1, np.where(mag == 0, 1, mag - 1))
+    sign = np.where(mag == 0, np.where(up, 0, 0x8000), b & 0x8000)
+    return (sign | mag2).astype(np.uint16)
+
+
+def faithful(o: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """True where the float o equals one of the two bf16 values bracketing ref."""
+    ref = np.asarray(ref, dtype=np.float64)
+    b = f32_to_bf16_bits(ref.astype(np.float32))
+    vb = bf16_bits_to_f32(b).astype(np.float64)
+    other = bf16_bits_to_f32(_bf16_succ_pred(b, vb <= ref)).astype(np.float64)
+    return (o == vb) | (o == other)
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref):
+    """Metrics dict for the GPU output (any float array) against the oracle (float64)."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    err = np.abs(o_gpu - o_ref)
+    floor = np.abs(bf16_bits_to_f32(f32_to_bf16_bits(o_ref.astype(np.float32))) - o_ref)
+    over = err > MAX_ABS
+    unfaithful_over = over & ~faithful(o_gpu, o_ref) if over.any() else over
+    m = {
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "mean_abs": float(err.mean()) if err.size else 0.0,
+        "floor_max_abs": float(floor.max()) if floor.size else 0.0,
+        "floor_mean_abs": float(floor.mean()) if floor.size else 0.0,
+        "n_over_max_abs": int(over.sum()),
+        "n_over_not_faithful": int(unfaithful_over.sum()),
+        "finite": bool(np.all(np.isfinite(o_gpu))),
+    }
+    if lse_gpu is not None:
+        le = np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref)
+        m["lse_max_abs"] = float(le.max()) if le.size else 0.0
+        m["lse_finite"] = bool(np.all(np.isfinite(lse_gpu)))
+    return m
+
+
+def check(m, what=""):
+    assert m["finite"], f"{what}: non-finite output {m}"
+    assert m["n_over_not_faithful"] == 0, f"{what}: max-abs {m}"
+    assert m["mean_abs"] <= MEAN_ABS, f"{what}: mean-abs {m}"
+    if "lse_max_abs" in m:
+        assert m["lse_finite"] and m["lse_max_abs"] <= LSE_ABS, f"{what}: LSE {m}"
+
+
+def sample_rows(B, Hq, N, rng, per_head=24, tile=128, heads=None):
+    """Flat row ids ((b*Hq + h)*N + i) covering the first and last rows, query-tile
+    edges and random rows of each (b, h) (or of the given list of (b, h))."""
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    out = []
+    edges = sorted({0, 1, N - 1, N - 2} | {min(N - 1, t + d) for t in range(tile, N, tile * 37)
+                                           for d in (-1, 0)})
+    for b, h in pairs:
+        base = (b * Hq + h) * N
+        rows = set(x for x in edges if 0 <= x < N)
+        rows |= set(int(x) for x in rng.integers(0, N, per_head))
+        out.extend(base + r for r in sorted(rows))
+    return np.array(out, dtype=np.int64)
