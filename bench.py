@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one attn_fwd launch over the headline workload: non-causal MHA,
+B=2, N=16384, 16 heads, d=128, bf16 inputs (seeded synthetic N(0,1) data
+already resident in HBM).  Prints ONE JSON line on stdout:
+TFLOPS = 4*B*H*N^2*D / time (halved for causal), with the roofline of the
+kernel and the oracle's CPU rate on a bounded sample as a reported baseline.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
+                  [--no-cpu-baseline]
+
+``--sweep`` also times every workload of the catalogue and prints a table on
+stderr (stdout stays one JSON line).  Only one GPU is supported: --gpus > 1
+exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "attention fwd TFLOPS (bf16, d=128) and % of MI355X dense BF16 MFMA peak"
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU (v_mfma 32x32x16 bf16:
+# 32768 flop per 32 clocks per SIMD, 4 SIMDs) x 2.4 GHz = 2516.6 TFLOP/s.
+PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_17_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"hbm_traffic_attn_fwd_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.lstrip().startswith("#"):
+                key, val = ln.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def upload(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_workload(w, steps, warmup):
+    """Returns (ms_per_step wall, mean launch ms from HIP events, per-launch list)."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    q, k, v = w.generate()
+    qg, kg, vg = upload(q), upload(k), upload(v)
+    del q, k, v
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=qg.device)
+    for _ in range(warmup):
+        sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE in the benchmark output"
+    del qg, kg, vg, o, lse
+    torch.cuda.empty_cache()
+    return wall * 1e3 / steps, float(np.mean(per)), per
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of
+    query rows of the same workload; rate in the metric's unit (TFLOPS)."""
+    import oracle
+    oracle.build(force=False)
+    q, k, v = w.generate()
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(1)
+    total_rows = w.B * w.H_q * w.N
+
+    def run(n):
+        rows = np.sort(rng.choice(total_rows, n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_ref(q, k, v, w.causal, w.scale, rows=rows, n_threads=threads)
+        dt = time.perf_counter() - t0
+        i = rows % w.N
+        keys = (i + 1) if w.causal else np.full(n, w.N)
+        return dt, float(keys.sum()) * 4 * w.D   # 4*D flops per allowed pair
+    n0 = max(threads, 32)
+    dt, fl = run(n0)
+    n = int(min(total_rows, max(n0, n0 * target_s / max(dt, 1e-3))))
+    dt, fl = run(n)
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{n} random query rows of {w.name} (all {w.N} keys each, fp64), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path (the heads of a "
+              "step shard across GPUs with no exchange; run one process per GPU)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    sdpa.load()
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} D={w.D} causal={w.causal}")
+    ms_step, ms_launch, per = time_workload(w, args.steps, args.warmup)
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    achieved = w.flops / (ms_launch * 1e-3) / 1e12
+    log(f"[bench] {ms_step:.3f} ms/step wall, {ms_launch:.3f} ms/launch (events), "
+        f"{tflops:.1f} TFLOPS = {100 * tflops / PEAK_TFLOPS:.1f}% of peak")
+
+    traffic = stored_traffic(w.name)
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, SplitMix64 + Box-Muller)",
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N": w.N,
+                   "D": w.D, "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_kernel",
+                     "launch_ms_mean": round(ms_launch, 4),
+                     "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
+                                           round(float(np.percentile(per, 90)), 4)]},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        log(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}")
+        for name, x in synth.WORKLOADS.items():
+            _, ms, _ = time_workload(x, max(5, args.steps // 5), 3)
+            tf = x.flops / (ms * 1e-3) / 1e12
+            log(f"{name:36s} {ms:9.3f} {tf:9.1f} {100 * tf / PEAK_TFLOPS:7.1f}")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
