@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "known-size reference for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path (the heads of a "
@@ -148,6 +151,17 @@ def main():
     import scaled_dot_product_17_amd as sdpa
     if not torch.cuda.is_available():
         sys.exit("no GPU visible")
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for i in range(3):
+            t0 = time.perf_counter()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"[copy] {args.calibrate_copy} MiB copy {i}: {(time.perf_counter() - t0) * 1e3:.3f} ms")
+        return
     sdpa.load()
 
     w = synth.WORKLOADS[args.workload]

@@ -9,14 +9,17 @@
 //   * "local computation + global reduction" and the shared K/V of a GQA
 //     group: the QiMeng page, sections 3.1.1 and 3.2;
 //   * scale folded into the score stage, max-subtracted softmax, mask fused
-//     into the softmax, double-buffered tile staging: page
-//     "AVO算法优化Transformer注意力机制性能解析", sections 2.2, 3.1, 3.2, 5.1.
+//     into the softmax, double-buffered tile staging and look-ahead prefetch:
+//     page "AVO算法优化Transformer注意力机制性能解析", sections 2.2, 3.1, 3.2, 5.1.
 //
 // Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
 //   * each wave owns 32 query rows; its Q rows live in VGPRs as the B operand
 //     of v_mfma_f32_32x32x16_bf16 for the whole kernel;
-//   * key tiles of 64 rows of K and V are staged HBM -> VGPR -> LDS, double
-//     buffered, one barrier per tile;
+//   * key tiles of 64 rows of K and V are copied HBM -> LDS by the buffer
+//     unit's LDS DMA (no VGPR staging).  K runs one tile ahead of V: while a
+//     wave turns the scores of tile j into probabilities and multiplies them
+//     into V_j, the MFMAs of the scores of tile j+1 are already in flight, so
+//     the softmax VALU work overlaps matrix-core work inside every wave;
 //   * scores are computed transposed, S^T = K Q^T, so each lane owns one query
 //     column: the row max and row sum are in-lane reductions plus one
 //     permlane32 swap, and the output rescale is a per-lane scalar;
@@ -25,15 +28,18 @@
 //     accumulator holds them; V^T fragments are read in the same key order with
 //     the gfx950 transposing LDS read (ds_read_b64_tr_b16), so V never needs a
 //     transposed copy;
-//   * softmax in base 2: p = exp2(s * scale*log2(e) - m * scale*log2(e)).  The
-//     running max is exact (O and l are rescaled whenever any row's max grows);
-//     a wave skips the rescale when no row's max grew.
+//   * softmax in base 2 against a reference max m: p = exp2(s*c - m*c) with
+//     c = scale*log2(e).  The reference only moves (rescaling O and l) when a
+//     row's max exceeds it by more than 2^8 in p; otherwise p <= 256, which
+//     fp32 accumulation absorbs.  The final O / l and LSE = m*scale + ln(l) are
+//     the same quantities whichever reference was used.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -41,19 +47,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
 constexpr int BR = 128;                    // query rows per workgroup
-constexpr int BC = 64;                     // keys per tile
+constexpr int BC = 64;                     // keys per tile (one LDS refill, one barrier)
 constexpr int NWAVE = 4;                   // waves per workgroup
 constexpr int NTHREAD = NWAVE * 64;
 constexpr int ROW_BYTES = HD * 2;          // 256 B per K/V/Q/O row
-constexpr int TILE_BYTES = BC * ROW_BYTES; // 16 KiB per K or V tile
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES; // two stages of K and V: 64 KiB
+constexpr int KB = 32;                     // keys per pipeline step (one MFMA M block)
+constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB per K or V block
+constexpr int K_RING = 0;                  // LDS: a ring of 4 K blocks, then 4 V blocks
+constexpr int V_RING = 4 * BLK_BYTES;
+constexpr int LDS_BYTES = 8 * BLK_BYTES;   // 64 KiB
+constexpr float RESCALE_LOG2 = 8.0f;       // reference max moves when p would exceed 2^8
 constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
 
 struct Params {
@@ -76,18 +87,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              (int)RSRC_DWORD3);
 }
 
-// 16-byte buffer load; offsets at or beyond the range return zeros.
+// 16-byte buffer load into VGPRs; offsets at or beyond the range return zeros.
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// LDS byte address of the 16-byte chunk (row, chunk) of a K tile.  The chunk
+// LDS byte offset of the 16-byte chunk (row, chunk) of a K tile.  The chunk
 // index is XOR-swizzled with the low 4 row bits so the 32 rows one MFMA A
-// operand touches (same logical chunk) fall in distinct banks.
+// operand read touches (same logical chunk) fall in distinct banks.
 __device__ __forceinline__ uint32_t k_lds_off(int row, int chunk) {
     return (uint32_t)(row * ROW_BYTES + ((chunk ^ (row & 15)) << 4));
 }
-// LDS byte address of the 16-byte chunk (row, chunk) of a V tile.  The chunk
+// LDS byte offset of the 16-byte chunk (row, chunk) of a V tile.  The chunk
 // index is XOR-swizzled with 4*(row mod 4): a transposing read touches 4
 // consecutive rows x 64 contiguous bytes per half-wave, and this spreads the
 // four rows over the four 64-byte bank groups.
@@ -123,13 +134,34 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return start + s;
 }
 
+// LDS DMA of one 16-byte chunk per lane: the buffer unit copies
+// rsrc[voff .. voff+15] to LDS byte lds_addr + 16*lane, without passing
+// through VGPRs.  Out-of-range offsets read as zeros.  Issued as inline
+// assembly so that the compiler does not order later LDS reads behind it; the
+// caller waits for completion (vmcnt) before the workgroup barrier that
+// publishes the data.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Raw buffer descriptor in SGPRs for inline assembly.
+__device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;   // query column owned by this lane
     const int hh = lane >> 5;    // which half of the wave
 
@@ -146,18 +178,84 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     const int wq0 = q0 + wave * 32;       // first query row of this wave
     const int myq = wq0 + l32;            // query row of this lane
 
-    const uint32_t panel_bytes = (uint32_t)N * ROW_BYTES;
     const size_t qo_panel = ((size_t)b * p.Hq + h) * (size_t)N * HD;
     const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + qo_panel, panel_bytes);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_panel, panel_bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_panel, panel_bytes);
+    const uint16_t* kbase = p.k + kv_panel;
+    const uint16_t* vbase = p.v + kv_panel;
 
-    // ---- Q fragments: B operand of S^T = K Q^T, k-steps of 16 head dims
-    bf16x8 qf[8];
+    // ---- key blocks of 32: n_blk_wg streamed through LDS, n_blk used by this wave.
+    // Causal: a wave's 32 rows start on a block boundary, so every block before
+    // its diagonal block is fully visible and only its last block is masked.
+    const int n_blk_all = (N + KB - 1) / KB;
+    int n_blk_wg = n_blk_all, n_blk = n_blk_all;
+    if (CAUSAL) {
+        n_blk_wg = min(n_blk_all, (min(q0 + BR, N) - 1) / KB + 1);
+        n_blk = min(n_blk_all, wq0 / KB + 1);
+    }
+    if (wq0 >= N) n_blk = 0;   // a wave of padding rows past the end computes nothing
+
+    // ---- LDS rings: K block g lives in slot g % 4 of the K ring, V block g in
+    // slot g % 4 of the V ring.  Each wave copies rows 8*wave .. 8*wave+7 of a
+    // block with two DMA instructions of 4 rows (1 KiB, 16 bytes per lane in
+    // lane order).  The bank swizzle is applied on the global side: lane L
+    // fetches the logical chunk that belongs at its physical LDS position.
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    uint32_t k_dma[2], v_dma[2];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, (uint32_t)myq * ROW_BYTES + (16 * ks + 8 * hh) * 2));
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * wave + 4 * i + (lane >> 4);
+        const int pc = lane & 15;
+        k_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ (row & 15)) << 4));
+        v_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ ((row & 3) << 2)) << 4));
+    }
+    auto dma_block = [&](const uint16_t* panel, const uint32_t* voff, int ring, int g) {
+        if (g < n_blk_wg) {
+            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW_BYTES);
+            const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 8 * wave * ROW_BYTES;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
+        }
+    };
+
+    // ---- per-lane LDS read offsets (relative to a block slot)
+    uint32_t k_rd[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) k_rd[ks] = k_lds_off(l32, 2 * ks + hh);
+    uint32_t v_rd[4];
+    {
+        const int g = lane >> 4;          // 16-lane group
+        const int rs = (lane & 15) >> 2;  // source row within the 4-row block
+        const int cs = lane & 3;          // source 4-element column block
+        const int row = 4 * (g >> 1) + rs;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int col = 32 * db + 16 * (g & 1) + 4 * cs;  // element column
+            v_rd[db] = v_lds_off(row, col >> 3) + ((col & 4) ? 8 : 0);
+        }
+    }
+
+    // ---- prologue: K blocks 0-2 and V blocks 0-1 in flight, then Q into VGPRs
+    if (N % KB != 0) {
+        // rows past N of the tail block must read as zeros, not stale LDS
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < LDS_BYTES / (16 * NTHREAD); ++i)
+            *(u32x4*)(lds + 16 * (tid + NTHREAD * i)) = z;
+        __syncthreads();
+    }
+    dma_block(kbase, k_dma, K_RING, 0);
+    dma_block(vbase, v_dma, V_RING, 0);
+    dma_block(kbase, k_dma, K_RING, 1);
+    dma_block(vbase, v_dma, V_RING, 1);
+    dma_block(kbase, k_dma, K_RING, 2);
+
+    bf16x8 qf[8];   // B operand of S^T = K Q^T, k-steps of 16 head dims
+    {
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + qo_panel, (uint32_t)N * ROW_BYTES);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, (uint32_t)myq * ROW_BYTES + (16 * ks + 8 * hh) * 2));
+    }
     // A negative scale is applied as |scale| on -Q (a sign flip is exact in
     // bf16) and a zero scale as zero scores, so the exp2 argument below always
     // multiplies by a positive constant and masked -inf scores stay -inf.
@@ -169,153 +267,158 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         for (int ks = 0; ks < 8; ++ks)
             qf[ks] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, qf[ks]) & keep) ^ flip);
     }
-
-    // ---- number of key tiles this workgroup visits
-    const int n_ktiles_all = (N + BC - 1) / BC;
-    int n_kt = n_ktiles_all;
-    if (CAUSAL) {
-        const int last_q = min(q0 + BR, N) - 1;
-        n_kt = min(n_ktiles_all, last_q / BC + 1);
-    }
-
-    // ---- per-thread staging coordinates: 4 rows x one 16-byte chunk of each tile
-    const int st_row = tid >> 4;   // 0..15, plus 16*it
-    const int st_chunk = tid & 15;
-    uint32_t k_st_off[4], v_st_off[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        k_st_off[it] = k_lds_off(st_row + 16 * it, st_chunk);
-        v_st_off[it] = TILE_BYTES + v_lds_off(st_row + 16 * it, st_chunk);
-    }
-
-    // ---- per-lane LDS read addresses (stage 0; stage 1 adds STAGE_BYTES)
-    uint32_t k_rd[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) k_rd[ks] = k_lds_off(l32, 2 * ks + hh);
-    uint32_t v_rd[4];
-    {
-        const int g = lane >> 4;        // 16-lane group
-        const int rs = (lane & 15) >> 2;  // source row within the 4-row block
-        const int cs = lane & 3;          // source 4-element column block
-        const int row = 4 * (g >> 1) + rs;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int col = 32 * db + 16 * (g & 1) + 4 * cs;  // element column
-            v_rd[db] = TILE_BYTES + v_lds_off(row, col >> 3) + ((col & 4) ? 8 : 0);
-        }
-    }
-
-    u32x4 kst[4], vst[4];
-    auto load_tile = [&](int j) {
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const uint32_t goff = (uint32_t)(j * BC + st_row + 16 * it) * ROW_BYTES + st_chunk * 16;
-            kst[it] = buf_load16(kr, goff);
-            vst[it] = buf_load16(vr, goff);
-        }
-    };
-    auto store_tile = [&](int stage) {
-        char* base = lds + stage * STAGE_BYTES;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            *(u32x4*)(base + k_st_off[it]) = kst[it];
-            *(u32x4*)(base + v_st_off[it]) = vst[it];
-        }
-    };
-
-    f32x16 oacc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;   // running max of raw scores (exact)
-    float l_run = 0.f;         // this lane's partial row sum
     const float c = p.c;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // S^T of one 32-key block, from a K ring slot
+    auto scores = [&](f32x16& s, uint32_t kslot) {
+        s = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 a = *(const bf16x8*)(lds + kslot + k_rd[ks]);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+        }
+    };
+    // key >= N (ragged tail) or key > query (causal) -> -inf
+    auto needs_mask = [&](int g) {
+        return (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
+    };
+    auto apply_mask = [&](f32x16& s, int g) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = g * KB + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool bad = (key >= N) || (CAUSAL && key > myq);
+            s[r] = bad ? -INFINITY : s[r];
+        }
+    };
+    auto row_max = [&](const f32x16& s) {
+        float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return wave_swap_max(mx);
+    };
 
-    for (int j = 0; j < n_kt; ++j) {
-        const int stage = j & 1;
-        if (j + 1 < n_kt) load_tile(j + 1);
-        const char* sb = lds + stage * STAGE_BYTES;
-        const int key0 = j * BC;
-        // causal: a tile whose first key is past this wave's last query is skipped
-        const bool active = !CAUSAL || key0 <= wq0 + 31;
-        if (active) {
-            // ---- S^T = K Q^T for keys key0..key0+63 (two 32-key blocks)
-            f32x16 sacc[2];
+    f32x16 o[4];          // O^T: 4 blocks of 32 head dims x 32 query columns
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sacc[kb] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 a = *(const bf16x8*)(sb + k_rd[ks] + kb * 32 * ROW_BYTES);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
-                }
-            }
-            // ---- mask: key > query (causal) or key >= N (ragged tail)
-            const bool need_mask = (CAUSAL && key0 + BC - 1 > wq0) || (key0 + BC > N);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const bool bad = (key >= N) || (CAUSAL && key > myq);
-                        sacc[kb][r] = bad ? -INFINITY : sacc[kb][r];
-                    }
-            }
-            // ---- online softmax
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-            mx = wave_swap_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const bool grew = m_new > m_run;
-            if (__builtin_amdgcn_ballot_w64(grew)) {
-                const float alpha = grew ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                m_run = m_new;
-            }
-            const float mb = (m_run == -INFINITY) ? 0.f : m_run * c;
-            bf16x8 pf[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * kk + i], c, -mb));
-                        l_run += e;
-                        pf[kb][kk][i] = (__bf16)e;
-                    }
-            // ---- O^T += V^T P^T; the MFMA k index walks keys in accumulator order
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    float m = -INFINITY;  // reference max of the raw scores q.k of this lane's row
+    float mb = 0.f;       // m * c, or 0 while m is -inf
+    float l = 0.f;        // this lane's partial sum of p (fp32): the LSE
+    float lb = 0.f;       // partial sum of bf16(p), the weights the PV MFMA applies: O's divisor
+
+    // Moves the reference max of rows whose max grew by more than 2^RESCALE_LOG2
+    // in p, rescaling O and l.  Wave-uniform branch, rarely taken.
+    auto update_ref = [&](float mx) {
+        const float m_new = fmaxf(m, mx);
+        const bool move = (m_new - m) * c > RESCALE_LOG2;   // false for NaN (-inf - -inf)
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float alpha = move ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
+            l *= alpha;
+            lb *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const uint32_t rowoff = (uint32_t)(32 * kb + 16 * kk) * ROW_BYTES;
-                        const bf16x4 lo = lds_read_tr(sb, v_rd[db] + rowoff);
-                        const bf16x4 hi = lds_read_tr(sb, v_rd[db] + rowoff + 8 * ROW_BYTES);
-                        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][kk], oacc[db], 0, 0, 0);
-                    }
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m = move ? m_new : m;
+            mb = (m == -INFINITY) ? 0.f : m * c;
         }
-        if (j + 1 < n_kt) store_tile(stage ^ 1);
+    };
+
+    f32x16 sa, sb;   // scores of even / odd key blocks
+    // vmcnt(0) through the builtin, so the compiler also knows the Q loads are
+    // complete and never waits on vmcnt (which counts the DMA) inside the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (n_blk > 0) {
+        scores(sa, K_RING);
+        if (needs_mask(0)) apply_mask(sa, 0);
+        const float mx = row_max(sa);
+        m = mx;
+        mb = (mx == -INFINITY) ? 0.f : mx * c;
+    }
+    __syncthreads();   // K slot 0 is refilled in the first iteration
+
+    // Key block g: P_g from s, O += V_g^T P_g^T, and the scores sn of block
+    // g+1, issued first so they run on the matrix core meanwhile.  For the
+    // wave's last block sn is computed from whatever the slot holds and never
+    // used.
+    auto block = [&](auto kslot_t, auto vslot_t, int g, f32x16& s, f32x16& sn) {
+        constexpr uint32_t KSLOT = K_RING + decltype(kslot_t)::value * BLK_BYTES;
+        constexpr uint32_t VSLOT = V_RING + decltype(vslot_t)::value * BLK_BYTES;
+        if (g >= n_blk) return;
+        scores(sn, KSLOT);
+        // ---- P_g = exp2(s*c - m*c): bf16 B operand of the PV MFMA, fp32 row sum
+        // ---- P_g = exp2(s*c - m*c), rounded to bf16 in pairs: the B operand of
+        // the PV MFMA.  l sums the fp32 p; lb sums the bf16 pairs with v_dot2
+        // against (1, 1).
+        u32x4 pw[2];
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        float ls0 = 0.f, ls1 = 0.f, lb0 = lb, lb1 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + 2 * i], c, -mb));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + 2 * i + 1], c, -mb));
+                ls0 += e0;
+                ls1 += e1;
+                const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+                if (i & 1) lb1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lb1, false);
+                else lb0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lb0, false);
+                pw[kk][i] = __builtin_bit_cast(uint32_t, pr);
+            }
+        l += ls0 + ls1;
+        lb = lb0 + lb1;
+        const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
+        // ---- O^T += V_g^T P_g^T; the MFMA k index walks keys in accumulator order
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const uint32_t off = VSLOT + v_rd[db] + (uint32_t)(16 * kk) * ROW_BYTES;
+                const bf16x4 lo = lds_read_tr(lds, off);
+                const bf16x4 hi = lds_read_tr(lds, off + 8 * ROW_BYTES);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[db], 0, 0, 0);
+            }
+        if (g + 1 < n_blk) {
+            if (needs_mask(g + 1)) apply_mask(sn, g + 1);
+            update_ref(row_max(sn));
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    // Tile loop: tile j = blocks 2j and 2j+1.  During tile j the workgroup
+    // reads K blocks 2j+1, 2j+2 and V blocks 2j, 2j+1, and refills K blocks
+    // 2j+3, 2j+4 and V blocks 2j+2, 2j+3 into the slots freed by tile j-1.
+    const int n_tiles = (n_blk_wg + 1) / 2;
+    for (int j = 0; j < n_tiles; j += 2) {
+        dma_block(kbase, k_dma, K_RING, 2 * j + 3);
+        dma_block(kbase, k_dma, K_RING, 2 * j + 4);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 2);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 3);
+        block(I1{}, I0{}, 2 * j, sa, sb);
+        block(I2{}, I1{}, 2 * j + 1, sb, sa);
+        wait_dma();
+        __syncthreads();
+        if (j + 1 >= n_tiles) break;
+        dma_block(kbase, k_dma, K_RING, 2 * j + 5);
+        dma_block(kbase, k_dma, K_RING, 2 * j + 6);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 4);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 5);
+        block(I3{}, I2{}, 2 * j + 2, sa, sb);
+        block(I0{}, I3{}, 2 * j + 3, sb, sa);
+        wait_dma();
         __syncthreads();
     }
 
-    // ---- epilogue: O = O^T / l (bf16, round to nearest even), LSE = m*scale + ln l
-    const float l_tot = wave_swap_sum(l_run);
-    const float inv = 1.0f / l_tot;
+    // ---- epilogue: O = O^T / sum bf16(p) (bf16, round to nearest even),
+    // LSE = m*scale + ln(sum p).  Dividing by the sum of the weights the MFMA
+    // actually applied makes the rounding of a dominant weight cancel.
+    const float l_tot = wave_swap_sum(l);
+    const float inv = 1.0f / wave_swap_sum(lb);
     if (myq < N) {
         uint16_t* orow = p.o + qo_panel + (size_t)myq * HD;
 #pragma unroll
@@ -324,12 +427,12 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
             for (int r4 = 0; r4 < 4; ++r4) {
                 bf16x4 ov;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][4 * r4 + i] * inv);
+                for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[db][4 * r4 + i] * inv);
                 *(bf16x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = ov;
             }
         if (p.lse != nullptr && hh == 0) {
             const size_t li = ((size_t)b * p.Hq + h) * (size_t)N + myq;
-            p.lse[li] = m_run * p.lse_scale + logf(l_tot);
+            p.lse[li] = m * p.lse_scale + logf(l_tot);
         }
     }
 }
