@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         }
     }
 
-    // ---- prologue: K blocks 0-2 and V blocks 0-1 in flight, then Q into VGPRs
+    // ---- prologue: K blocks 0-2 and V block 0 in flight, then Q into VGPRs
     if (N % KB != 0) {
         // rows past N of the tail block must read as zeros, not stale LDS
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -246,7 +246,6 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     dma_block(kbase, k_dma, K_RING, 0);
     dma_block(vbase, v_dma, V_RING, 0);
     dma_block(kbase, k_dma, K_RING, 1);
-    dma_block(vbase, v_dma, V_RING, 1);
     dma_block(kbase, k_dma, K_RING, 2);
 
     bf16x8 qf[8];   // B operand of S^T = K Q^T, k-steps of 16 head dims
@@ -290,12 +289,6 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
             s[r] = bad ? -INFINITY : s[r];
         }
     };
-    auto row_max = [&](const f32x16& s) {
-        float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        return wave_swap_max(mx);
-    };
 
     f32x16 o[4];          // O^T: 4 blocks of 32 head dims x 32 query columns
 #pragma unroll
@@ -305,54 +298,26 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     float l = 0.f;        // this lane's partial sum of p (fp32): the LSE
     float lb = 0.f;       // partial sum of bf16(p), the weights the PV MFMA applies: O's divisor
 
-    // Moves the reference max of rows whose max grew by more than 2^RESCALE_LOG2
-    // in p, rescaling O and l.  Wave-uniform branch, rarely taken.
-    auto update_ref = [&](float mx) {
-        const float m_new = fmaxf(m, mx);
-        const bool move = (m_new - m) * c > RESCALE_LOG2;   // false for NaN (-inf - -inf)
-        if (__builtin_amdgcn_ballot_w64(move)) {
-            const float alpha = move ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
-            l *= alpha;
-            lb *= alpha;
+    // O^T += V^T P^T for one block; the MFMA k index walks keys in the order
+    // the score accumulator holds them (P was built from it lane by lane).
+    auto pv = [&](const u32x4 (&pw)[2], uint32_t vslot) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-            m = move ? m_new : m;
-            mb = (m == -INFINITY) ? 0.f : m * c;
-        }
+            for (int db = 0; db < 4; ++db) {
+                const uint32_t off = vslot + v_rd[db] + (uint32_t)(16 * kk) * ROW_BYTES;
+                const bf16x4 lo = lds_read_tr(lds, off);
+                const bf16x4 hi = lds_read_tr(lds, off + 8 * ROW_BYTES);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pw[kk]),
+                                                                o[db], 0, 0, 0);
+            }
     };
-
-    f32x16 sa, sb;   // scores of even / odd key blocks
-    // vmcnt(0) through the builtin, so the compiler also knows the Q loads are
-    // complete and never waits on vmcnt (which counts the DMA) inside the loop
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (n_blk > 0) {
-        scores(sa, K_RING);
-        if (needs_mask(0)) apply_mask(sa, 0);
-        const float mx = row_max(sa);
-        m = mx;
-        mb = (mx == -INFINITY) ? 0.f : mx * c;
-    }
-    __syncthreads();   // K slot 0 is refilled in the first iteration
-
-    // Key block g: P_g from s, O += V_g^T P_g^T, and the scores sn of block
-    // g+1, issued first so they run on the matrix core meanwhile.  For the
-    // wave's last block sn is computed from whatever the slot holds and never
-    // used.
-    auto block = [&](auto kslot_t, auto vslot_t, int g, f32x16& s, f32x16& sn) {
-        constexpr uint32_t KSLOT = K_RING + decltype(kslot_t)::value * BLK_BYTES;
-        constexpr uint32_t VSLOT = V_RING + decltype(vslot_t)::value * BLK_BYTES;
-        if (g >= n_blk) return;
-        scores(sn, KSLOT);
-        // ---- P_g = exp2(s*c - m*c): bf16 B operand of the PV MFMA, fp32 row sum
-        // ---- P_g = exp2(s*c - m*c), rounded to bf16 in pairs: the B operand of
-        // the PV MFMA.  l sums the fp32 p; lb sums the bf16 pairs with v_dot2
-        // against (1, 1).
-        u32x4 pw[2];
+    // P = exp2(s*c - mb) rounded to bf16 in pairs (the B operand of the PV
+    // MFMA); ls sums the fp32 p, lbs the bf16 pairs (v_dot2 against (1, 1)).
+    auto probs = [&](const f32x16& s, u32x4 (&pw)[2], float& ls, float& lbs) {
         const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-        float ls0 = 0.f, ls1 = 0.f, lb0 = lb, lb1 = 0.f;
+        float ls0 = 0.f, ls1 = 0.f, lb0 = 0.f, lb1 = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -366,50 +331,98 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
                 else lb0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lb0, false);
                 pw[kk][i] = __builtin_bit_cast(uint32_t, pr);
             }
-        l += ls0 + ls1;
-        lb = lb0 + lb1;
-        const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
-        // ---- O^T += V_g^T P_g^T; the MFMA k index walks keys in accumulator order
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint32_t off = VSLOT + v_rd[db] + (uint32_t)(16 * kk) * ROW_BYTES;
-                const bf16x4 lo = lds_read_tr(lds, off);
-                const bf16x4 hi = lds_read_tr(lds, off + 8 * ROW_BYTES);
-                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[db], 0, 0, 0);
-            }
-        if (g + 1 < n_blk) {
-            if (needs_mask(g + 1)) apply_mask(sn, g + 1);
-            update_ref(row_max(sn));
-        }
+        ls = ls0 + ls1;
+        lbs = lb0 + lb1;
     };
+
+    // Key block g (valid while g < n_blk; g == n_blk only drains the last PV).
+    // Issued together, with no dependence on this block's softmax:
+    //   * the scores sn of block g+1 (K ring slot KS),
+    //   * O += V_{g-1}^T P_{g-1}^T for the previous block (V ring slot VS),
+    // while the VALU turns the scores s of block g into P_g against the current
+    // reference.  If a row's max moved by more than 2^RESCALE_LOG2 in p (rare,
+    // wave-uniform branch) the reference moves, O and the sums are rescaled
+    // once the previous PV has landed, and P_g is recomputed.
+    auto step = [&](auto first_t, auto ks_t, auto vs_t, int g, f32x16& s, f32x16& sn,
+                    const u32x4 (&pp)[2], u32x4 (&pc)[2]) {
+        constexpr bool FIRST = decltype(first_t)::value;
+        constexpr uint32_t KS = K_RING + decltype(ks_t)::value * BLK_BYTES;
+        constexpr uint32_t VS = V_RING + decltype(vs_t)::value * BLK_BYTES;
+        const bool valid = g < n_blk;
+        if (valid && needs_mask(g)) apply_mask(s, g);
+        scores(sn, KS);
+        if constexpr (!FIRST) pv(pp, VS);
+        float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = wave_swap_max(mx);
+        float ls, lbs;
+        probs(s, pc, ls, lbs);
+        // keep P_g ahead of the branch below (not sunk into its fall-through
+        // path), so its VALU work interleaves with the MFMAs issued above
+        asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(ls), "+v"(lbs));
+        const float m_new = fmaxf(m, mx);
+        const bool move = valid && (m_new - m) * c > RESCALE_LOG2;  // false for NaN
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float alpha = move ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
+            m = move ? m_new : m;
+            mb = (m == -INFINITY) ? 0.f : m * c;
+            l *= alpha;
+            lb *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            probs(s, pc, ls, lbs);
+        }
+        l += valid ? ls : 0.f;
+        lb += valid ? lbs : 0.f;
+    };
+
+    f32x16 sa, sb;    // scores of even / odd key blocks
+    u32x4 pa[2], pb[2];  // bf16 P of even / odd key blocks
+    // vmcnt(0) through the builtin, so the compiler also knows the Q loads are
+    // complete and never waits on vmcnt (which counts the DMA) inside the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (n_blk > 0) scores(sa, K_RING);
+    __syncthreads();   // K slot 0 is refilled in the first tile
+
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+    using F = std::false_type;
 
-    // Tile loop: tile j = blocks 2j and 2j+1.  During tile j the workgroup
-    // reads K blocks 2j+1, 2j+2 and V blocks 2j, 2j+1, and refills K blocks
-    // 2j+3, 2j+4 and V blocks 2j+2, 2j+3 into the slots freed by tile j-1.
-    const int n_tiles = (n_blk_wg + 1) / 2;
-    for (int j = 0; j < n_tiles; j += 2) {
+    // Tile j = steps 2j and 2j+1.  Step g reads K block g+1 (slot (g+1)%4) and
+    // V block g-1 (slot (g-1)%4), so during tile j the workgroup refills K
+    // blocks 2j+3, 2j+4 and V blocks 2j+1, 2j+2 into slots freed by tile j-1.
+    // The loop runs one step past the last block so every wave drains its PV.
+    const int n_tiles = n_blk_wg / 2 + 1;
+    auto refill = [&](int j) {
         dma_block(kbase, k_dma, K_RING, 2 * j + 3);
         dma_block(kbase, k_dma, K_RING, 2 * j + 4);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 1);
         dma_block(vbase, v_dma, V_RING, 2 * j + 2);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 3);
-        block(I1{}, I0{}, 2 * j, sa, sb);
-        block(I2{}, I1{}, 2 * j + 1, sb, sa);
+    };
+    // tile 0: step 0 has no previous block
+    refill(0);
+    if (0 <= n_blk) step(std::true_type{}, I1{}, I3{}, 0, sa, sb, pb, pa);
+    if (1 <= n_blk) step(F{}, I2{}, I0{}, 1, sb, sa, pa, pb);
+    wait_dma();
+    __syncthreads();
+    for (int j = 1; j < n_tiles; j += 2) {
+        // odd tile: blocks 2j = 2 (mod 4), 2j+1 = 3 (mod 4)
+        refill(j);
+        if (2 * j <= n_blk) step(F{}, I3{}, I1{}, 2 * j, sa, sb, pb, pa);
+        if (2 * j + 1 <= n_blk) step(F{}, I0{}, I2{}, 2 * j + 1, sb, sa, pa, pb);
         wait_dma();
         __syncthreads();
         if (j + 1 >= n_tiles) break;
-        dma_block(kbase, k_dma, K_RING, 2 * j + 5);
-        dma_block(kbase, k_dma, K_RING, 2 * j + 6);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 4);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 5);
-        block(I3{}, I2{}, 2 * j + 2, sa, sb);
-        block(I0{}, I3{}, 2 * j + 3, sb, sa);
+        // even tile: blocks 2j+2 = 0 (mod 4), 2j+3 = 1 (mod 4)
+        refill(j + 1);
+        if (2 * j + 2 <= n_blk) step(F{}, I1{}, I3{}, 2 * j + 2, sa, sb, pb, pa);
+        if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb, sa, pa, pb);
         wait_dma();
         __syncthreads();
     }
