@@ -28,11 +28,11 @@
 //     accumulator holds them; V^T fragments are read in the same key order with
 //     the gfx950 transposing LDS read (ds_read_b64_tr_b16), so V never needs a
 //     transposed copy;
-//   * softmax in base 2 against a reference max m: p = exp2(s*c - m*c) with
-//     c = scale*log2(e).  The reference only moves (rescaling O and l) when a
-//     row's max exceeds it by more than 2^8 in p; otherwise p <= 256, which
-//     fp32 accumulation absorbs.  The final O / l and LSE = m*scale + ln(l) are
-//     the same quantities whichever reference was used.
+//   * softmax in base 2 against a reference m: p = exp2(s*c - m*c) with
+//     c = scale*log2(e), m starting at the row max of the first key block.
+//     The reference only moves (rescaling O and the sums) when p could stop
+//     being finite: the final O / sum(bf16 p) and LSE = m*scale + ln(sum p)
+//     are the same quantities whichever reference was used.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -64,7 +64,8 @@ constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB per K or V block
 constexpr int K_RING = 0;                  // LDS: a ring of 4 K blocks, then 4 V blocks
 constexpr int V_RING = 4 * BLK_BYTES;
 constexpr int LDS_BYTES = 8 * BLK_BYTES;   // 64 KiB
-constexpr float RESCALE_LOG2 = 8.0f;       // reference max moves when p would exceed 2^8
+constexpr float MOVE_SUM = 18446744073709551616.0f;  // 2^64: a lane's block sum of p above
+                                                      // this moves the softmax reference
 constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
 
 struct Params {
@@ -335,37 +336,45 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         lbs = lb0 + lb1;
     };
 
+    auto row_max = [&](const f32x16& s) {
+        float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return wave_swap_max(mx);
+    };
+
     // Key block g (valid while g < n_blk; g == n_blk only drains the last PV).
     // Issued together, with no dependence on this block's softmax:
     //   * the scores sn of block g+1 (K ring slot KS),
     //   * O += V_{g-1}^T P_{g-1}^T for the previous block (V ring slot VS),
     // while the VALU turns the scores s of block g into P_g against the current
-    // reference.  If a row's max moved by more than 2^RESCALE_LOG2 in p (rare,
-    // wave-uniform branch) the reference moves, O and the sums are rescaled
-    // once the previous PV has landed, and P_g is recomputed.
+    // reference m.  p only has to stay finite: bf16 and fp32 keep their
+    // relative precision at any magnitude, and O / sum(bf16 p) and
+    // m*scale + ln(sum p) do not depend on which reference was used.  So the
+    // reference only moves when a lane's block sum exceeds 2^64 (or is not
+    // finite): then (rare, wave-uniform branch) every row moves to its true
+    // running max, O and the sums are rescaled once the previous PV has
+    // landed, and P_g is recomputed.
     auto step = [&](auto first_t, auto ks_t, auto vs_t, int g, f32x16& s, f32x16& sn,
                     const u32x4 (&pp)[2], u32x4 (&pc)[2]) {
         constexpr bool FIRST = decltype(first_t)::value;
         constexpr uint32_t KS = K_RING + decltype(ks_t)::value * BLK_BYTES;
         constexpr uint32_t VS = V_RING + decltype(vs_t)::value * BLK_BYTES;
         const bool valid = g < n_blk;
-        if (valid && needs_mask(g)) apply_mask(s, g);
+        if (!FIRST && valid && needs_mask(g)) apply_mask(s, g);
         scores(sn, KS);
         if constexpr (!FIRST) pv(pp, VS);
-        float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = wave_swap_max(mx);
         float ls, lbs;
         probs(s, pc, ls, lbs);
         // keep P_g ahead of the branch below (not sunk into its fall-through
         // path), so its VALU work interleaves with the MFMAs issued above
         asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(ls), "+v"(lbs));
-        const float m_new = fmaxf(m, mx);
-        const bool move = valid && (m_new - m) * c > RESCALE_LOG2;  // false for NaN
-        if (__builtin_amdgcn_ballot_w64(move)) {
+        const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM));
+        if (valid && over != 0) {
+            const float m_new = fmaxf(m, row_max(s));
+            const bool move = m_new > m;
             const float alpha = move ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
-            m = move ? m_new : m;
+            m = m_new;
             mb = (m == -INFINITY) ? 0.f : m * c;
             l *= alpha;
             lb *= alpha;
@@ -375,8 +384,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             probs(s, pc, ls, lbs);
         }
-        l += valid ? ls : 0.f;
-        lb += valid ? lbs : 0.f;
+        if (valid) {
+            l += ls;
+            lb += lbs;
+        }
     };
 
     f32x16 sa, sb;    // scores of even / odd key blocks
@@ -385,7 +396,13 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     // complete and never waits on vmcnt (which counts the DMA) inside the loop
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (n_blk > 0) scores(sa, K_RING);
+    if (n_blk > 0) {
+        // block 0's scores and the first reference (its row max)
+        scores(sa, K_RING);
+        if (needs_mask(0)) apply_mask(sa, 0);
+        m = row_max(sa);
+        mb = (m == -INFINITY) ? 0.f : m * c;
+    }
     __syncthreads();   // K slot 0 is refilled in the first tile
 
     using I0 = std::integral_constant<int, 0>;
