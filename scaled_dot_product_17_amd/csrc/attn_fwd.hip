@@ -54,10 +54,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
-constexpr int BR = 128;                    // query rows per workgroup
+constexpr int BR = 256;                    // query rows per workgroup
 constexpr int BC = 64;                     // keys per tile (one LDS refill, one barrier)
-constexpr int NWAVE = 4;                   // waves per workgroup
+constexpr int NWAVE = 8;                   // waves per workgroup
 constexpr int NTHREAD = NWAVE * 64;
+constexpr int DMA_PER_WAVE = 32 / (4 * NWAVE);   // 4-row DMA instructions per wave per key block
 constexpr int ROW_BYTES = HD * 2;          // 256 B per K/V/Q/O row
 constexpr int KB = 32;                     // keys per pipeline step (one MFMA M block)
 constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB per K or V block
@@ -201,10 +202,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     // lane order).  The bank swizzle is applied on the global side: lane L
     // fetches the logical chunk that belongs at its physical LDS position.
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-    uint32_t k_dma[2], v_dma[2];
+    uint32_t k_dma[DMA_PER_WAVE], v_dma[DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 8 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+        const int row = 4 * DMA_PER_WAVE * wave + 4 * i + (lane >> 4);
         const int pc = lane & 15;
         k_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ (row & 15)) << 4));
         v_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ ((row & 3) << 2)) << 4));
@@ -212,9 +213,9 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     auto dma_block = [&](const uint16_t* panel, const uint32_t* voff, int ring, int g) {
         if (g < n_blk_wg) {
             const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW_BYTES);
-            const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 8 * wave * ROW_BYTES;
+            const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 4 * DMA_PER_WAVE * wave * ROW_BYTES;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
+            for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
         }
     };
 
