@@ -6,6 +6,8 @@ links or calls anything here, and nothing here imports the product package.
 
 ``attn_ref`` wraps the C routine in ``attn_ref.c`` (the plain definition,
 softmax(scale * Q K^T [causal]) V and its log-sum-exp, in double precision).
+``attn_bwd_ref`` wraps ``attn_bwd_ref.c`` (the chain rule through that
+definition: dQ, dK, dV for a given dO, in double precision).
 """
 from __future__ import annotations
 
@@ -17,7 +19,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "attn_ref.c")
+_SRCS = [os.path.join(_HERE, "attn_ref.c"), os.path.join(_HERE, "attn_bwd_ref.c")]
 _LIB = os.path.join(_HERE, "libattn_ref.so")
 _lock = threading.Lock()
 _lib = None
@@ -25,10 +27,11 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile the oracle with the host C compiler (no fast-math: IEEE double)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB) or \
+            os.path.getmtime(_LIB) < max(os.path.getmtime(s) for s in _SRCS):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
-               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+               "-ffp-contract=off", "-o", tmp] + _SRCS + ["-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -40,6 +43,11 @@ def _bind(path: str):
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
+    if hasattr(lib, "attn_bwd_ref_f64"):
+        bw = lib.attn_bwd_ref_f64
+        bw.restype = ctypes.c_int
+        bw.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
     return lib
 
 
@@ -101,3 +109,56 @@ def call_lib(lib, q, k, v, causal, scale, rows=None, n_threads=None):
     if rc != 0:
         raise ValueError(f"attn_ref_f64 failed with code {rc}")
     return o, lse
+
+
+def attn_bwd_ref(q, k, v, do, causal: bool, scale: float, rows=None, mags: bool = False,
+                 n_threads: int | None = None):
+    """Oracle backward pass (gradients of the forward for an output gradient dO).
+
+    q, do: uint16 bf16 bits [B, H_q, N, D]; k, v: uint16 bf16 bits [B, H_kv, N, D].
+    Returns (dq, dk, dv) as float64 ([B,H_q,N,D], [B,H_kv,N,D], [B,H_kv,N,D]).
+    ``rows``: optional int64 flat row ids; then only dq is computed and returned,
+    as [len(rows), D].  ``mags``: also return the error-scale sums (same shapes,
+    appended after the gradients) that the parity tolerance is built from.
+    """
+    return call_bwd_lib(_load(), q, k, v, do, causal, scale, rows, mags, n_threads)
+
+
+def call_bwd_lib(lib, q, k, v, do, causal, scale, rows=None, mags=False, n_threads=None):
+    """``attn_bwd_ref`` against an explicitly loaded oracle library (see ``_bind``)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    do = np.ascontiguousarray(do, dtype=np.uint16)
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape or do.shape != q.shape:
+        raise ValueError("q, do must be [B,H_q,N,D], k and v [B,H_kv,N,D]")
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
+        raise ValueError("shape mismatch between q and k/v")
+    nt = default_threads() if n_threads is None else int(n_threads)
+    if rows is None:
+        dq = np.empty((B, Hq, N, D))
+        dk = np.empty((B, Hkv, N, D))
+        dv = np.empty((B, Hkv, N, D))
+        out = [dq, dk, dv]
+        mg = [np.empty_like(a) for a in out] if mags else [None] * 3
+        rows_p, n_rows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        dq = np.empty((rows.size, D))
+        out = [dq]
+        mg = [np.empty_like(dq) if mags else None, None, None]
+        rows_p, n_rows = rows.ctypes.data, rows.size
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.attn_bwd_ref_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                              ptr(out[0]), ptr(out[1]) if rows is None else None,
+                              ptr(out[2]) if rows is None else None,
+                              ptr(mg[0]), ptr(mg[1]), ptr(mg[2]),
+                              B, Hq, Hkv, N, D, int(bool(causal)), float(scale), nt,
+                              rows_p, n_rows)
+    if rc != 0:
+        raise ValueError(f"attn_bwd_ref_f64 failed with code {rc}")
+    if rows is not None:
+        return (dq, mg[0]) if mags else dq
+    return tuple(out + mg) if mags else tuple(out)
