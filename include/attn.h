@@ -1,5 +1,6 @@
 /*
- * attn.h: C ABI of the MI355X (gfx950) fused attention forward library.
+ * attn.h: C ABI of the MI355X (gfx950) fused attention library (forward and
+ * backward).
  *
  * The operation.  Scaled dot-product attention forward with the log-sum-exp
  * of every score row:
@@ -75,6 +76,49 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int B, int H_q, int H_kv, int N, int D, int causal, float scale,
                      void* stream);
 
+/*
+ * attn_bwd: enqueue the attention backward pass on `stream`: the gradients of
+ * a scalar loss with respect to q, k and v, given its gradient dout with
+ * respect to the forward output.
+ *
+ * The operation.  The chain rule through the forward above, with the
+ * probabilities recomputed from the forward's LSE rather than stored (page
+ * "AVO算法优化Transformer注意力机制性能解析", section 2.2: recomputation and
+ * gradient reuse in the backward pass; page "GPU注意力算子性能优化"
+ * (QiMeng-Attention), section 2.2.2: the backward's gradients).  With
+ * P_ij = exp(scale * q_i.k_j - LSE_i) over the allowed keys:
+ *
+ *     delta_i = dO_i . O_i
+ *     dS_ij   = P_ij (dO_i . v_j - delta_i)
+ *     dQ_i    = scale * sum_j dS_ij k_j
+ *     dK_j    = scale * sum_i dS_ij q_i      (summed over the query heads
+ *     dV_j    = sum_i P_ij dO_i               of the K/V head's group)
+ *
+ * q, dout  device pointers, bf16 [B, H_q, N, D] (dout: dL/dO).
+ * k, v     device pointers, bf16 [B, H_kv, N, D].
+ * o, lse   the forward's outputs for these q, k, v, causal and scale: bf16
+ *          [B, H_q, N, D] and fp32 [B, H_q, N] (natural log).
+ * dq       device pointer, bf16 [B, H_q, N, D], written.
+ * dk, dv   device pointers, bf16 [B, H_kv, N, D], written.
+ * delta    device pointer, fp32 [B, H_q, N], written with delta_i above (the
+ *          dK/dV kernel reads it back; its value after the call is the row sum
+ *          dO_i . O_i in fp32).
+ * B, H_q, H_kv, N, D, causal, scale, stream: as for attn_fwd.
+ *
+ * Precision: P and dS are rounded to bf16 (nearest even) as matrix-core
+ * operands, every sum is accumulated in fp32, and the three gradients are
+ * rounded to bf16 (nearest even) once at the end.  No atomics: results are
+ * bitwise reproducible.
+ *
+ * Ownership and errors as for attn_fwd.  No output may overlap an input or
+ * another output (ATTN_ERR_ALIAS); q, k, v, o, dout, dq, dk, dv must be
+ * 16-byte aligned and lse, delta 4-byte aligned (ATTN_ERR_ALIGN).
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
+                     float scale, void* stream);
+
 /* attn_status_string: a static, human-readable description of a status code. */
 const char* attn_status_string(int status);
 
@@ -83,6 +127,12 @@ const char* attn_status_string(int status);
  * 4 * B * H_q * N^2 * D, halved when causal.  Host-only arithmetic.
  */
 double attn_fwd_flops(int B, int H_q, int N, int D, int causal);
+
+/*
+ * attn_bwd_flops: 10 * B * H_q * N^2 * D (the five N x N x D products S, dP,
+ * dV, dK, dQ), halved when causal.  Host-only arithmetic.
+ */
+double attn_bwd_flops(int B, int H_q, int N, int D, int causal);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,10 @@ def _bind(path: str):
         bw.restype = ctypes.c_int
         bw.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
+        bk = lib.attn_bwd_ref_keys_f64
+        bk.restype = ctypes.c_int
+        bk.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
     return lib
 
 
@@ -112,19 +116,22 @@ def call_lib(lib, q, k, v, causal, scale, rows=None, n_threads=None):
 
 
 def attn_bwd_ref(q, k, v, do, causal: bool, scale: float, rows=None, mags: bool = False,
-                 n_threads: int | None = None):
+                 n_threads: int | None = None, keys=None):
     """Oracle backward pass (gradients of the forward for an output gradient dO).
 
     q, do: uint16 bf16 bits [B, H_q, N, D]; k, v: uint16 bf16 bits [B, H_kv, N, D].
     Returns (dq, dk, dv) as float64 ([B,H_q,N,D], [B,H_kv,N,D], [B,H_kv,N,D]).
     ``rows``: optional int64 flat row ids; then only dq is computed and returned,
-    as [len(rows), D].  ``mags``: also return the error-scale sums (same shapes,
-    appended after the gradients) that the parity tolerance is built from.
+    as [len(rows), D].  ``keys``: optional int64 flat key ids ((b*H_kv + kv)*N + j);
+    then only (dk, dv) of those keys are returned, as [len(keys), D] each.
+    ``mags``: also return the error-scale sums (same shapes, appended after the
+    gradients) that the parity tolerance is built from.
     """
-    return call_bwd_lib(_load(), q, k, v, do, causal, scale, rows, mags, n_threads)
+    return call_bwd_lib(_load(), q, k, v, do, causal, scale, rows, mags, n_threads, keys)
 
 
-def call_bwd_lib(lib, q, k, v, do, causal, scale, rows=None, mags=False, n_threads=None):
+def call_bwd_lib(lib, q, k, v, do, causal, scale, rows=None, mags=False, n_threads=None,
+                 keys=None):
     """``attn_bwd_ref`` against an explicitly loaded oracle library (see ``_bind``)."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     k = np.ascontiguousarray(k, dtype=np.uint16)
@@ -137,6 +144,23 @@ def call_bwd_lib(lib, q, k, v, do, causal, scale, rows=None, mags=False, n_threa
     if k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
         raise ValueError("shape mismatch between q and k/v")
     nt = default_threads() if n_threads is None else int(n_threads)
+    if keys is not None:
+        if rows is not None:
+            raise ValueError("give rows or keys, not both")
+        keys = np.ascontiguousarray(keys, dtype=np.int64).reshape(-1)
+        dk = np.empty((keys.size, D))
+        dv = np.empty((keys.size, D))
+        mdk = np.empty_like(dk) if mags else None
+        mdv = np.empty_like(dv) if mags else None
+        rc = lib.attn_bwd_ref_keys_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                       dk.ctypes.data, dv.ctypes.data,
+                                       None if mdk is None else mdk.ctypes.data,
+                                       None if mdv is None else mdv.ctypes.data,
+                                       B, Hq, Hkv, N, D, int(bool(causal)), float(scale), nt,
+                                       keys.ctypes.data, keys.size)
+        if rc != 0:
+            raise ValueError(f"attn_bwd_ref_keys_f64 failed with code {rc}")
+        return (dk, dv, mdk, mdv) if mags else (dk, dv)
     if rows is None:
         dq = np.empty((B, Hq, N, D))
         dk = np.empty((B, Hkv, N, D))

@@ -64,7 +64,9 @@ typedef struct {
     double *lse, *delta, *amag;   /* per row of [B, H_q, N], written by phase 1 */
     int B, Hq, Hkv, N, D, causal;
     double scale;
-    const int64_t *rows;          /* phase 1 only: NULL = every row */
+    const int64_t *rows;          /* phase 1: NULL = every row */
+    int rows_give_dq;             /* phase 1: write dQ (row list order) or only the stats */
+    const int64_t *keys;          /* phase 2: NULL = every key row */
 } bctx_t;
 
 typedef struct {
@@ -119,6 +121,12 @@ static void bwd_row(const bctx_t *c, int64_t r, double *dq_row, double *mdq_row,
         delta += p[j] * dot;
         a += p[j] * mag;
     }
+    if (slot >= 0) {
+        c->lse[slot] = m + log(l);
+        c->delta[slot] = delta;
+        c->amag[slot] = a;
+    }
+    if (!dq_row) return;
     /* dQ_i = scale * sum_j P_ij (dP_ij - delta_i) K_j */
     for (int d = 0; d < D; ++d) {
         dq_row[d] = 0.0;
@@ -137,17 +145,12 @@ static void bwd_row(const bctx_t *c, int64_t r, double *dq_row, double *mdq_row,
         dq_row[d] *= c->scale;
         if (mdq_row) mdq_row[d] *= fabs(c->scale);
     }
-    if (slot >= 0) {
-        c->lse[slot] = m + log(l);
-        c->delta[slot] = delta;
-        c->amag[slot] = a;
-    }
 }
 
 /* Phase 2: dK_j and dV_j (and their error-scale sums) for key row t of
  * [B, H_kv, N], summed over the query heads of the group and the rows that
  * see key j. */
-static void bwd_key(const bctx_t *c, int64_t t, double *qrow, double *dorow)
+static void bwd_key(const bctx_t *c, int64_t out, int64_t t, double *qrow, double *dorow)
 {
     const int N = c->N, D = c->D;
     const int64_t j = t % N;
@@ -157,9 +160,9 @@ static void bwd_key(const bctx_t *c, int64_t t, double *qrow, double *dorow)
     const int64_t group = c->Hq / c->Hkv;
     const uint16_t *kj = c->k + t * D;
     const uint16_t *vj = c->v + t * D;
-    double *dk = c->dk + t * D, *dv = c->dv + t * D;
-    double *mdk = c->mdk ? c->mdk + t * D : NULL;
-    double *mdv = c->mdv ? c->mdv + t * D : NULL;
+    double *dk = c->dk + out * D, *dv = c->dv + out * D;
+    double *mdk = c->mdk ? c->mdk + out * D : NULL;
+    double *mdv = c->mdv ? c->mdv + out * D : NULL;
 
     for (int d = 0; d < D; ++d) {
         dk[d] = 0.0;
@@ -209,15 +212,26 @@ static void *bwd_worker(void *arg)
     for (int64_t t = jb->first; t < jb->last; ++t) {
         if (jb->phase == 1) {
             const int64_t r = c->rows ? c->rows[t] : t;
-            bwd_row(c, r, c->dq + t * c->D, c->mdq ? c->mdq + t * c->D : NULL,
-                    c->rows ? -1 : r, qrow, dorow, p, dp);
+            double *dq = c->rows_give_dq ? c->dq + t * c->D : NULL;
+            double *mdq = (c->rows_give_dq && c->mdq) ? c->mdq + t * c->D : NULL;
+            bwd_row(c, r, dq, mdq, c->lse ? r : -1, qrow, dorow, p, dp);
         } else {
-            bwd_key(c, t, qrow, dorow);
+            bwd_key(c, t, c->keys ? c->keys[t] : t, qrow, dorow);
         }
     }
     free(buf);
     jb->status = 0;
     return NULL;
+}
+
+/* Per-row statistics (lse, delta, a) of [B, H_q, N] rows, filled with NaN so
+ * that a row phase 1 did not visit poisons every result that reads it. */
+static double *bwd_stats_alloc(int64_t total)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)(3 * total));
+    if (s)
+        for (int64_t t = 0; t < 3 * total; ++t) s[t] = NAN;
+    return s;
 }
 
 static int bwd_par_for(const bctx_t *c, int phase, int64_t n, int n_threads)
@@ -281,9 +295,10 @@ int attn_bwd_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     c.causal = causal ? 1 : 0;
     c.scale = scale;
     c.rows = rows;
+    c.rows_give_dq = 1;
     if (rows) return bwd_par_for(&c, 1, n_rows, n_threads);
 
-    double *stats = (double *)malloc(sizeof(double) * (size_t)(3 * total));
+    double *stats = bwd_stats_alloc(total);
     if (!stats) return -2;
     c.lse = stats;
     c.delta = stats + total;
@@ -291,5 +306,69 @@ int attn_bwd_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     int rc = bwd_par_for(&c, 1, total, n_threads);
     if (rc == 0) rc = bwd_par_for(&c, 2, (int64_t)B * H_kv * N, n_threads);
     free(stats);
+    return rc;
+}
+
+/*
+ * dK and dV of a subset of key rows: n_keys flat key ids ((b*H_kv + kv)*N + j).
+ * dk, dv (and the optional mag_dk, mag_dv) are [n_keys, D] doubles in the order
+ * given.  Phase 1 runs, without dQ, over every row of the query heads whose
+ * group contains a listed key; phase 2 only for the listed keys.  Same
+ * arithmetic as attn_bwd_ref_f64, so the rows agree with its full result.
+ * Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int attn_bwd_ref_keys_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          const uint16_t *dout, double *dk, double *dv,
+                          double *mag_dk, double *mag_dv,
+                          int B, int H_q, int H_kv, int N, int D, int causal, double scale,
+                          int n_threads, const int64_t *keys, int64_t n_keys)
+{
+    if (!q || !k || !v || !dout || !dk || !dv || !keys || n_keys < 0) return -1;
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || D <= 0) return -1;
+    if (H_q % H_kv != 0) return -1;
+    const int64_t total = (int64_t)B * H_q * N;
+    const int64_t nkv = (int64_t)B * H_kv;
+    for (int64_t t = 0; t < n_keys; ++t)
+        if (keys[t] < 0 || keys[t] >= nkv * N) return -1;
+    if (n_keys == 0) return 0;
+
+    /* the (b, kv) panels that hold a listed key, and every row of their heads */
+    char *used = (char *)calloc((size_t)nkv, 1);
+    double *stats = bwd_stats_alloc(total);
+    int64_t *rows = NULL;
+    int rc = -2;
+    if (!used || !stats) goto done;
+    for (int64_t t = 0; t < n_keys; ++t) used[keys[t] / N] = 1;
+    int64_t n_used = 0;
+    for (int64_t u = 0; u < nkv; ++u) n_used += used[u];
+    const int64_t group = H_q / H_kv;
+    rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_used * group * N));
+    if (!rows) goto done;
+    int64_t n_rows = 0;
+    for (int64_t u = 0; u < nkv; ++u) {
+        if (!used[u]) continue;
+        const int64_t b = u / H_kv, kvh = u % H_kv;
+        for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)
+            for (int64_t i = 0; i < N; ++i) rows[n_rows++] = (b * H_q + h) * N + i;
+    }
+    bctx_t c;
+    memset(&c, 0, sizeof c);
+    c.q = q; c.k = k; c.v = v; c.dout = dout;
+    c.dk = dk; c.dv = dv; c.mdk = mag_dk; c.mdv = mag_dv;
+    c.B = B; c.Hq = H_q; c.Hkv = H_kv; c.N = N; c.D = D;
+    c.causal = causal ? 1 : 0;
+    c.scale = scale;
+    c.lse = stats;
+    c.delta = stats + total;
+    c.amag = stats + 2 * total;
+    c.rows = rows;
+    c.rows_give_dq = 0;
+    c.keys = keys;
+    rc = bwd_par_for(&c, 1, n_rows, n_threads);
+    if (rc == 0) rc = bwd_par_for(&c, 2, n_keys, n_threads);
+done:
+    free(used);
+    free(stats);
+    free(rows);
     return rc;
 }

@@ -1,8 +1,8 @@
-"""MI355X (gfx950) fused scaled dot-product attention forward.
+"""MI355X (gfx950) fused scaled dot-product attention, forward and backward.
 
 Thin Python binding over the C ABI declared in ``include/attn.h``: argument
-marshalling only.  Every step of the computation runs in the HIP kernel of
-``libattn_fwd.so``; torch provides device memory and streams.  There is no CPU
+marshalling only.  Every step of the computation runs in the HIP kernels of
+``libattn.so``; torch provides device memory and streams.  There is no CPU
 or fallback path: if the library is missing or the GPU is not a gfx950 the
 calls raise.
 """
@@ -14,13 +14,13 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
+LIB_PATH = os.path.join(PKG, "libattn.so")
 
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GQA",
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE"}
-EXPORTED = ("attn_fwd", "attn_status_string", "attn_fwd_flops")
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_status_string", "attn_fwd_flops", "attn_bwd_flops")
 
 _lock = threading.Lock()
 _lib = None
@@ -48,6 +48,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_status_string.argtypes = [ctypes.c_int]
             lib.attn_fwd_flops.restype = ctypes.c_double
             lib.attn_fwd_flops.argtypes = [ctypes.c_int] * 5
+            lib.attn_bwd.restype = ctypes.c_int
+            lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
+                ctypes.c_float, ctypes.c_void_p]
+            lib.attn_bwd_flops.restype = ctypes.c_double
+            lib.attn_bwd_flops.argtypes = [ctypes.c_int] * 5
             _lib = lib
     return _lib
 
@@ -64,6 +69,32 @@ def attn_fwd(q, k, v, o, lse, B, H_q, H_kv, N, D, causal, scale, stream) -> int:
 
 def attn_fwd_flops(B, H_q, N, D, causal) -> float:
     return load().attn_fwd_flops(int(B), int(H_q), int(N), int(D), int(bool(causal)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H_q, H_kv, N, D, causal, scale,
+             stream) -> int:
+    """Direct C-ABI call with raw device pointers (ints); returns the status code."""
+    return load().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H_q),
+                           int(H_kv), int(N), int(D), int(bool(causal)), float(scale), stream)
+
+
+def attn_bwd_flops(B, H_q, N, D, causal) -> float:
+    return load().attn_bwd_flops(int(B), int(H_q), int(N), int(D), int(bool(causal)))
+
+
+def _check_bf16(name, t, shape=None, device=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D torch.bfloat16 tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -112,3 +143,49 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     if st != ATTN_OK:
         raise AttnError(st, status_string(st))
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, delta=None):
+    """dQ, dK, dV of attention on the current torch stream of q's device.
+
+    q, o, dout: bf16 [B, H_q, N, D]; k, v: bf16 [B, H_kv, N, D]; lse: fp32
+    [B, H_q, N] from ``fwd`` with the same causal and scale.  Output buffers may
+    be given to avoid allocation.  Returns (dq, dk, dv, delta) with delta the
+    fp32 [B, H_q, N] row sums dO . O.
+    """
+    import torch
+
+    _check_bf16("q", q)
+    B, Hq, N, D = q.shape
+    _check_bf16("k", k, device=q.device)
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
+        raise ValueError("k/v must be [B, H_kv, N, D] with q's B, N and D")
+    _check_bf16("v", v, k.shape, q.device)
+    _check_bf16("o", o, q.shape, q.device)
+    _check_bf16("dout", dout, q.shape, q.device)
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or \
+            tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [B, H_q, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_bf16("dq", dq, q.shape, q.device)
+    _check_bf16("dk", dk, k.shape, q.device)
+    _check_bf16("dv", dv, k.shape, q.device)
+    if delta is None:
+        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif delta.dtype != torch.float32 or tuple(delta.shape) != (B, Hq, N) or \
+            not delta.is_contiguous() or delta.device != q.device:
+        raise ValueError("delta must be a contiguous fp32 [B, H_q, N] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      delta.data_ptr(), B, Hq, Hkv, N, D, causal, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_string(st))
+    return dq, dk, dv, delta

@@ -1,4 +1,4 @@
-"""Builds the gfx950 HIP library ``libattn_fwd.so`` in-tree with hipcc."""
+"""Builds the gfx950 HIP library ``libattn.so`` in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -7,15 +7,15 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 HDR = os.path.join(ROOT, "include", "attn.h")
-LIB = os.path.join(PKG, "libattn_fwd.so")
+LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for every HIP translation unit.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-Wall", "-Wno-unused-function"]
+               "-Wall", "-Wno-unused-function", "-Wno-inline-asm"]
 
 
 def hipcc() -> str:
@@ -29,7 +29,7 @@ def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     """Compile the library (always recompiles).  Returns the .so path."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
-           "-o", tmp, SRC]
+           "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]

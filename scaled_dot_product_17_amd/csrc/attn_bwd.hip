@@ -1,0 +1,563 @@
+// Fused scaled dot-product attention backward for MI355X (gfx950, CDNA4).
+//
+// Given Q, K, V, the forward's output O and per-row LSE, and the output
+// gradient dO, computes dQ, dK, dV by recomputing the probabilities from the
+// saved LSE instead of storing them (page "AVO算法优化Transformer注意力机制性能
+// 解析", section 2.2: recomputation in the backward pass; page "GPU注意力算子
+// 性能优化" (QiMeng-Attention), section 2.2.2: the backward's gradients).  With
+// c = scale * log2(e) and the chain rule through softmax:
+//
+//     P_ij    = exp2(c * q_i.k_j - LSE_i * log2(e))
+//     delta_i = dO_i . O_i                   (= sum_j P_ij dP_ij)
+//     dP_ij   = dO_i . v_j,   dS_ij = P_ij (dP_ij - delta_i)
+//     dV_j    = sum_i P_ij dO_i
+//     dK_j    = scale * sum_i dS_ij q_i,   dQ_i = scale * sum_j dS_ij k_j
+//
+// dK and dV of a shared K/V head sum over the query heads of its group.
+//
+// Two kernels, no atomics (results are bitwise reproducible):
+//   * attn_bwd_dq: one workgroup = 8 waves = 256 query rows of one head; the
+//     structure of the forward kernel.  Each wave keeps its 32 rows of Q and dO
+//     in VGPRs as MFMA B operands and streams 32-key blocks of K and V through
+//     LDS (LDS DMA, double-buffered 64-key tiles).  Per block it computes
+//     S^T = K Q^T and dP^T = V dO^T, turns them into dS^T (one query per lane,
+//     so LSE and delta are per-lane scalars) and accumulates
+//     dQ^T += K^T dS^T, reading K^T with the transposing LDS read.  It also
+//     computes delta_i from O and dO once per row and writes it out.
+//   * attn_bwd_dkdv: one workgroup = 4 waves = 128 keys of one K/V head; each
+//     wave keeps its 32 keys of K and V in VGPRs as MFMA B operands and the
+//     fp32 accumulators dK^T, dV^T (128 x 32 each).  64-row tiles of Q, dO,
+//     LSE and delta of every query head of the group stream through LDS.  Per
+//     32-row sub-block: S = Q K^T and dP = dO V^T (one key per lane), then
+//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "attn.h"
+#include "cdna4.h"
+
+namespace {
+
+using namespace cdna4;
+
+constexpr int HD = 128;                    // head dimension handled by these kernels
+constexpr int ROW_BYTES = HD * 2;          // 256 B per bf16 row
+constexpr int KB = 32;                     // rows per MFMA block
+constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB
+constexpr float LOG2E = 1.4426950408889634f;
+
+// attn_bwd_dq: 8 waves, rings of 4 K blocks and 4 V blocks
+constexpr int DQ_WAVES = 8;
+constexpr int DQ_THREADS = DQ_WAVES * 64;
+constexpr int DQ_ROWS = DQ_WAVES * 32;
+constexpr int DQ_K_RING = 0;
+constexpr int DQ_V_RING = 4 * BLK_BYTES;
+constexpr int DQ_LDS = 8 * BLK_BYTES;      // 64 KiB
+
+// attn_bwd_dkdv: 4 waves x 32 keys; two stages of (Q, dO, LSE, delta) x 64 rows
+constexpr int KV_WAVES = 4;
+constexpr int KV_THREADS = KV_WAVES * 64;
+constexpr int KV_KEYS = KV_WAVES * 32;
+constexpr int KV_QROWS = 64;
+constexpr int KV_TILE = KV_QROWS * ROW_BYTES;           // 16 KiB
+constexpr int KV_LSE = 2 * KV_TILE;                     // offset of LSE in a stage
+constexpr int KV_DELTA = KV_LSE + KV_QROWS * 4;         // offset of delta in a stage
+constexpr int KV_STAGE = KV_DELTA + KV_QROWS * 4;
+constexpr int KV_LDS = 2 * KV_STAGE;
+
+struct BwdParams {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float* lse;
+    uint16_t *dq, *dk, *dv;
+    float* delta;
+    int B, Hq, Hkv, N;
+    int group;              // Hq / Hkv
+    int n_qtiles, total_q;  // attn_bwd_dq grid: B * Hq * ceil(N / 256)
+    int n_ktiles, total_k;  // attn_bwd_dkdv grid: B * Hkv * ceil(N / 128)
+    float c;                // scale * log2(e)
+    float scale;
+};
+
+// LDS layout of every 256-byte row tile (K, V, Q, dO): 16-byte chunk c of row r
+// sits at chunk position c ^ swz(r).  A row-wise MFMA operand read (16 rows,
+// one chunk) hits 16 distinct positions; a transposing read (4 rows x 4
+// chunks) puts each row in its own 64-byte bank group.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+    return (uint32_t)(row * ROW_BYTES + ((chunk ^ swz(row)) << 4));
+}
+
+// Per-lane LDS offsets of the two operand read patterns of a 32-row block.
+//   rd_row[ks]: A operand with rows = MFMA m, 8 consecutive head dims of k step ks.
+//   tr_lo/tr_hi[db]: A operand with head dims 32db.. = MFMA m and rows = MFMA k in
+//   the order an fp32 accumulator holds them (rows 8(r/4) + 4(lane/32) + r%4 of
+//   register r), so an accumulator turned into bf16 pairs is the matching B
+//   operand.  Rows 16..31 of the block add 16 * ROW_BYTES (the swizzle repeats).
+struct TileReads {
+    uint32_t rd_row[8];
+    uint32_t tr_lo[4], tr_hi[4];
+    __device__ __forceinline__ void init(int lane) {
+        const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) rd_row[ks] = tile_off(l32, 2 * ks + hh);
+        const int g = lane >> 4;          // 16-lane group
+        const int rs = (lane & 15) >> 2;  // row within the 4-row group
+        const int cs = lane & 3;          // 4-element column group
+        const int row = 4 * (g >> 1) + rs;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int col = 32 * db + 16 * (g & 1) + 4 * cs;
+            const uint32_t half = (col & 4) ? 8u : 0u;
+            tr_lo[db] = tile_off(row, col >> 3) + half;
+            tr_hi[db] = tile_off(row + 8, col >> 3) + half;
+        }
+    }
+    // A operand of rows 16kk..16kk+15 (accumulator order) x head dims 32db..32db+31
+    __device__ __forceinline__ bf16x8 tr(const char* lds, uint32_t base, int db, int kk) const {
+        const bf16x4 lo = lds_read_tr(lds, base + tr_lo[db] + (uint32_t)(16 * kk * ROW_BYTES));
+        const bf16x4 hi = lds_read_tr(lds, base + tr_hi[db] + (uint32_t)(16 * kk * ROW_BYTES));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    __device__ __forceinline__ bf16x8 row(const char* lds, uint32_t base, int ks) const {
+        return *(const bf16x8*)(lds + base + rd_row[ks]);
+    }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void store_row_bf16(uint16_t* row, const f32x16 (&acc)[4], float mul,
+                                               int hh) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[db][4 * r4 + i] * mul);
+            *(bf16x4*)(row + 32 * db + 8 * r4 + 4 * hh) = v;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and delta)
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(DQ_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[DQ_LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;   // query column owned by this lane
+    const int hh = lane >> 5;
+
+    const int logical = xcd_remap(blockIdx.x, p.total_q);
+    const int bh = logical / p.n_qtiles;
+    int qt = logical % p.n_qtiles;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
+    const int b = bh / p.Hq;
+    const int h = bh % p.Hq;
+    const int kvh = h / p.group;
+    const int N = p.N;
+    const int q0 = qt * DQ_ROWS;
+    const int wq0 = q0 + wave * 32;
+    const int myq = wq0 + l32;
+
+    const size_t row_panel = ((size_t)b * p.Hq + h) * (size_t)N;
+    const size_t qo_panel = row_panel * HD;
+    const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
+    const uint16_t* kbase = p.k + kv_panel;
+    const uint16_t* vbase = p.v + kv_panel;
+
+    // key blocks streamed by the workgroup (n_blk_wg) and used by this wave (n_blk)
+    const int n_blk_all = (N + KB - 1) / KB;
+    int n_blk_wg = n_blk_all, n_blk = n_blk_all;
+    if (CAUSAL) {
+        n_blk_wg = min(n_blk_all, (min(q0 + DQ_ROWS, N) - 1) / KB + 1);
+        n_blk = min(n_blk_all, wq0 / KB + 1);
+    }
+    if (wq0 >= N) n_blk = 0;
+
+    // LDS DMA: block g of K (V) goes to slot g % 4 of the K (V) ring; wave w
+    // copies rows 4w..4w+3 with one 16-byte-per-lane DMA.  The swizzle is
+    // applied on the global side: a lane fetches the chunk that belongs at its
+    // LDS position.
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    const int drow = 4 * wave + (lane >> 4);
+    const uint32_t dma_off = (uint32_t)(drow * ROW_BYTES + (((lane & 15) ^ swz(drow)) << 4));
+    auto dma_block = [&](const uint16_t* panel, int ring, int g) {
+        if (g < n_blk_wg) {
+            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW_BYTES);
+            lds_dma16(r, lds_base + ring + (g & 3) * BLK_BYTES + 4 * wave * ROW_BYTES, dma_off);
+        }
+    };
+
+    TileReads rd;
+    rd.init(lane);
+
+    if (N % KB != 0) {
+        // rows past N of the tail block must read as finite values (zeros)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < DQ_LDS / (16 * DQ_THREADS); ++i)
+            *(u32x4*)(lds + 16 * (tid + DQ_THREADS * i)) = z;
+        __syncthreads();
+    }
+    dma_block(kbase, DQ_K_RING, 0);
+    dma_block(vbase, DQ_V_RING, 0);
+    dma_block(kbase, DQ_K_RING, 1);
+    dma_block(vbase, DQ_V_RING, 1);
+
+    // this lane's half row (head dims 16ks + 8hh .. +7) of Q and dO as B
+    // operands; delta from O and dO; the row's LSE in base 2
+    bf16x8 qf[8], df[8];
+    float delta, lse2;
+    {
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + qo_panel, (uint32_t)N * ROW_BYTES);
+        const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + qo_panel, (uint32_t)N * ROW_BYTES);
+        const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.o + qo_panel, (uint32_t)N * ROW_BYTES);
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint32_t off = (uint32_t)myq * ROW_BYTES + (16 * ks + 8 * hh) * 2;
+            qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, off));
+            df[ks] = __builtin_bit_cast(bf16x8, buf_load16(dr, off));
+            const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(orr, off));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf((float)df[ks][i], (float)ov[i], acc);
+        }
+        delta = wave_swap_sum(acc);
+        const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse + row_panel, (uint32_t)N * 4);
+        lse2 = buf_load_f32(lr, (uint32_t)myq * 4) * LOG2E;
+    }
+    if (hh == 0 && myq < N) p.delta[row_panel + myq] = delta;
+    const float c = p.c;
+
+    f32x16 dq[4];   // dQ^T: 4 blocks of 32 head dims x 32 query columns
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
+
+    // Key block g from ring slot SLOT.
+    auto step = [&](auto slot_t, int g) __attribute__((always_inline)) {
+        constexpr uint32_t KS = DQ_K_RING + decltype(slot_t)::value * BLK_BYTES;
+        constexpr uint32_t VS = DQ_V_RING + decltype(slot_t)::value * BLK_BYTES;
+        if (g >= n_blk) return;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, KS, ks), qf[ks], s, 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, VS, ks), df[ks], dp, 0, 0, 0);
+        const bool mask = (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
+        u32x4 dsw[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float d2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 8 * kk + 2 * i + e;
+                    float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+                    if (mask) {
+                        const int key = g * KB + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        pr = (key >= N || (CAUSAL && key > myq)) ? 0.f : pr;
+                    }
+                    d2[e] = pr * (dp[r] - delta);
+                }
+                dsw[kk][i] = pack_bf16(d2[0], d2[1]);
+            }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(lds, KS, db, kk),
+                                                                 __builtin_bit_cast(bf16x8, dsw[kk]),
+                                                                 dq[db], 0, 0, 0);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    // vmcnt(0) through the builtin: the compiler then knows every VGPR load
+    // above is complete and never waits on vmcnt (which counts the DMA) later
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    // Tile t = blocks 2t, 2t+1 in slots (2t)%4, (2t+1)%4.  At its start the
+    // workgroup prefetches tile t+1 into the slots tile t-1 used.
+    const int n_tiles = (n_blk_wg + 1) / 2;
+    for (int t = 0; t < n_tiles; t += 2) {
+        dma_block(kbase, DQ_K_RING, 2 * t + 2);
+        dma_block(vbase, DQ_V_RING, 2 * t + 2);
+        dma_block(kbase, DQ_K_RING, 2 * t + 3);
+        dma_block(vbase, DQ_V_RING, 2 * t + 3);
+        step(I0{}, 2 * t);
+        step(I1{}, 2 * t + 1);
+        wait_dma();
+        __syncthreads();
+        if (t + 1 >= n_tiles) break;
+        dma_block(kbase, DQ_K_RING, 2 * t + 4);
+        dma_block(vbase, DQ_V_RING, 2 * t + 4);
+        dma_block(kbase, DQ_K_RING, 2 * t + 5);
+        dma_block(vbase, DQ_V_RING, 2 * t + 5);
+        step(I2{}, 2 * t + 2);
+        step(I3{}, 2 * t + 3);
+        wait_dma();
+        __syncthreads();
+    }
+
+    if (myq < N) store_row_bf16(p.dq + qo_panel + (size_t)myq * HD, dq, p.scale, hh);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(KV_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[KV_LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;   // key column owned by this lane
+    const int hh = lane >> 5;
+
+    // with a causal mask the first key tiles of a head see the most rows, and
+    // they come first in this order
+    const int logical = xcd_remap(blockIdx.x, p.total_k);
+    const int bk = logical / p.n_ktiles;
+    const int kt = logical % p.n_ktiles;
+    const int b = bk / p.Hkv;
+    const int kvh = bk % p.Hkv;
+    const int N = p.N;
+    const int k0 = kt * KV_KEYS;
+    const int wk0 = k0 + 32 * wave;
+    const int myk = wk0 + l32;
+    const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
+
+    // query tiles of 64 rows: t0..n_qt-1 for each query head of the group
+    const int n_qt = (N + KV_QROWS - 1) / KV_QROWS;
+    const int t0 = CAUSAL ? k0 / KV_QROWS : 0;
+    const int n_t = n_qt - t0;
+    const int n_it = p.group * n_t;
+
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    uint32_t dma_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        dma_off[i] = (uint32_t)(row * ROW_BYTES + (((lane & 15) ^ swz(row)) << 4));
+    }
+    // stage it & 1 <- Q, dO, LSE, delta of iteration it
+    auto issue = [&](int it) {
+        if (it >= n_it) return;
+        const int hq = kvh * p.group + it / n_t;
+        const int t = t0 + it % n_t;
+        const size_t r0 = ((size_t)b * p.Hq + hq) * (size_t)N + (size_t)t * KV_QROWS;
+        const uint32_t left = (uint32_t)(N - t * KV_QROWS);
+        const uint32_t st = lds_base + (uint32_t)(it & 1) * KV_STAGE;
+        const u32x4 qr = sgpr_rsrc(p.q + r0 * HD, left * ROW_BYTES);
+        const u32x4 dr = sgpr_rsrc(p.dout + r0 * HD, left * ROW_BYTES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(qr, st + (16 * wave + 4 * i) * ROW_BYTES, dma_off[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(dr, st + KV_TILE + (16 * wave + 4 * i) * ROW_BYTES, dma_off[i]);
+        if (wave == 0) lds_dma4(sgpr_rsrc(p.lse + r0, left * 4), st + KV_LSE, (uint32_t)lane * 4);
+        if (wave == 1) lds_dma4(sgpr_rsrc(p.delta + r0, left * 4), st + KV_DELTA, (uint32_t)lane * 4);
+    };
+
+    TileReads rd;
+    rd.init(lane);
+
+    if (N % KV_QROWS != 0) {
+        // rows past N of the tail tile must read as finite values (zeros)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < KV_LDS / 16; i += KV_THREADS) *(u32x4*)(lds + 16 * i) = z;
+        __syncthreads();
+    }
+    issue(0);
+
+    // this lane's key row (head dims 16ks + 8hh .. +7) of K and V as B
+    // operands; zeros past N
+    bf16x8 kf[8], vf[8];
+    {
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_panel, (uint32_t)N * ROW_BYTES);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_panel, (uint32_t)N * ROW_BYTES);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint32_t off = (uint32_t)myk * ROW_BYTES + (16 * ks + 8 * hh) * 2;
+            kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(kr, off));
+            vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(vr, off));
+        }
+    }
+    const float c = p.c;
+
+    f32x16 dk[4], dv[4];   // dK^T, dV^T: 4 blocks of 32 head dims x 32 key columns
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    // One 32-row sub-block whose first query row is r0, at LDS stage offset st.
+    auto sub = [&](uint32_t st, int sb, int r0, bool mask) __attribute__((always_inline)) {
+        const uint32_t qs = st + (uint32_t)(32 * sb * ROW_BYTES);
+        const uint32_t ds = qs + KV_TILE;
+        const uint32_t ls = st + KV_LSE + (uint32_t)(32 * sb * 4);
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, qs, ks), kf[ks], s, 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, ds, ks), vf[ks], dp, 0, 0, 0);
+        float pr[16], dsr[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            // rows 8a + 4hh .. +3 of the sub-block: registers 4a .. 4a+3
+            const f32x4 l4 = *(const f32x4*)(lds + ls + (8 * a + 4 * hh) * 4);
+            const f32x4 d4 = *(const f32x4*)(lds + ls + (KV_DELTA - KV_LSE) + (8 * a + 4 * hh) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * a + i;
+                float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[i] * LOG2E));
+                if (mask) {
+                    const int row = r0 + 8 * a + 4 * hh + i;
+                    pv = (row >= N || (CAUSAL && row < myk)) ? 0.f : pv;
+                }
+                pr[r] = pv;
+                dsr[r] = pv * (dp[r] - d4[i]);
+            }
+        }
+        u32x4 pw[2], dsw[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pw[kk][i] = pack_bf16(pr[8 * kk + 2 * i], pr[8 * kk + 2 * i + 1]);
+                dsw[kk][i] = pack_bf16(dsr[8 * kk + 2 * i], dsr[8 * kk + 2 * i + 1]);
+            }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(lds, ds, db, kk),
+                                                                 __builtin_bit_cast(bf16x8, pw[kk]),
+                                                                 dv[db], 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(lds, qs, db, kk),
+                                                                 __builtin_bit_cast(bf16x8, dsw[kk]),
+                                                                 dk[db], 0, 0, 0);
+    };
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int it = 0; it < n_it; ++it) {
+        issue(it + 1);   // the other stage, released by the barrier that ended it-1
+        const int t = t0 + it % n_t;
+        const uint32_t st = (uint32_t)(it & 1) * KV_STAGE;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r0 = t * KV_QROWS + 32 * sb;
+            if (CAUSAL && r0 + 31 < wk0) continue;   // every row precedes every key of the wave
+            const bool mask = (CAUSAL && r0 < wk0 + 31) || (r0 + 32 > N);
+            sub(st, sb, r0, mask);
+        }
+        wait_dma();
+        __syncthreads();
+    }
+
+    if (myk < N) {
+        store_row_bf16(p.dk + kv_panel + (size_t)myk * HD, dk, p.scale, hh);
+        store_row_bf16(p.dv + kv_panel + (size_t)myk * HD, dv, 1.0f, hh);
+    }
+}
+
+}  // namespace
+
+extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
+                                float scale, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_GQA;
+    if (D != HD) return ATTN_ERR_HEAD_DIM;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    const int64_t n_qtiles = ((int64_t)N + DQ_ROWS - 1) / DQ_ROWS;
+    const int64_t n_ktiles = ((int64_t)N + KV_KEYS - 1) / KV_KEYS;
+    const int64_t total_q = (int64_t)B * H_q * n_qtiles;
+    const int64_t total_k = (int64_t)B * H_kv * n_ktiles;
+    if (total_q > INT32_MAX || total_k > INT32_MAX || (int64_t)B * H_q > INT32_MAX)
+        return ATTN_ERR_SHAPE;
+    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
+                           (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15;
+    if (mis != 0 || (((uintptr_t)lse | (uintptr_t)delta) & 3) != 0) return ATTN_ERR_ALIGN;
+    const size_t qb = (size_t)B * H_q * N * HD * 2;
+    const size_t kb = (size_t)B * H_kv * N * HD * 2;
+    const size_t rb = (size_t)B * H_q * N * 4;
+    const void* ins[6] = {q, k, v, o, dout, lse};
+    const size_t in_bytes[6] = {qb, kb, kb, qb, qb, rb};
+    const void* outs[4] = {dq, dk, dv, delta};
+    const size_t out_bytes[4] = {qb, kb, kb, rb};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (ranges_overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ATTN_ERR_ALIAS;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
+
+    BwdParams p;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o;
+    p.dout = (const uint16_t*)dout;
+    p.lse = lse;
+    p.dq = (uint16_t*)dq;
+    p.dk = (uint16_t*)dk;
+    p.dv = (uint16_t*)dv;
+    p.delta = delta;
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.N = N;
+    p.group = H_q / H_kv;
+    p.n_qtiles = (int)n_qtiles;
+    p.total_q = (int)total_q;
+    p.n_ktiles = (int)n_ktiles;
+    p.total_k = (int)total_k;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    p.scale = scale;
+
+    hipStream_t s = (hipStream_t)stream;
+    // delta is written by the dQ kernel and read by the dK/dV kernel: same
+    // stream, in this order
+    if (causal) {
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<true>, dim3((unsigned)total_q), dim3(DQ_THREADS), 0, s, p);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)total_k), dim3(KV_THREADS), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<false>, dim3((unsigned)total_q), dim3(DQ_THREADS), 0, s, p);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)total_k), dim3(KV_THREADS), 0, s, p);
+    }
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
+}
+
+extern "C" double attn_bwd_flops(int B, int H_q, int N, int D, int causal) {
+    // five N x N x D products (S, dP, dV, dK, dQ) of 2 flops per multiply-add
+    const double f = 10.0 * B * H_q * (double)N * (double)N * D;
+    return causal ? 0.5 * f : f;
+}

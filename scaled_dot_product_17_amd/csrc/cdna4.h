@@ -1,0 +1,107 @@
+// Small gfx950 (CDNA4) device and host helpers shared by the backward kernels:
+// vector types, buffer descriptors, LDS DMA, the transposing LDS read, cross-
+// half wave reductions, the XCD-aware workgroup order and argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+namespace cdna4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)RSRC_DWORD3);
+}
+
+// 16-byte buffer load into VGPRs; offsets at or beyond the range return zeros.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Raw buffer descriptor in SGPRs for inline assembly.
+__device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
+}
+
+// LDS DMA: the buffer unit copies rsrc[voff .. voff+15] (or +3) of every lane
+// to LDS byte lds_addr + 16*lane (or 4*lane) without passing through VGPRs.
+// Lanes whose offset is out of range copy nothing.  Inline assembly, so the
+// compiler does not order later LDS reads behind it; the caller waits for
+// completion (vmcnt) before the workgroup barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ds_read_b64_tr_b16: each 16-lane group reads a 4 x 16 block of bf16 and
+// every lane receives one column of it (4 values), so a row-major tile is
+// read as the column-major MFMA operand.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ float wave_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                              false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// Maps the hardware workgroup id to a logical id so that consecutive logical
+// ids land on the same XCD (the dispatcher deals workgroups to the 8 XCDs
+// round-robin): tiles of one head then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int nx = 8;
+    const int q = total / nx, r = total % nx;
+    const int x = bid % nx, s = bid / nx;
+    const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+    return start + s;
+}
+
+// ---- host side
+inline bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
+
+// Per-process cache of "is device d a gfx950".
+inline bool device_is_gfx950(int dev) {
+    constexpr int MAX_DEVICES = 64;
+    static std::atomic<int> cache[MAX_DEVICES];   // 0 unknown, 1 gfx950, 2 other
+    if (dev < 0 || dev >= MAX_DEVICES) return false;
+    int s = cache[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        cache[dev].store(s, std::memory_order_relaxed);
+    }
+    return s == 1;
+}
+
+}  // namespace cdna4

@@ -1,6 +1,7 @@
 """Checks that pin the fp64 backward oracle to facts other than itself.
 
-Each ``pin_*`` takes ``bref(q, k, v, do, causal, scale, rows=None, mags=False)``
+Each ``pin_*`` takes ``bref(q, k, v, do, causal, scale, rows=None, mags=False,
+keys=None)``
 (bf16 bit arrays in; float64 (dq, dk, dv) out, plus the error-scale sums when
 ``mags``) and raises AssertionError when the result contradicts finite
 differences of the (separately pinned) forward oracle, a library autograd, a
@@ -245,6 +246,20 @@ def pin_bwd_rows_subset(bref):
         assert np.array_equal(dqs, dq.reshape(-1, D)[rows]), "dQ row subset"
 
 
+def pin_bwd_keys_subset(bref):
+    """The key-subset mode returns exactly those key rows of the full dK, dV (and
+    of their error-scale sums)."""
+    B, Hq, Hkv, N, D = 2, 6, 3, 19, 16
+    q, k = rnd(65, (B, Hq, N, D)), rnd(66, (B, Hkv, N, D))
+    v, do = rnd(67, (B, Hkv, N, D)), rnd(68, (B, Hq, N, D))
+    keys = np.array([0, 18, 19, 40, B * Hkv * N - 1, 3], np.int64)
+    for causal in (False, True):
+        _, dk, dv, _, mk, mv = bref(q, k, v, do, causal, SCALE, mags=True)
+        dks, dvs, mks, mvs = bref(q, k, v, do, causal, SCALE, keys=keys, mags=True)
+        for full, sub in ((dk, dks), (dv, dvs), (mk, mks), (mv, mvs)):
+            assert np.array_equal(sub, full.reshape(-1, D)[keys]), "key subset"
+
+
 def pin_bwd_error_scales(bref):
     """The error-scale sums bound each gradient (triangle inequality), and equal
     it where every term is non-negative: mag_dV = dV when dO >= 0."""
@@ -265,4 +280,5 @@ def pin_bwd_error_scales(bref):
 
 ALL_PINS = [pin_bwd_finite_difference, pin_bwd_library, pin_bwd_hand_example,
             pin_bwd_uniform, pin_bwd_sums, pin_bwd_key_shift, pin_bwd_gqa,
-            pin_bwd_causal_structure, pin_bwd_rows_subset, pin_bwd_error_scales]
+            pin_bwd_causal_structure, pin_bwd_rows_subset, pin_bwd_keys_subset,
+            pin_bwd_error_scales]

@@ -83,3 +83,40 @@ def sample_rows(B, Hq, N, rng, per_head=24, tile=128, heads=None):
         rows |= set(int(x) for x in rng.integers(0, N, per_head))
         out.extend(base + r for r in sorted(rows))
     return np.array(out, dtype=np.int64)
+
+
+# ---------------------------------------------------------------- backward
+# Each gradient element is a sum of products in which the kernel rounds one
+# factor to bf16 (P for dV, dS for dK and dQ; nearest even, relative error at
+# most U), takes delta from a bf16 O (error up to about 2U times
+# a_i = sum_j P_ij sum_d |dO_id||V_jd|), accumulates in fp32 and rounds the
+# result to bf16 once (relative error U).  The oracle's error-scale sum ``mag``
+# is the same sum with every term replaced by its magnitude and |dP - delta|
+# widened by a_i, so |g - ref| <= U |ref| + (U + 2U + fp32 terms) * mag.
+# KAPPA = 4 covers the rounding of the operand, the delta error and fp32
+# accumulation over up to 32K terms (worst case < U/2 * mag); the 2^-24
+# relative floor covers fp32 round-off of elements whose every term is tiny.
+U_BF16 = 2.0 ** -8
+BWD_KAPPA = 4.0
+
+
+def bwd_compare(g_gpu, g_ref, mag):
+    """Metrics of one GPU gradient (any float array) against the oracle: the worst
+    ratio of the error to its bound and the count of elements over it."""
+    g = np.asarray(g_gpu, dtype=np.float64)
+    err = np.abs(g - g_ref)
+    floor = 2.0 ** -24 * (float(np.abs(g_ref).max()) if g_ref.size else 0.0)
+    bound = U_BF16 * np.abs(g_ref) + BWD_KAPPA * U_BF16 * mag + floor
+    ratio = err / np.where(bound > 0, bound, np.inf)
+    return {
+        "finite": bool(np.all(np.isfinite(g))),
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "max_ratio": float(ratio.max()) if ratio.size else 0.0,
+        "n_over": int((err > bound).sum()),
+        "rel_fro": float(np.linalg.norm(g - g_ref) / max(np.linalg.norm(g_ref), 1e-300)),
+    }
+
+
+def bwd_check(m, what=""):
+    assert m["finite"], f"{what}: non-finite gradient {m}"
+    assert m["n_over"] == 0, f"{what}: error over U|g| + {BWD_KAPPA}U*mag {m}"

@@ -112,3 +112,52 @@ def test_faithful_rounding_helper():
     lo, hi, far = grid[i - 1], grid[i], grid[i - 2]
     assert faithful(lo, ref).all() and faithful(hi, ref).all()
     assert not faithful(far, ref).any()
+
+
+def test_bwd_flops_convention(lib):
+    assert sdpa.attn_bwd_flops(2, 16, 16384, 128, False) == 10.0 * 2 * 16 * 16384 ** 2 * 128
+    assert sdpa.attn_bwd_flops(2, 16, 16384, 128, True) == 5.0 * 2 * 16 * 16384 ** 2 * 128
+
+
+# attn_bwd: inputs q, k, v, o, dout, lse; outputs dq, dk, dv, delta (fake, far apart)
+BW = dict(q=0x100000, k=0x200000000, v=0x400000000, o=0x600000000, dout=0x800000000,
+          lse=0xA00000000, dq=0xC00000000, dk=0xE00000000, dv=0x1000000000,
+          delta=0x1200000000, B=1, H_q=4, H_kv=2, N=64, D=128, causal=1,
+          scale=1 / math.sqrt(128), stream=None)
+
+
+def call_bwd(**kw):
+    a = dict(BW)
+    a.update(kw)
+    return sdpa.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                         a["dv"], a["delta"], a["B"], a["H_q"], a["H_kv"], a["N"], a["D"],
+                         a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(dout=None), 1), (dict(lse=None), 1),
+    (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
+    (dict(B=0), 2), (dict(N=-3), 2), (dict(N=1 << 23), 2),
+    (dict(H_q=6, H_kv=4), 3), (dict(D=64), 4),
+    (dict(scale=float("nan")), 5),
+    (dict(dout=0x800000008), 6), (dict(dk=0xE00000002), 6), (dict(delta=0x1200000002), 6),
+    (dict(dq=0x100000), 7), (dict(dk=0x400000000 + 256), 7), (dict(delta=0x600000000), 7),
+    (dict(dv=0xC00000000 + 1024), 7), (dict(delta=0xA00000000 + 64), 7),
+])
+def test_bwd_argument_errors(lib, kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_valid_arguments_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_bwd() == 9
+
+
+def test_python_bwd_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 128, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        sdpa.bwd(q, q, q, q, lse, q)            # CPU tensors

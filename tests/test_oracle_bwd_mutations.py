@@ -25,7 +25,8 @@ MUTATIONS = {
     "dk_uses_k": ("dk[d] += ds * qrow[d];", "dk[d] += ds * bwd_widen(kj[d]);"),
     "dv_uses_v": ("dv[d] += p * dorow[d];", "dv[d] += p * bwd_widen(vj[d]);"),
     "dv_uses_ds": ("dv[d] += p * dorow[d];", "dv[d] += ds * dorow[d];"),
-    "gqa_first_head_only": ("h < (kvh + 1) * group; ++h", "h < kvh * group + 1; ++h"),
+    "gqa_first_head_only": ("h < (kvh + 1) * group; ++h) {\n        const int64_t first_row",
+                            "h < kvh * group + 1; ++h) {\n        const int64_t first_row"),
     "gqa_modulo_map": ("const int64_t kvh = h / (c->Hq / c->Hkv);",
                        "const int64_t kvh = h % c->Hkv;"),
     "key_mask_off": ("const int64_t first_row = c->causal ? j : 0;",
@@ -46,6 +47,8 @@ MUTATIONS = {
                               "const double kjd = bwd_widen(kp[(nkeys - 1 - j) * D + d]);"),
     "mag_dv_signed": ("if (mdv) mdv[d] += p * fabs(dorow[d]);",
                       "if (mdv) mdv[d] += p * dorow[d];"),
+    "keys_mode_skips_group": ("for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)\n            for (int64_t i = 0; i < N; ++i) rows[n_rows++]",
+                              "for (int64_t h = kvh * group; h < kvh * group + 1; ++h)\n            for (int64_t i = 0; i < N; ++i) rows[n_rows++]"),
     "mag_dq_drops_k_abs": ("if (mdq_row) mdq_row[d] += w * fabs(kjd);",
                            "if (mdq_row) mdq_row[d] += w * kjd;"),
 }
@@ -73,8 +76,9 @@ def test_planted_mistake_is_caught(name, tmp_path):
                     str(path_so), FWD_SRC, str(path_c), "-lm"], check=True)
     lib = oracle._bind(str(path_so))
 
-    def bref(q, k, v, do, causal, scale, rows=None, mags=False):
-        return oracle.call_bwd_lib(lib, q, k, v, do, causal, scale, rows, mags, n_threads=2)
+    def bref(q, k, v, do, causal, scale, rows=None, mags=False, keys=None):
+        return oracle.call_bwd_lib(lib, q, k, v, do, causal, scale, rows, mags, n_threads=2,
+                                   keys=keys)
 
     failed = _run_pins(bref)
     assert failed, f"no pin caught the planted mistake '{name}'"

@@ -1,0 +1,200 @@
+"""GPU parity of the backward pass: dQ, dK, dV from the HIP kernels against the
+fp64 backward oracle, element by element.
+
+The gradients come from the whole path a caller runs (the HIP forward's O and
+LSE feed the HIP backward).  Each element must satisfy
+|g - ref| <= U |ref| + KAPPA U mag (tests/parity.py derives the bound from the
+kernel's arithmetic; ``mag`` is the oracle's error-scale sum).  Small shapes are
+compared in full (several tiles of both kernels, ragged tails, MHA/GQA/MQA,
+both mask modes, other scales).  The benchmark workloads run at their real
+sizes in the launch configuration the benchmark times and are compared on
+sampled dQ rows and sampled dK/dV key rows that the oracle computes on their
+own, plus the column sum of dV, which holds at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+from tests.gpu_util import bf16_to_np, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1 / math.sqrt(128)))
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_dot_product_17_amd as sdpa
+    sdpa.load()   # raises if the library was not built
+
+
+def inputs(B, Hq, Hkv, N, seed):
+    q = synth.normal_bf16(seed, (B, Hq, N, 128))
+    k = synth.normal_bf16(seed + 1, (B, Hkv, N, 128))
+    v = synth.normal_bf16(seed + 2, (B, Hkv, N, 128))
+    do = synth.normal_bf16(seed + 3, (B, Hq, N, 128))
+    return q, k, v, do
+
+
+def run_bwd(q, k, v, do, causal, scale, o=None, lse=None):
+    """HIP forward (unless o, lse are given) then HIP backward; numpy results."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
+    if o is None:
+        og, lg = sdpa.fwd(qg, kg, vg, causal=causal, scale=scale)
+    else:
+        og, lg = to_gpu(o), torch.from_numpy(np.ascontiguousarray(lse, np.float32)).cuda()
+    dq, dk, dv, delta = sdpa.bwd(qg, kg, vg, og, lg, dog, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return {"dq": bf16_to_np(dq), "dk": bf16_to_np(dk), "dv": bf16_to_np(dv),
+            "delta": delta.cpu().numpy()}
+
+
+def check_all(res, ref, what):
+    dq, dk, dv, mq, mk, mv = ref
+    for name, r, m in (("dq", dq, mq), ("dk", dk, mk), ("dv", dv, mv)):
+        met = parity.bwd_compare(res[name], r, m)
+        say(f"  {what} {name}: {met}")
+        parity.bwd_check(met, f"{what} {name}")
+
+
+SMALL = [(1, 2, 2, 256), (2, 4, 2, 1), (1, 2, 1, 17), (1, 3, 3, 64), (1, 2, 2, 65),
+         (1, 2, 2, 129), (1, 8, 2, 200), (2, 4, 1, 1000), (1, 2, 2, 777), (1, 16, 8, 384),
+         (1, 4, 4, 1536)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "b%d_hq%d_hkv%d_n%d" % s)
+def test_bwd_small_full(shape, causal):
+    B, Hq, Hkv, N = shape
+    say(f"[bwd small] {shape} causal={causal}")
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=11000 + N)
+    res = run_bwd(q, k, v, do, causal, SCALE)
+    ref = oracle.attn_bwd_ref(q, k, v, do, causal, SCALE, mags=True)
+    check_all(res, ref, f"{shape} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.5])
+def test_bwd_other_scales(scale):
+    say(f"[bwd scale] {scale}")
+    q, k, v, do = inputs(1, 4, 2, 300, seed=12000)
+    for causal in (False, True):
+        res = run_bwd(q, k, v, do, causal, scale)
+        ref = oracle.attn_bwd_ref(q, k, v, do, causal, scale, mags=True)
+        check_all(res, ref, f"scale={scale} causal={causal}")
+
+
+def test_bwd_delta_from_given_o():
+    """O and LSE taken from the oracle (rounded to bf16 / fp32) instead of the
+    HIP forward: delta must be the fp32 row sum dO . O of that O, and the
+    gradients must still meet the bound."""
+    say("[bwd delta]")
+    B, Hq, Hkv, N = 1, 4, 2, 333
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=12500)
+    for causal in (False, True):
+        o_ref, lse_ref = oracle.attn_ref(q, k, v, causal, SCALE)
+        o_bits = synth.f32_to_bf16_bits(o_ref.astype(np.float32))
+        res = run_bwd(q, k, v, do, causal, SCALE, o=o_bits, lse=lse_ref.astype(np.float32))
+        terms = synth.bf16_bits_to_f32(do).astype(np.float64) * \
+            synth.bf16_bits_to_f32(o_bits).astype(np.float64)
+        exact = terms.sum(axis=-1)
+        tol = 2.0 ** -17 * np.abs(terms).sum(axis=-1) + 1e-30
+        assert np.all(np.abs(res["delta"] - exact) <= tol), "delta != dO . O"
+        check_all(res, oracle.attn_bwd_ref(q, k, v, do, causal, SCALE, mags=True),
+                  f"given O causal={causal}")
+
+
+def test_bwd_deterministic():
+    q, k, v, do = inputs(2, 8, 2, 1024, seed=12600)
+    for causal in (False, True):
+        a = run_bwd(q, k, v, do, causal, SCALE)
+        b = run_bwd(q, k, v, do, causal, SCALE)
+        for name in a:
+            assert np.array_equal(a[name], b[name]), f"{name} differs between runs"
+
+
+def test_bwd_gqa_dq_equals_repeated_mha():
+    """dQ of GQA equals dQ of MHA with K/V repeated per group (same arithmetic)."""
+    B, Hq, Hkv, N = 1, 8, 2, 400
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=12700)
+    g = Hq // Hkv
+    for causal in (False, True):
+        a = run_bwd(q, k, v, do, causal, SCALE)
+        b = run_bwd(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), do, causal, SCALE)
+        assert np.array_equal(a["dq"], b["dq"])
+
+
+def _panel_keys(B, Hkv, N, panels, rng, per_panel=16):
+    out = []
+    for b, kv in panels:
+        js = {0, 1, N - 1, N - 2, 127, 128} | set(rng.integers(0, N, per_panel).tolist())
+        out += [(b * Hkv + kv) * N + j for j in sorted(j for j in js if 0 <= j < N)]
+    return np.array(out, np.int64)
+
+
+BWD_WORKLOADS = ["mha_noncausal_b2_h16_n16384", "mha_causal_b2_h16_n16384",
+                 "gqa_b8_hq16_hkv2_n2048", "mqa_causal_peaky_b1_hq16_n32768"]
+
+
+@pytest.mark.parametrize("name", BWD_WORKLOADS)
+def test_bwd_workload_sampled(name):
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    w = synth.WORKLOADS[name]
+    say(f"[bwd workload] {name}")
+    q, k, v = w.generate()
+    do = synth.normal_bf16(w.seed_base + 3, q.shape)
+    qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
+    o, lse = sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale)
+    dq, dk, dv, _ = sdpa.bwd(qg, kg, vg, o, lse, dog, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    rng = np.random.default_rng(abs(hash(name)) % (2 ** 32))
+
+    # dQ on sampled rows
+    rows = parity.sample_rows(w.B, w.H_q, w.N, rng, per_head=8)
+    rq, mq = oracle.attn_bwd_ref(q, k, v, do, w.causal, w.scale, rows=rows, mags=True)
+    gq = bf16_to_np(dq.view(-1, 128)[torch.from_numpy(rows).cuda()])
+    met = parity.bwd_compare(gq, rq, mq)
+    say(f"  {name} dq rows: {met}")
+    parity.bwd_check(met, f"{name} dq")
+
+    # dK, dV on sampled keys of one or two K/V panels (the oracle then needs
+    # every row of those panels' query heads)
+    group_rows = (w.H_q // w.H_kv) * w.N * w.N
+    panels = [(0, 0)] if group_rows > 2 ** 28 or w.B * w.H_kv == 1 else \
+        [(0, 0), (w.B - 1, w.H_kv - 1)]
+    if group_rows <= 2 ** 30:
+        keys = _panel_keys(w.B, w.H_kv, w.N, panels, rng)
+        rk, rv, mk, mv = oracle.attn_bwd_ref(q, k, v, do, w.causal, w.scale, keys=keys, mags=True)
+        kidx = torch.from_numpy(keys).cuda()
+        for nm, g, r, m in (("dk", dk, rk, mk), ("dv", dv, rv, mv)):
+            met = parity.bwd_compare(bf16_to_np(g.view(-1, 128)[kidx]), r, m)
+            say(f"  {name} {nm} keys: {met}")
+            parity.bwd_check(met, f"{name} {nm}")
+
+    # every row of P sums to one: sum_j dV_j = sum of dO over the group's rows,
+    # within U (sum_j |dV_j| + sum_i |dO_i|) (the rounding of P and of dV)
+    g = w.H_q // w.H_kv
+    dv64 = dv.double().view(w.B, w.H_kv, w.N, 128)
+    do64 = dog.double().view(w.B, w.H_kv, g * w.N, 128)
+    lhs = dv64.sum(dim=2)
+    rhs = do64.sum(dim=2)
+    tol = 1.25 * parity.U_BF16 * (dv64.abs().sum(dim=2) + do64.abs().sum(dim=2))
+    over = int(((lhs - rhs).abs() > tol).sum())
+    say(f"  {name} sum dV: max |diff| {float((lhs - rhs).abs().max()):.3e}, over {over}")
+    assert over == 0, "sum_j dV_j != sum_i dO_i"
