@@ -1,14 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark of the fused attention forward on one MI355X.
+"""Benchmark of the fused attention forward (default) or backward on one MI355X.
 
-One step = one attn_fwd launch over the headline workload: non-causal MHA,
-B=2, N=16384, 16 heads, d=128, bf16 inputs (seeded synthetic N(0,1) data
-already resident in HBM).  Prints ONE JSON line on stdout:
-TFLOPS = 4*B*H*N^2*D / time (halved for causal), with the roofline of the
-kernel and the oracle's CPU rate on a bounded sample as a reported baseline.
+Forward: one step = one attn_fwd launch over the headline workload: non-causal
+MHA, B=2, N=16384, 16 heads, d=128, bf16 inputs (seeded synthetic N(0,1) data
+already resident in HBM).  TFLOPS = 4*B*H*N^2*D / time (halved for causal).
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
-                  [--no-cpu-baseline]
+Backward (--op bwd): one step = one attn_bwd call (the dQ kernel, then the
+dK/dV kernel) on the same workload, with O and LSE from the forward and a
+seeded N(0,1) dO.  TFLOPS = 10*B*H*N^2*D / time (halved for causal).
+
+Prints ONE JSON line on stdout, with the roofline of the dominant kernel and
+the oracle's CPU rate on a bounded sample as a reported baseline.
+
+  python bench.py [--op fwd|bwd] [--steps K] [--warmup W] [--workload NAME]
+                  [--sweep] [--no-cpu-baseline]
 
 ``--sweep`` also times every workload of the catalogue and prints a table on
 stderr (stdout stays one JSON line).  Only one GPU is supported: --gpus > 1
@@ -31,10 +36,14 @@ import numpy as np  # noqa: E402
 import synth  # noqa: E402
 
 METRIC = "attention fwd TFLOPS (bf16, d=128) and % of MI355X dense BF16 MFMA peak"
+METRIC_BWD = ("attention bwd TFLOPS (bf16, d=128; 10*B*H*N^2*D flops) and % of MI355X "
+              "dense BF16 MFMA peak")
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU (v_mfma 32x32x16 bf16:
 # 32768 flop per 32 clocks per SIMD, 4 SIMDs) x 2.4 GHz = 2516.6 TFLOP/s.
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
-KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_17_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "scaled_dot_product_17_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "attn_fwd.hip")
+BWD_SRC = os.path.join(CSRC, "attn_bwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -42,15 +51,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, kernel: str = "attn_fwd", src: str = KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"hbm_traffic_attn_fwd_{workload}.txt")
+    path = os.path.join(PROFILES, f"hbm_traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -59,7 +68,7 @@ def stored_traffic(workload: str):
             if ":" in ln and not ln.lstrip().startswith("#"):
                 key, val = ln.split(":", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_hash(src):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -128,9 +137,156 @@ def cpu_baseline(w, target_s: float = 12.0):
                       f"{dt:.1f} s"}
 
 
+def bwd_inputs(w):
+    """Device tensors of the backward step: q, k, v, dO, and O, LSE from attn_fwd."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    q, k, v = w.generate()
+    do = synth.normal_bf16(w.seed_base + 3, q.shape)
+    qg, kg, vg, dog = upload(q), upload(k), upload(v), upload(do)
+    del q, k, v, do
+    o, lse = sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return qg, kg, vg, dog, o, lse
+
+
+def _event_loop(fn, steps, stream):
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, [a.elapsed_time(b) for a, b in ev]
+
+
+def time_bwd(w, steps, warmup):
+    """Whole backward steps, then each of its two kernels alone (HIP events on
+    the stream they run on).  Returns a dict of timings in ms."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    qg, kg, vg, dog, o, lse = bwd_inputs(w)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    args = (w.B, w.H_q, w.H_kv, w.N, w.D, w.causal, w.scale, sp)
+
+    def step():
+        sdpa.bwd(qg, kg, vg, o, lse, dog, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                 delta=delta)
+
+    def k_dq():
+        st = sdpa.attn_bwd_dq(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), o.data_ptr(),
+                              dog.data_ptr(), lse.data_ptr(), dq.data_ptr(), delta.data_ptr(),
+                              *args)
+        assert st == 0, st
+
+    def k_dkdv():
+        st = sdpa.attn_bwd_dkdv(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), dog.data_ptr(),
+                                lse.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                *args)
+        assert st == 0, st
+
+    for _ in range(warmup):
+        step()
+    ms_step, per = _event_loop(step, steps, stream)
+    ks = max(3, steps // 2)
+    _, per_dq = _event_loop(k_dq, ks, stream)
+    _, per_kv = _event_loop(k_dkdv, ks, stream)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all()), "non-finite gradient in the benchmark"
+    del qg, kg, vg, dog, o, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "ms_event": float(np.mean(per)),
+            "dq": float(np.mean(per_dq)), "dkdv": float(np.mean(per_kv)),
+            "dq_p10_p90": [float(np.percentile(per_dq, 10)), float(np.percentile(per_dq, 90))],
+            "dkdv_p10_p90": [float(np.percentile(per_kv, 10)), float(np.percentile(per_kv, 90))]}
+
+
+def bwd_pairs(w) -> float:
+    """Allowed (query, key) pairs of the workload, by the benchmark convention
+    (N^2 per head, halved when causal)."""
+    return w.B * w.H_q * float(w.N) * w.N * (0.5 if w.causal else 1.0)
+
+
+def cpu_baseline_bwd(w):
+    """The backward oracle as it stands, on this host's cores, over one K/V head
+    of the same workload (with every query head of its group, all rows and keys):
+    rate in the metric's unit (10*D flops per allowed pair)."""
+    import oracle
+    oracle.build(force=False)
+    q, k, v = w.generate()
+    do = synth.normal_bf16(w.seed_base + 3, q.shape)
+    g = w.H_q // w.H_kv
+    sl = (slice(0, 1), slice(0, g))
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.attn_bwd_ref(q[sl], k[0:1, 0:1], v[0:1, 0:1], do[sl], w.causal, w.scale,
+                        n_threads=threads)
+    dt = time.perf_counter() - t0
+    pairs = g * (w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N)
+    return {"value": pairs * 10 * w.D / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full fp64 backward of batch 0, K/V head 0 ({g} query head(s), all "
+                      f"{w.N} rows and keys) of {w.name}, {dt:.1f} s"}
+
+
+def main_bwd(args, w):
+    log(f"[bench bwd] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} D={w.D} "
+        f"causal={w.causal}")
+    t = time_bwd(w, args.steps, args.warmup)
+    flops = 10 * w.D * bwd_pairs(w)
+    tflops = flops / (t["ms_step"] * 1e-3) / 1e12
+    # per-kernel MFMA work: dQ kernel S, dP, dQ (6*D per pair); dK/dV kernel
+    # S, dP, dV, dK (8*D per pair)
+    kflops = {"dq": 6 * w.D * bwd_pairs(w), "dkdv": 8 * w.D * bwd_pairs(w)}
+    dom = max(("dq", "dkdv"), key=lambda n: t[n])
+    achieved = kflops[dom] / (t[dom] * 1e-3) / 1e12
+    log(f"[bench bwd] {t['ms_step']:.3f} ms/step wall ({t['ms_event']:.3f} events): dQ kernel "
+        f"{t['dq']:.3f} ms, dK/dV kernel {t['dkdv']:.3f} ms; {tflops:.1f} TFLOPS = "
+        f"{100 * tflops / PEAK_TFLOPS:.1f}% of peak")
+    traffic = stored_traffic(w.name, f"attn_bwd_{dom}", BWD_SRC)
+    res = {
+        "metric": METRIC_BWD, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t["ms_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, SplitMix64 + Box-Muller)",
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "config": {"workload": w.name, "op": "bwd", "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "N": w.N, "D": w.D, "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": f"attn_bwd_{dom}_kernel",
+                     "launch_ms_mean": round(t[dom], 4),
+                     "launch_ms_p10_p90": [round(x, 4) for x in t[f"{dom}_p10_p90"]]},
+        "kernels_ms": {"attn_bwd_dq_kernel": round(t["dq"], 4),
+                       "attn_bwd_dkdv_kernel": round(t["dkdv"], 4)},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        log(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s} {'dq ms':>8s} {'dkdv ms':>8s}")
+        for name, x in synth.WORKLOADS.items():
+            tt = time_bwd(x, max(5, args.steps // 5), 3)
+            tf = 10 * x.D * bwd_pairs(x) / (tt["ms_step"] * 1e-3) / 1e12
+            log(f"{name:36s} {tt['ms_step']:9.3f} {tf:9.1f} {100 * tf / PEAK_TFLOPS:7.1f} "
+                f"{tt['dq']:8.3f} {tt['dkdv']:8.3f}")
+    if not args.no_cpu_baseline:
+        log("[bench bwd] timing the backward oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_bwd(w)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--op", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
@@ -165,6 +321,9 @@ def main():
     sdpa.load()
 
     w = synth.WORKLOADS[args.workload]
+    if args.op == "bwd":
+        main_bwd(args, w)
+        return
     log(f"[bench] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} D={w.D} causal={w.causal}")
     ms_step, ms_launch, per = time_workload(w, args.steps, args.warmup)
     tflops = w.flops / (ms_step * 1e-3) / 1e12

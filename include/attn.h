@@ -119,6 +119,23 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
                      float scale, void* stream);
 
+/*
+ * attn_bwd_dq and attn_bwd_dkdv: the two kernels of attn_bwd as separate
+ * calls (attn_bwd enqueues exactly these two, in this order).  attn_bwd_dq
+ * writes dq and delta; attn_bwd_dkdv reads delta (as written by attn_bwd_dq
+ * for the same q, k, v, o, dout, lse, causal and scale, earlier in stream
+ * order) and writes dk, dv.  Arguments, layouts, precision, ownership and
+ * errors as for attn_bwd; for attn_bwd_dkdv, delta is an input.
+ */
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, float* delta,
+                        int B, int H_q, int H_kv, int N, int D, int causal, float scale,
+                        void* stream);
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, void* dk, void* dv,
+                          int B, int H_q, int H_kv, int N, int D, int causal, float scale,
+                          void* stream);
+
 /* attn_status_string: a static, human-readable description of a status code. */
 const char* attn_status_string(int status);
 

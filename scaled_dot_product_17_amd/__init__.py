@@ -20,7 +20,8 @@ ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GQA",
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE"}
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_status_string", "attn_fwd_flops", "attn_bwd_flops")
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_string",
+            "attn_fwd_flops", "attn_bwd_flops")
 
 _lock = threading.Lock()
 _lib = None
@@ -51,6 +52,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_bwd.restype = ctypes.c_int
             lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
                 ctypes.c_float, ctypes.c_void_p]
+            lib.attn_bwd_dq.restype = ctypes.c_int
+            lib.attn_bwd_dq.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
+                ctypes.c_float, ctypes.c_void_p]
+            lib.attn_bwd_dkdv.restype = ctypes.c_int
+            lib.attn_bwd_dkdv.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
+                ctypes.c_float, ctypes.c_void_p]
             lib.attn_bwd_flops.restype = ctypes.c_double
             lib.attn_bwd_flops.argtypes = [ctypes.c_int] * 5
             _lib = lib
@@ -76,6 +83,21 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H_q, H_kv, N, D, causa
     """Direct C-ABI call with raw device pointers (ints); returns the status code."""
     return load().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H_q),
                            int(H_kv), int(N), int(D), int(bool(causal)), float(scale), stream)
+
+
+def attn_bwd_dq(q, k, v, o, dout, lse, dq, delta, B, H_q, H_kv, N, D, causal, scale,
+                stream) -> int:
+    """Direct C-ABI call (the dQ kernel alone); returns the status code."""
+    return load().attn_bwd_dq(q, k, v, o, dout, lse, dq, delta, int(B), int(H_q), int(H_kv),
+                              int(N), int(D), int(bool(causal)), float(scale), stream)
+
+
+def attn_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, H_q, H_kv, N, D, causal, scale,
+                  stream) -> int:
+    """Direct C-ABI call (the dK/dV kernel alone); returns the status code."""
+    return load().attn_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, int(B), int(H_q),
+                                int(H_kv), int(N), int(D), int(bool(causal)), float(scale),
+                                stream)
 
 
 def attn_bwd_flops(B, H_q, N, D, causal) -> float:

@@ -482,17 +482,29 @@ __global__ __launch_bounds__(KV_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams 
     }
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct Buf {
+    const void* ptr;
+    size_t bytes;
+    unsigned align;
+};
 
-extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                                float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
-                                float scale, void* stream) {
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+// Checks the sizes, the pointers (non-NULL, aligned, outputs disjoint from
+// inputs and from each other) and the device, then fills the kernel
+// parameters.  Nothing is launched unless the result is ATTN_OK.
+attn_status prepare(const Buf* ins, int n_in, const Buf* outs, int n_out, int B, int H_q,
+                    int H_kv, int N, int D, float scale, BwdParams& p) {
+    for (int i = 0; i < n_in; ++i)
+        if (!ins[i].ptr) return ATTN_ERR_NULL;
+    for (int i = 0; i < n_out; ++i)
+        if (!outs[i].ptr) return ATTN_ERR_NULL;
     if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || D <= 0) return ATTN_ERR_SHAPE;
     if (H_q % H_kv != 0) return ATTN_ERR_GQA;
     if (D != HD) return ATTN_ERR_HEAD_DIM;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    // one head panel is addressed with 32-bit byte offsets
     if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
     const int64_t n_qtiles = ((int64_t)N + DQ_ROWS - 1) / DQ_ROWS;
     const int64_t n_ktiles = ((int64_t)N + KV_KEYS - 1) / KV_KEYS;
@@ -500,36 +512,22 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
     const int64_t total_k = (int64_t)B * H_kv * n_ktiles;
     if (total_q > INT32_MAX || total_k > INT32_MAX || (int64_t)B * H_q > INT32_MAX)
         return ATTN_ERR_SHAPE;
-    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
-                           (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15;
-    if (mis != 0 || (((uintptr_t)lse | (uintptr_t)delta) & 3) != 0) return ATTN_ERR_ALIGN;
-    const size_t qb = (size_t)B * H_q * N * HD * 2;
-    const size_t kb = (size_t)B * H_kv * N * HD * 2;
-    const size_t rb = (size_t)B * H_q * N * 4;
-    const void* ins[6] = {q, k, v, o, dout, lse};
-    const size_t in_bytes[6] = {qb, kb, kb, qb, qb, rb};
-    const void* outs[4] = {dq, dk, dv, delta};
-    const size_t out_bytes[4] = {qb, kb, kb, rb};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 6; ++j)
-            if (ranges_overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
-            if (ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ATTN_ERR_ALIAS;
+    for (int i = 0; i < n_in; ++i)
+        if ((uintptr_t)ins[i].ptr % ins[i].align != 0) return ATTN_ERR_ALIGN;
+    for (int i = 0; i < n_out; ++i)
+        if ((uintptr_t)outs[i].ptr % outs[i].align != 0) return ATTN_ERR_ALIGN;
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (ranges_overlap(outs[i].ptr, outs[i].bytes, ins[j].ptr, ins[j].bytes))
+                return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < n_out; ++j)
+            if (ranges_overlap(outs[i].ptr, outs[i].bytes, outs[j].ptr, outs[j].bytes))
+                return ATTN_ERR_ALIAS;
     }
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
 
-    BwdParams p;
-    p.q = (const uint16_t*)q;
-    p.k = (const uint16_t*)k;
-    p.v = (const uint16_t*)v;
-    p.o = (const uint16_t*)o;
-    p.dout = (const uint16_t*)dout;
-    p.lse = lse;
-    p.dq = (uint16_t*)dq;
-    p.dk = (uint16_t*)dk;
-    p.dv = (uint16_t*)dv;
-    p.delta = delta;
+    p = BwdParams{};
     p.B = B;
     p.Hq = H_q;
     p.Hkv = H_kv;
@@ -541,19 +539,103 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
     p.total_k = (int)total_k;
     p.c = (float)((double)scale * 1.4426950408889634);
     p.scale = scale;
+    return ATTN_OK;
+}
 
-    hipStream_t s = (hipStream_t)stream;
+size_t q_bytes(int B, int H_q, int N) { return (size_t)B * H_q * N * HD * 2; }
+size_t kv_bytes(int B, int H_kv, int N) { return (size_t)B * H_kv * N * HD * 2; }
+size_t row_bytes(int B, int H_q, int N) { return (size_t)B * H_q * N * 4; }
+
+void launch_dq(const BwdParams& p, bool causal, hipStream_t s) {
+    if (causal)
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<true>, dim3((unsigned)p.total_q), dim3(DQ_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<false>, dim3((unsigned)p.total_q), dim3(DQ_THREADS), 0, s, p);
+}
+void launch_dkdv(const BwdParams& p, bool causal, hipStream_t s) {
+    if (causal)
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)p.total_k), dim3(KV_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)p.total_k), dim3(KV_THREADS), 0, s, p);
+}
+
+}  // namespace
+
+extern "C" attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, float* delta,
+                                   int B, int H_q, int H_kv, int N, int D, int causal, float scale,
+                                   void* stream) {
+    const Buf ins[6] = {{q, q_bytes(B, H_q, N), 16}, {k, kv_bytes(B, H_kv, N), 16},
+                        {v, kv_bytes(B, H_kv, N), 16}, {o, q_bytes(B, H_q, N), 16},
+                        {dout, q_bytes(B, H_q, N), 16}, {lse, row_bytes(B, H_q, N), 4}};
+    const Buf outs[2] = {{dq, q_bytes(B, H_q, N), 16}, {delta, row_bytes(B, H_q, N), 4}};
+    BwdParams p;
+    const attn_status st = prepare(ins, 6, outs, 2, B, H_q, H_kv, N, D, scale, p);
+    if (st != ATTN_OK) return st;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o;
+    p.dout = (const uint16_t*)dout;
+    p.lse = lse;
+    p.dq = (uint16_t*)dq;
+    p.delta = delta;
+    launch_dq(p, causal != 0, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v,
+                                     const void* dout, const float* lse, const float* delta,
+                                     void* dk, void* dv, int B, int H_q, int H_kv, int N, int D,
+                                     int causal, float scale, void* stream) {
+    const Buf ins[6] = {{q, q_bytes(B, H_q, N), 16}, {k, kv_bytes(B, H_kv, N), 16},
+                        {v, kv_bytes(B, H_kv, N), 16}, {dout, q_bytes(B, H_q, N), 16},
+                        {lse, row_bytes(B, H_q, N), 4}, {delta, row_bytes(B, H_q, N), 4}};
+    const Buf outs[2] = {{dk, kv_bytes(B, H_kv, N), 16}, {dv, kv_bytes(B, H_kv, N), 16}};
+    BwdParams p;
+    const attn_status st = prepare(ins, 6, outs, 2, B, H_q, H_kv, N, D, scale, p);
+    if (st != ATTN_OK) return st;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.dout = (const uint16_t*)dout;
+    p.lse = lse;
+    p.delta = const_cast<float*>(delta);   // only read by this kernel
+    p.dk = (uint16_t*)dk;
+    p.dv = (uint16_t*)dv;
+    launch_dkdv(p, causal != 0, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
+                                float scale, void* stream) {
+    const Buf ins[6] = {{q, q_bytes(B, H_q, N), 16}, {k, kv_bytes(B, H_kv, N), 16},
+                        {v, kv_bytes(B, H_kv, N), 16}, {o, q_bytes(B, H_q, N), 16},
+                        {dout, q_bytes(B, H_q, N), 16}, {lse, row_bytes(B, H_q, N), 4}};
+    const Buf outs[4] = {{dq, q_bytes(B, H_q, N), 16}, {dk, kv_bytes(B, H_kv, N), 16},
+                         {dv, kv_bytes(B, H_kv, N), 16}, {delta, row_bytes(B, H_q, N), 4}};
+    BwdParams p;
+    const attn_status st = prepare(ins, 6, outs, 4, B, H_q, H_kv, N, D, scale, p);
+    if (st != ATTN_OK) return st;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o;
+    p.dout = (const uint16_t*)dout;
+    p.lse = lse;
+    p.dq = (uint16_t*)dq;
+    p.dk = (uint16_t*)dk;
+    p.dv = (uint16_t*)dv;
+    p.delta = delta;
     // delta is written by the dQ kernel and read by the dK/dV kernel: same
     // stream, in this order
-    if (causal) {
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<true>, dim3((unsigned)total_q), dim3(DQ_THREADS), 0, s, p);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)total_k), dim3(KV_THREADS), 0, s, p);
-    } else {
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<false>, dim3((unsigned)total_q), dim3(DQ_THREADS), 0, s, p);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)total_k), dim3(KV_THREADS), 0, s, p);
-    }
+    const hipStream_t s = (hipStream_t)stream;
+    launch_dq(p, causal != 0, s);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
-    return ATTN_OK;
+    launch_dkdv(p, causal != 0, s);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 extern "C" double attn_bwd_flops(int B, int H_q, int N, int D, int causal) {

@@ -161,3 +161,44 @@ def test_python_bwd_rejects_bad_tensors():
     lse = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         sdpa.bwd(q, q, q, q, lse, q)            # CPU tensors
+
+
+def call_dq(**kw):
+    a = dict(BW)
+    a.update(kw)
+    return sdpa.attn_bwd_dq(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"],
+                            a["delta"], a["B"], a["H_q"], a["H_kv"], a["N"], a["D"], a["causal"],
+                            a["scale"], a["stream"])
+
+
+def call_dkdv(**kw):
+    a = dict(BW)
+    a.update(kw)
+    return sdpa.attn_bwd_dkdv(a["q"], a["k"], a["v"], a["dout"], a["lse"], a["delta"], a["dk"],
+                              a["dv"], a["B"], a["H_q"], a["H_kv"], a["N"], a["D"], a["causal"],
+                              a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), 1), (dict(dq=None), 1), (dict(delta=None), 1), (dict(N=0), 2),
+    (dict(H_q=5), 3), (dict(D=96), 4), (dict(scale=float("inf")), 5), (dict(dq=0xC00000004), 6),
+    (dict(delta=0xA00000000), 7), (dict(dq=0x600000000 + 512), 7),
+])
+def test_bwd_dq_argument_errors(lib, kw, code):
+    assert call_dq(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(delta=None), 1), (dict(dk=None), 1), (dict(k=None), 1), (dict(B=-1), 2),
+    (dict(H_kv=3), 3), (dict(D=129), 4), (dict(delta=0x1200000001), 6),
+    (dict(dk=0x1200000000), 7), (dict(dv=0xE00000000 + 16), 7), (dict(dv=0x800000000), 7),
+])
+def test_bwd_dkdv_argument_errors(lib, kw, code):
+    assert call_dkdv(**kw) == code
+
+
+def test_bwd_split_calls_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_dq() == 9 and call_dkdv() == 9

@@ -198,3 +198,46 @@ def test_bwd_workload_sampled(name):
     over = int(((lhs - rhs).abs() > tol).sum())
     say(f"  {name} sum dV: max |diff| {float((lhs - rhs).abs().max()):.3e}, over {over}")
     assert over == 0, "sum_j dV_j != sum_i dO_i"
+
+
+def test_bwd_split_calls_match():
+    """attn_bwd_dq then attn_bwd_dkdv (raw C-ABI calls) give attn_bwd's outputs bitwise."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = 1, 4, 2, 700
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=12800)
+    qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
+    for causal in (False, True):
+        o, lse = sdpa.fwd(qg, kg, vg, causal=causal, scale=SCALE)
+        dq, dk, dv, delta = sdpa.bwd(qg, kg, vg, o, lse, dog, causal=causal, scale=SCALE)
+        dq2, dk2, dv2 = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+        delta2 = torch.empty_like(lse)
+        sp = torch.cuda.current_stream().cuda_stream
+        a = (B, Hq, Hkv, N, 128, causal, SCALE, sp)
+        assert sdpa.attn_bwd_dq(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), o.data_ptr(),
+                                dog.data_ptr(), lse.data_ptr(), dq2.data_ptr(),
+                                delta2.data_ptr(), *a) == 0
+        assert sdpa.attn_bwd_dkdv(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), dog.data_ptr(),
+                                  lse.data_ptr(), delta2.data_ptr(), dk2.data_ptr(),
+                                  dv2.data_ptr(), *a) == 0
+        torch.cuda.synchronize()
+        for x, y in ((dq, dq2), (dk, dk2), (dv, dv2), (delta, delta2)):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+def test_bwd_errors_reported():
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    q, k, v, do = inputs(1, 4, 2, 64, seed=12900)
+    qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
+    o, lse = sdpa.fwd(qg, kg, vg)
+    with pytest.raises(sdpa.AttnError) as e:
+        sdpa.bwd(qg, kg, vg, o, lse, dog, scale=float("nan"))
+    assert e.value.status == 5
+    with pytest.raises(ValueError):
+        sdpa.bwd(qg, kg, vg, o, lse[:, :, :10].contiguous(), dog)
+    bad = torch.empty(1, 4, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sdpa.AttnError) as e:
+        sdpa.bwd(bad, kg[..., :64].contiguous(), vg[..., :64].contiguous(), bad, lse, bad)
+    assert e.value.status == 4
