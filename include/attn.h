@@ -106,9 +106,10 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  * B, H_q, H_kv, N, D, causal, scale, stream: as for attn_fwd.
  *
  * Precision: P and dS are rounded to bf16 (nearest even) as matrix-core
- * operands, every sum is accumulated in fp32, and the three gradients are
- * rounded to bf16 (nearest even) once at the end.  No atomics: results are
- * bitwise reproducible.
+ * operands (for dK, dS is formed from the bf16 P; for dQ from the fp32 P),
+ * every sum is accumulated in fp32, and the three gradients are rounded to
+ * bf16 (nearest even) once at the end.  No atomics: results are bitwise
+ * reproducible.
  *
  * Ownership and errors as for attn_fwd.  No output may overlap an input or
  * another output (ATTN_ERR_ALIAS); q, k, v, o, dout, dq, dk, dv must be

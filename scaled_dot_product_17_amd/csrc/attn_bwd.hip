@@ -24,12 +24,15 @@
 //     so LSE and delta are per-lane scalars) and accumulates
 //     dQ^T += K^T dS^T, reading K^T with the transposing LDS read.  It also
 //     computes delta_i from O and dO once per row and writes it out.
-//   * attn_bwd_dkdv: one workgroup = 4 waves = 128 keys of one K/V head; each
-//     wave keeps its 32 keys of K and V in VGPRs as MFMA B operands and the
-//     fp32 accumulators dK^T, dV^T (128 x 32 each).  64-row tiles of Q, dO,
-//     LSE and delta of every query head of the group stream through LDS.  Per
-//     32-row sub-block: S = Q K^T and dP = dO V^T (one key per lane), then
-//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+//   * attn_bwd_dkdv: one workgroup = 8 waves = 128 keys of one K/V head,
+//     as 4 pairs of waves that own 32 keys each.  Wave A of a pair keeps K of
+//     its keys in VGPRs (MFMA B operand) and the fp32 dV^T accumulator; wave B
+//     keeps V and dK^T.  64-row tiles of Q, dO, LSE and delta of every query
+//     head of the group stream through LDS.  Per tile, wave A computes S = Q K^T
+//     (one key per lane), P, and dV^T += dO^T P, and leaves P (bf16) in LDS;
+//     one tile later wave B computes dP = dO V^T, dS = P (dP - delta) and
+//     dK^T += Q^T dS.  dO^T and Q^T are read with the transposing LDS read.
+//     The two waves of a pair share a SIMD, so A's softmax overlaps B's MFMAs.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -57,16 +60,24 @@ constexpr int DQ_K_RING = 0;
 constexpr int DQ_V_RING = 4 * BLK_BYTES;
 constexpr int DQ_LDS = 8 * BLK_BYTES;      // 64 KiB
 
-// attn_bwd_dkdv: 4 waves x 32 keys; two stages of (Q, dO, LSE, delta) x 64 rows
-constexpr int KV_WAVES = 4;
+// attn_bwd_dkdv: 8 waves = 4 pairs x 32 keys.  In a pair, wave A (waves 0-3)
+// computes S, P and dV; wave B (waves 4-7) computes dP, dS and dK one tile
+// later, reading A's P from LDS.  Three stages of (Q, dO, LSE, delta) x 64
+// rows (A's tile, B's tile, the tile in flight) and two sets of P slots.
+constexpr int KV_PAIRS = 4;
+constexpr int KV_WAVES = 2 * KV_PAIRS;
 constexpr int KV_THREADS = KV_WAVES * 64;
-constexpr int KV_KEYS = KV_WAVES * 32;
+constexpr int KV_KEYS = KV_PAIRS * 32;
 constexpr int KV_QROWS = 64;
 constexpr int KV_TILE = KV_QROWS * ROW_BYTES;           // 16 KiB
 constexpr int KV_LSE = 2 * KV_TILE;                     // offset of LSE in a stage
 constexpr int KV_DELTA = KV_LSE + KV_QROWS * 4;         // offset of delta in a stage
 constexpr int KV_STAGE = KV_DELTA + KV_QROWS * 4;
-constexpr int KV_LDS = 2 * KV_STAGE;
+constexpr int KV_NSTAGE = 3;
+constexpr int KV_PSUB = 2 * 1024;                       // bf16 P of one 32x32 sub-block
+constexpr int KV_PSET = KV_PAIRS * (KV_QROWS / 32) * KV_PSUB;
+constexpr int KV_P = KV_NSTAGE * KV_STAGE;              // offset of the P slots
+constexpr int KV_LDS = KV_P + 2 * KV_PSET;
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *o, *dout;
@@ -321,13 +332,15 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p)
 // dK, dV
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
-__global__ __launch_bounds__(KV_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[KV_LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;   // key column owned by this lane
+    const int pair = wave % KV_PAIRS;
+    const bool is_a = wave < KV_PAIRS;   // A: S, P, dV.  B: dP, dS, dK.
+    const int l32 = lane & 31;           // key column owned by this lane
     const int hh = lane >> 5;
 
     // with a causal mask the first key tiles of a head see the most rows, and
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams 
     const int kvh = bk % p.Hkv;
     const int N = p.N;
     const int k0 = kt * KV_KEYS;
-    const int wk0 = k0 + 32 * wave;
+    const int wk0 = k0 + 32 * pair;      // first key of this pair
     const int myk = wk0 + l32;
     const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
 
@@ -350,29 +363,34 @@ __global__ __launch_bounds__(KV_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams 
     const int n_it = p.group * n_t;
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-    uint32_t dma_off[4];
+    uint32_t dma_off[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * wave + 4 * i + (lane >> 4);
         dma_off[i] = (uint32_t)(row * ROW_BYTES + (((lane & 15) ^ swz(row)) << 4));
     }
-    // stage it & 1 <- Q, dO, LSE, delta of iteration it
+    // stage it % 3 <- Q, dO, LSE, delta of iteration it
     auto issue = [&](int it) {
         if (it >= n_it) return;
         const int hq = kvh * p.group + it / n_t;
         const int t = t0 + it % n_t;
         const size_t r0 = ((size_t)b * p.Hq + hq) * (size_t)N + (size_t)t * KV_QROWS;
         const uint32_t left = (uint32_t)(N - t * KV_QROWS);
-        const uint32_t st = lds_base + (uint32_t)(it & 1) * KV_STAGE;
+        const uint32_t st = lds_base + (uint32_t)(it % KV_NSTAGE) * KV_STAGE;
         const u32x4 qr = sgpr_rsrc(p.q + r0 * HD, left * ROW_BYTES);
         const u32x4 dr = sgpr_rsrc(p.dout + r0 * HD, left * ROW_BYTES);
+        const uint32_t wrow = (uint32_t)(8 * wave) * ROW_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(qr, st + (16 * wave + 4 * i) * ROW_BYTES, dma_off[i]);
+        for (int i = 0; i < 2; ++i) lds_dma16(qr, st + wrow + 4 * i * ROW_BYTES, dma_off[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(dr, st + KV_TILE + (16 * wave + 4 * i) * ROW_BYTES, dma_off[i]);
+        for (int i = 0; i < 2; ++i) lds_dma16(dr, st + KV_TILE + wrow + 4 * i * ROW_BYTES, dma_off[i]);
         if (wave == 0) lds_dma4(sgpr_rsrc(p.lse + r0, left * 4), st + KV_LSE, (uint32_t)lane * 4);
         if (wave == 1) lds_dma4(sgpr_rsrc(p.delta + r0, left * 4), st + KV_DELTA, (uint32_t)lane * 4);
     };
+    // first row of iteration it's tile, and whether the pair computes it
+    auto tile_row = [&](int it) { return (t0 + it % n_t) * KV_QROWS; };
+    auto tile_live = [&](int rt) { return !(CAUSAL && rt + KV_QROWS - 1 < wk0); };
+    auto tile_mask = [&](int rt) { return (CAUSAL && rt < wk0 + 31) || rt + KV_QROWS > N; };
 
     TileReads rd;
     rd.init(lane);
@@ -380,105 +398,142 @@ __global__ __launch_bounds__(KV_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams 
     if (N % KV_QROWS != 0) {
         // rows past N of the tail tile must read as finite values (zeros)
         const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < KV_LDS / 16; i += KV_THREADS) *(u32x4*)(lds + 16 * i) = z;
+        for (int i = tid; i < KV_P / 16; i += KV_THREADS) *(u32x4*)(lds + 16 * i) = z;
         __syncthreads();
     }
     issue(0);
 
-    // this lane's key row (head dims 16ks + 8hh .. +7) of K and V as B
-    // operands; zeros past N
-    bf16x8 kf[8], vf[8];
+    // K (wave A) or V (wave B) of this lane's key as MFMA B operands, head
+    // dims 16ks + 8hh .. +7; zeros past N
+    bf16x8 kv[8];
     {
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_panel, (uint32_t)N * ROW_BYTES);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_panel, (uint32_t)N * ROW_BYTES);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc((is_a ? p.k : p.v) + kv_panel, (uint32_t)N * ROW_BYTES);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const uint32_t off = (uint32_t)myk * ROW_BYTES + (16 * ks + 8 * hh) * 2;
-            kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(kr, off));
-            vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(vr, off));
-        }
+        for (int ks = 0; ks < 8; ++ks)
+            kv[ks] = __builtin_bit_cast(bf16x8, buf_load16(r, (uint32_t)myk * ROW_BYTES + (16 * ks + 8 * hh) * 2));
     }
     const float c = p.c;
 
-    f32x16 dk[4], dv[4];   // dK^T, dV^T: 4 blocks of 32 head dims x 32 key columns
+    f32x16 acc[4];   // dV^T (wave A) or dK^T (wave B): 4 blocks of 32 head dims x 32 keys
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
+    for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
 
-    // One 32-row sub-block whose first query row is r0, at LDS stage offset st.
-    auto sub = [&](uint32_t st, int sb, int r0, bool mask) __attribute__((always_inline)) {
-        const uint32_t qs = st + (uint32_t)(32 * sb * ROW_BYTES);
-        const uint32_t ds = qs + KV_TILE;
-        const uint32_t ls = st + KV_LSE + (uint32_t)(32 * sb * 4);
-        f32x16 s = f32x16{}, dp = f32x16{};
+    // X = R K^T or R V^T for the 32 rows of R at LDS offset rs (S or dP)
+    auto rows_x_kv = [&](uint32_t rs, f32x16& x) __attribute__((always_inline)) {
+        x = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, qs, ks), kf[ks], s, 0, 0, 0);
+        for (int ks = 0; ks < 8; ++ks) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, rs, ks), kv[ks], x, 0, 0, 0);
+    };
+    // acc^T += T^T W for the 32 rows of T at LDS offset ts, W in accumulator order
+    auto accumulate = [&](uint32_t ts, const u32x4 (&w)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, ds, ks), vf[ks], dp, 0, 0, 0);
-        float pr[16], dsr[16];
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            // rows 8a + 4hh .. +3 of the sub-block: registers 4a .. 4a+3
-            const f32x4 l4 = *(const f32x4*)(lds + ls + (8 * a + 4 * hh) * 4);
-            const f32x4 d4 = *(const f32x4*)(lds + ls + (KV_DELTA - KV_LSE) + (8 * a + 4 * hh) * 4);
+            for (int db = 0; db < 4; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(lds, ts, db, kk),
+                                                                  __builtin_bit_cast(bf16x8, w[kk]),
+                                                                  acc[db], 0, 0, 0);
+    };
+    // P slot of (iteration parity, pair, sub-block): lane-major, two 16-byte halves
+    auto pslot = [&](int it, int sb) {
+        return (uint32_t)(KV_P + (it & 1) * KV_PSET + (pair * 2 + sb) * KV_PSUB + 16 * lane);
+    };
+
+    // Wave A, one tile: S -> P (bf16, also to LDS for wave B) -> dV^T += dO^T P.
+    auto tile_a = [&](bool masked, int it, int rt) __attribute__((always_inline)) {
+        const uint32_t st = (uint32_t)(it % KV_NSTAGE) * KV_STAGE;
+        f32x16 s[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * a + i;
-                float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[i] * LOG2E));
-                if (mask) {
-                    const int row = r0 + 8 * a + 4 * hh + i;
-                    pv = (row >= N || (CAUSAL && row < myk)) ? 0.f : pv;
+        for (int sb = 0; sb < 2; ++sb) {
+            rows_x_kv(st + 32 * sb * ROW_BYTES, s[sb]);
+            const uint32_t ls = st + KV_LSE + (uint32_t)(32 * sb * 4);
+            // register r holds row base + 8(r/4) + r%4 with base = rt + 32sb + 4hh; the
+            // allowed rows are [myk (causal) or 0, N), i.e. offsets [lo, lo + span]
+            int lo = -(1 << 20), span = 1 << 21;
+            if (masked) {
+                const int base = rt + 32 * sb + 4 * hh;
+                lo = CAUSAL ? myk - base : -base;
+                span = (N - 1 - base) - lo;
+                if (span < 0) { lo = 1 << 20; span = 0; }
+            }
+            u32x4 pw[2];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                // rows 8a + 4hh .. +3 of the sub-block are registers 4a .. 4a+3
+                const f32x4 l4 = *(const f32x4*)(lds + ls + (8 * a + 4 * hh) * 4);
+                float pv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float e = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * a + i], c, -l4[i] * LOG2E));
+                    e = (uint32_t)(8 * a + i - lo) <= (uint32_t)span ? e : 0.f;
+                    pv[i] = e;
                 }
-                pr[r] = pv;
-                dsr[r] = pv * (dp[r] - d4[i]);
+                pw[a >> 1][2 * (a & 1)] = pack_bf16(pv[0], pv[1]);
+                pw[a >> 1][2 * (a & 1) + 1] = pack_bf16(pv[2], pv[3]);
             }
+            const uint32_t ps = pslot(it, sb);
+            *(u32x4*)(lds + ps) = pw[0];
+            *(u32x4*)(lds + ps + 1024) = pw[1];
+            accumulate(st + KV_TILE + (uint32_t)(32 * sb * ROW_BYTES), pw);
         }
-        u32x4 pw[2], dsw[2];
+    };
+    // Wave B, one tile (A's tile of the previous iteration): dP, then
+    // dS = P (dP - delta) with A's bf16 P, then dK^T += Q^T dS.
+    auto tile_b = [&](int it) __attribute__((always_inline)) {
+        const uint32_t st = (uint32_t)(it % KV_NSTAGE) * KV_STAGE;
+        f32x16 dp[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int sb = 0; sb < 2; ++sb) {
+            rows_x_kv(st + KV_TILE + 32 * sb * ROW_BYTES, dp[sb]);
+            const uint32_t ps = pslot(it, sb);
+            const u32x4 pw[2] = {*(const u32x4*)(lds + ps), *(const u32x4*)(lds + ps + 1024)};
+            const uint32_t ls = st + KV_DELTA + (uint32_t)(32 * sb * 4);
+            u32x4 dsw[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pw[kk][i] = pack_bf16(pr[8 * kk + 2 * i], pr[8 * kk + 2 * i + 1]);
-                dsw[kk][i] = pack_bf16(dsr[8 * kk + 2 * i], dsr[8 * kk + 2 * i + 1]);
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 d4 = *(const f32x4*)(lds + ls + (8 * a + 4 * hh) * 4);
+                float dsv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * a + i;
+                    const uint32_t w = pw[r >> 3][(r & 7) >> 1];
+                    const float pr = __builtin_bit_cast(float, (r & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    dsv[i] = pr * (dp[sb][r] - d4[i]);
+                }
+                dsw[a >> 1][2 * (a & 1)] = pack_bf16(dsv[0], dsv[1]);
+                dsw[a >> 1][2 * (a & 1) + 1] = pack_bf16(dsv[2], dsv[3]);
             }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(lds, ds, db, kk),
-                                                                 __builtin_bit_cast(bf16x8, pw[kk]),
-                                                                 dv[db], 0, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(lds, qs, db, kk),
-                                                                 __builtin_bit_cast(bf16x8, dsw[kk]),
-                                                                 dk[db], 0, 0, 0);
+            accumulate(st + (uint32_t)(32 * sb * ROW_BYTES), dsw);
+        }
     };
 
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    for (int it = 0; it < n_it; ++it) {
-        issue(it + 1);   // the other stage, released by the barrier that ended it-1
-        const int t = t0 + it % n_t;
-        const uint32_t st = (uint32_t)(it & 1) * KV_STAGE;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int r0 = t * KV_QROWS + 32 * sb;
-            if (CAUSAL && r0 + 31 < wk0) continue;   // every row precedes every key of the wave
-            const bool mask = (CAUSAL && r0 < wk0 + 31) || (r0 + 32 > N);
-            sub(st, sb, r0, mask);
+    // Iteration it: the DMA fills tile it+1, wave A works on tile it and wave B
+    // on tile it-1; one extra iteration drains wave B.
+    // (each role runs its own copy of the loop; both pass the same n_it + 1 barriers)
+    if (is_a) {
+        for (int it = 0; it <= n_it; ++it) {
+            issue(it + 1);
+            if (it < n_it) {
+                const int rt = tile_row(it);
+                if (tile_live(rt)) tile_a(tile_mask(rt), it, rt);
+            }
+            wait_dma();
+            __syncthreads();
         }
-        wait_dma();
-        __syncthreads();
+    } else {
+        for (int it = 0; it <= n_it; ++it) {
+            issue(it + 1);
+            if (it > 0 && tile_live(tile_row(it - 1))) tile_b(it - 1);
+            wait_dma();
+            __syncthreads();
+        }
     }
 
     if (myk < N) {
-        store_row_bf16(p.dk + kv_panel + (size_t)myk * HD, dk, p.scale, hh);
-        store_row_bf16(p.dv + kv_panel + (size_t)myk * HD, dv, 1.0f, hh);
+        if (is_a) store_row_bf16(p.dv + kv_panel + (size_t)myk * HD, acc, 1.0f, hh);
+        else store_row_bf16(p.dk + kv_panel + (size_t)myk * HD, acc, p.scale, hh);
     }
 }
 

@@ -88,14 +88,16 @@ def sample_rows(B, Hq, N, rng, per_head=24, tile=128, heads=None):
 # ---------------------------------------------------------------- backward
 # Each gradient element is a sum of products in which the kernel rounds one
 # factor to bf16 (P for dV, dS for dK and dQ; nearest even, relative error at
-# most U), takes delta from a bf16 O (error up to about 2U times
-# a_i = sum_j P_ij sum_d |dO_id||V_jd|), accumulates in fp32 and rounds the
-# result to bf16 once (relative error U).  The oracle's error-scale sum ``mag``
-# is the same sum with every term replaced by its magnitude and |dP - delta|
-# widened by a_i, so |g - ref| <= U |ref| + (U + 2U + fp32 terms) * mag.
-# KAPPA = 4 covers the rounding of the operand, the delta error and fp32
-# accumulation over up to 32K terms (worst case < U/2 * mag); the 2^-24
-# relative floor covers fp32 round-off of elements whose every term is tiny.
+# most U; for dK, dS is itself formed from the bf16 P), takes delta from a bf16
+# O (error up to about 2U times a_i = sum_j P_ij sum_d |dO_id||V_jd|),
+# accumulates in fp32 and rounds the result to bf16 once (relative error U).
+# The oracle's error-scale sum ``mag`` is the same sum with every term replaced
+# by its magnitude and |dP - delta| widened by a_i.  To first order the dS
+# error is at most 2U P_ij (|dP_ij - delta_i| + a_i), so
+# |g - ref| <= U |ref| + (2U + fp32 terms) * mag; KAPPA = 4 leaves a factor of
+# about 2 for fp32 accumulation over up to 32K terms (worst case < U/2 * mag)
+# and second-order terms; the 2^-24 relative floor covers fp32 round-off of
+# elements whose every term is tiny.
 U_BF16 = 2.0 ** -8
 BWD_KAPPA = 4.0
 
