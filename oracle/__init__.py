@@ -8,6 +8,9 @@ links or calls anything here, and nothing here imports the product package.
 softmax(scale * Q K^T [causal]) V and its log-sum-exp, in double precision).
 ``attn_bwd_ref`` wraps ``attn_bwd_ref.c`` (the chain rule through that
 definition: dQ, dK, dV for a given dO, in double precision).
+``attn_decode_ref`` and ``attn_lse_merge_ref`` wrap ``attn_decode_ref.c`` (M
+query rows against an L-key cache, and the exact merge of partial results by
+their log-sum-exp).
 """
 from __future__ import annotations
 
@@ -19,7 +22,8 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "attn_ref.c"), os.path.join(_HERE, "attn_bwd_ref.c")]
+_SRCS = [os.path.join(_HERE, "attn_ref.c"), os.path.join(_HERE, "attn_bwd_ref.c"),
+         os.path.join(_HERE, "attn_decode_ref.c")]
 _LIB = os.path.join(_HERE, "libattn_ref.so")
 _lock = threading.Lock()
 _lib = None
@@ -52,6 +56,14 @@ def _bind(path: str):
         bk.restype = ctypes.c_int
         bk.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
+    if hasattr(lib, "attn_decode_ref_f64"):
+        dc = lib.attn_decode_ref_f64
+        dc.restype = ctypes.c_int
+        dc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [ctypes.c_double]
+        mg = lib.attn_lse_merge_ref_f64
+        mg.restype = ctypes.c_int
+        mg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                       ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -186,3 +198,51 @@ def call_bwd_lib(lib, q, k, v, do, causal, scale, rows=None, mags=False, n_threa
     if rows is not None:
         return (dq, mg[0]) if mags else dq
     return tuple(out + mg) if mags else tuple(out)
+
+
+def attn_decode_ref(q, k, v, causal: bool, scale: float):
+    """Oracle decode: q bf16 bits [B, H_q, M, D] against k, v bf16 bits
+    [B, H_kv, L, D]; with ``causal`` row i sees keys 0..L-M+i.  Returns (o, lse)
+    as float64 [B, H_q, M, D] and [B, H_q, M]."""
+    return call_decode_lib(_load(), q, k, v, causal, scale)
+
+
+def call_decode_lib(lib, q, k, v, causal, scale):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,H_q,M,D], k and v [B,H_kv,L,D]")
+    B, Hq, M, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch between q and k/v")
+    o = np.empty((B, Hq, M, D))
+    lse = np.empty((B, Hq, M))
+    rc = lib.attn_decode_ref_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                 lse.ctypes.data, B, Hq, Hkv, M, L, D, int(bool(causal)),
+                                 float(scale))
+    if rc != 0:
+        raise ValueError(f"attn_decode_ref_f64 failed with code {rc}")
+    return o, lse
+
+
+def attn_lse_merge_ref(o_part, lse_part):
+    """Oracle merge: o_part [rows, P, D] and lse_part [rows, P] (float64; -inf
+    marks an empty part) -> (o [rows, D], lse [rows])."""
+    return call_merge_lib(_load(), o_part, lse_part)
+
+
+def call_merge_lib(lib, o_part, lse_part):
+    o_part = np.ascontiguousarray(o_part, dtype=np.float64)
+    lse_part = np.ascontiguousarray(lse_part, dtype=np.float64)
+    if o_part.ndim != 3 or lse_part.shape != o_part.shape[:2]:
+        raise ValueError("o_part must be [rows, P, D] and lse_part [rows, P]")
+    rows, P, D = o_part.shape
+    o = np.empty((rows, D))
+    lse = np.empty((rows,))
+    rc = lib.attn_lse_merge_ref_f64(o_part.ctypes.data, lse_part.ctypes.data, rows, P, D,
+                                    o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"attn_lse_merge_ref_f64 failed with code {rc}")
+    return o, lse
