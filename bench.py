@@ -9,10 +9,15 @@ Backward (--op bwd): one step = one attn_bwd call (the dQ kernel, then the
 dK/dV kernel) on the same workload, with O and LSE from the forward and a
 seeded N(0,1) dO.  TFLOPS = 10*B*H*N^2*D / time (halved for causal).
 
+Decode (--op decode): one step = one attn_decode call (the split kernel, then
+the merge kernel) on a decode workload: M new query rows per head against an
+L-key cache, seeded N(0,1) data resident in HBM.  GB/s = algorithmic bytes
+(K and V read once, Q read once, O and LSE written once) / time.
+
 Prints ONE JSON line on stdout, with the roofline of the dominant kernel and
 the oracle's CPU rate on a bounded sample as a reported baseline.
 
-  python bench.py [--op fwd|bwd] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--op fwd|bwd|decode] [--steps K] [--warmup W] [--workload NAME]
                   [--sweep] [--no-cpu-baseline]
 
 ``--sweep`` also times every workload of the catalogue and prints a table on
@@ -36,6 +41,8 @@ import numpy as np  # noqa: E402
 import synth  # noqa: E402
 
 METRIC = "attention fwd TFLOPS (bf16, d=128) and % of MI355X dense BF16 MFMA peak"
+METRIC_DECODE = "decode attention HBM GB/s (bf16, d=128) and % of MI355X HBM bandwidth"
+PEAK_HBM_GBS = 8000.0
 METRIC_BWD = ("attention bwd TFLOPS (bf16, d=128; 10*B*H*N^2*D flops) and % of MI355X "
               "dense BF16 MFMA peak")
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU (v_mfma 32x32x16 bf16:
@@ -44,6 +51,7 @@ PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 CSRC = os.path.join(ROOT, "scaled_dot_product_17_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "attn_fwd.hip")
 BWD_SRC = os.path.join(CSRC, "attn_bwd.hip")
+DECODE_SRC = os.path.join(CSRC, "attn_decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -151,6 +159,10 @@ def bwd_inputs(w):
 
 
 def _event_loop(fn, steps, stream):
+    """Times `steps` calls of fn: (wall ms per call, per-call HIP event times in
+    ms, mean ms per call from one event pair around all calls back to back).
+    The last is the launch duration the roofline uses: an event pair around
+    every launch adds microseconds that matter for short kernels."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -162,7 +174,13 @@ def _event_loop(fn, steps, stream):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e3 / steps, [a.elapsed_time(b) for a, b in ev]
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(steps):
+        fn()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    return wall * 1e3 / steps, [a.elapsed_time(b) for a, b in ev], b0.elapsed_time(b1) / steps
 
 
 def time_bwd(w, steps, warmup):
@@ -195,16 +213,16 @@ def time_bwd(w, steps, warmup):
 
     for _ in range(warmup):
         step()
-    ms_step, per = _event_loop(step, steps, stream)
+    ms_step, per, _ = _event_loop(step, steps, stream)
     ks = max(3, steps // 2)
-    _, per_dq = _event_loop(k_dq, ks, stream)
-    _, per_kv = _event_loop(k_dkdv, ks, stream)
+    _, per_dq, mean_dq = _event_loop(k_dq, ks, stream)
+    _, per_kv, mean_kv = _event_loop(k_dkdv, ks, stream)
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all()), "non-finite gradient in the benchmark"
     del qg, kg, vg, dog, o, lse, dq, dk, dv, delta
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "ms_event": float(np.mean(per)),
-            "dq": float(np.mean(per_dq)), "dkdv": float(np.mean(per_kv)),
+            "dq": mean_dq, "dkdv": mean_kv,
             "dq_p10_p90": [float(np.percentile(per_dq, 10)), float(np.percentile(per_dq, 90))],
             "dkdv_p10_p90": [float(np.percentile(per_kv, 10)), float(np.percentile(per_kv, 90))]}
 
@@ -283,13 +301,124 @@ def main_bwd(args, w):
     print(json.dumps(res), flush=True)
 
 
+def time_decode(w, steps, warmup):
+    """Whole decode steps, then the split kernel alone (HIP events on the stream
+    they run on).  Returns a dict of timings in ms and the split count."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    q, k, v = w.generate()
+    qg, kg, vg = upload(q), upload(k), upload(v)
+    del q, k, v
+    S = sdpa.attn_decode_splits(w.B, w.H_q, w.H_kv, w.M, w.L, w.D, 0)
+    ws = torch.empty(sdpa.attn_decode_workspace_bytes(w.B, w.H_q, w.H_kv, w.M, w.L, w.D, 0),
+                     dtype=torch.uint8, device=qg.device)
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H_q, w.M), dtype=torch.float32, device=qg.device)
+    rows = w.B * w.H_q * w.M
+    op = torch.empty((rows, S, w.D), dtype=torch.float32, device=qg.device)
+    lp = torch.empty((rows, S), dtype=torch.float32, device=qg.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    args = (qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+            w.H_q, w.H_kv, w.M, w.L, w.D, w.causal, w.scale, 0, ws.data_ptr(), ws.numel(), sp)
+
+    def step():
+        # the raw C-ABI call: its host cost (a few microseconds) stays well under
+        # the kernels' time, so the GPU never waits for the next launch
+        st = sdpa.attn_decode(*args)
+        assert st == 0, st
+
+    def split():
+        st = sdpa.attn_decode_partial(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), op.data_ptr(),
+                                      lp.data_ptr(), w.B, w.H_q, w.H_kv, w.M, w.L, w.D, w.causal,
+                                      w.scale, S, sp)
+        assert st == 0, st
+
+    for _ in range(warmup):
+        step()
+    ms_step, per, _ = _event_loop(step, steps, stream)
+    _, per_split, mean_split = _event_loop(split, steps, stream)
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE in the benchmark output"
+    del qg, kg, vg, o, lse, ws, op, lp
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "ms_event": float(np.mean(per)),
+            "split": mean_split,
+            "split_p10_p90": [float(np.percentile(per_split, 10)),
+                              float(np.percentile(per_split, 90))], "n_splits": S}
+
+
+def cpu_baseline_decode(w, target_s: float = 10.0):
+    """The decode oracle as it stands (one thread): rate in the metric's unit
+    (algorithmic bytes of the workload per second)."""
+    import oracle
+    oracle.build(force=False)
+    q, k, v = w.generate()
+    reps, t0 = 0, time.perf_counter()
+    while True:   # the whole workload, repeated to about 10 s of CPU work
+        oracle.attn_decode_ref(q, k, v, w.causal, w.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt > target_s:
+            break
+    return {"value": reps * w.bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 decode of the whole {w.name} workload, {reps} time(s), {dt:.1f} s"}
+
+
+def main_decode(args, w):
+    import scaled_dot_product_17_amd as sdpa
+    log(f"[bench decode] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} M={w.M} L={w.L} D={w.D} "
+        f"causal={w.causal}")
+    t = time_decode(w, args.steps, args.warmup)
+    gbs = w.bytes / (t["ms_step"] * 1e-3) / 1e9
+    rows = w.B * w.H_q * w.M
+    # the split kernel reads K, V and Q once and writes each split's partial O and LSE
+    split_bytes = (2 * w.B * w.H_kv * w.L * w.D * 2 + w.B * w.H_q * w.M * w.D * 2
+                   + rows * t["n_splits"] * (w.D + 1) * 4)
+    achieved = split_bytes / (t["split"] * 1e-3) / 1e9
+    log(f"[bench decode] {t['ms_step'] * 1e3:.1f} us/step ({t['n_splits']} splits): "
+        f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of HBM; split kernel "
+        f"{t['split'] * 1e3:.1f} us, {achieved:.0f} GB/s")
+    traffic = stored_traffic(w.name, "attn_decode_split", DECODE_SRC)
+    res = {
+        "metric": METRIC_DECODE, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t["ms_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, SplitMix64 + Box-Muller)",
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tflops": round(w.flops / (t["ms_step"] * 1e-3) / 1e12, 2),
+        "config": {"workload": w.name, "op": "decode", "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "M": w.M, "L": w.L, "D": w.D, "causal": w.causal, "n_splits": t["n_splits"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "attn_decode_split_kernel",
+                     "launch_ms_mean": round(t["split"], 5),
+                     "launch_ms_p10_p90": [round(x, 5) for x in t["split_p10_p90"]]},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        log(f"{'workload':40s} {'us':>8s} {'GB/s':>8s} {'%HBM':>6s} {'splits':>6s}")
+        for name, x in synth.DECODE_WORKLOADS.items():
+            tt = time_decode(x, max(5, args.steps // 5), 3)
+            g = x.bytes / (tt["ms_step"] * 1e-3) / 1e9
+            log(f"{name:40s} {tt['ms_step'] * 1e3:8.1f} {g:8.0f} {100 * g / PEAK_HBM_GBS:6.1f} "
+                f"{tt['n_splits']:6d}")
+    if not args.no_cpu_baseline:
+        log("[bench decode] timing the decode oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_decode(w)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode"), default="fwd")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.DECODE_WORKLOADS),
+                    help="default: the headline workload of the op")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -320,7 +449,16 @@ def main():
         return
     sdpa.load()
 
-    w = synth.WORKLOADS[args.workload]
+    if args.op == "decode":
+        name = args.workload or synth.DECODE_HEADLINE
+        if name not in synth.DECODE_WORKLOADS:
+            sys.exit(f"{name} is not a decode workload")
+        main_decode(args, synth.DECODE_WORKLOADS[name])
+        return
+    name = args.workload or synth.HEADLINE
+    if name not in synth.WORKLOADS:
+        sys.exit(f"{name} is not a forward/backward workload")
+    w = synth.WORKLOADS[name]
     if args.op == "bwd":
         main_bwd(args, w)
         return

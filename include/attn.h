@@ -25,6 +25,8 @@
 #ifndef ATTN_H_
 #define ATTN_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -41,7 +43,8 @@ typedef enum attn_status {
     ATTN_ERR_ALIGN = 6,     /* a pointer is not 16-byte aligned                        */
     ATTN_ERR_ALIAS = 7,     /* an output range overlaps an input or the other output   */
     ATTN_ERR_LAUNCH = 8,    /* the HIP runtime rejected the kernel launch              */
-    ATTN_ERR_DEVICE = 9     /* the current device is not a gfx950 (MI350-series) GPU   */
+    ATTN_ERR_DEVICE = 9,    /* the current device is not a gfx950 (MI350-series) GPU   */
+    ATTN_ERR_WORKSPACE = 10 /* the workspace is smaller than the call needs            */
 } attn_status;
 
 /*
@@ -136,6 +139,89 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const voi
                           const float* lse, const float* delta, void* dk, void* dv,
                           int B, int H_q, int H_kv, int N, int D, int causal, float scale,
                           void* stream);
+
+/*
+ * attn_decode: enqueue split-KV decode attention on `stream`.
+ *
+ * The operation.  M query rows per (batch, query head) are the last M
+ * positions of a sequence whose L keys and values are cached.  Each row gets
+ * the forward's result (attn_fwd above) over its allowed keys: all L keys, or
+ * with `causal` keys 0 .. L - M + i for row i (0 <= i < M).  The key range is
+ * cut into splits computed in parallel, whose partial results are then merged
+ * exactly by their log-sum-exp (the "local computation plus global reduction"
+ * of the QiMeng page, section 3.1.1; see attn_lse_merge below).
+ *
+ * q      device pointer, bf16 [B, H_q, M, D].
+ * k, v   device pointers, bf16 [B, H_kv, L, D] (the cache).
+ * o      device pointer, bf16 [B, H_q, M, D], written (round to nearest even).
+ * lse    device pointer, fp32 [B, H_q, M], written (natural log), or NULL.
+ * causal 0: every row sees all L keys; non-zero: as above (needs M <= L).
+ * scale  multiplies the scores.
+ * n_splits   number of key splits, or <= 0 to let the library choose (about
+ *        2048 waves of work); it is reduced to at most one split per 32 keys.
+ * workspace  device memory of at least attn_decode_workspace_bytes(B, H_q,
+ *        H_kv, M, L, D, n_splits) bytes, 16-byte aligned, owned by the caller;
+ *        it holds the partial results between the two kernels of the call and
+ *        must not be used by other work until the call's work has finished.
+ * stream as for attn_fwd.
+ *
+ * Precision: scores and P V accumulate in fp32 on the matrix cores with P
+ * rounded to bf16; each partial O is divided by the sum of the bf16 weights
+ * it applied; partials and the merge are fp32; O is rounded to bf16 once.
+ * Errors as for attn_fwd, plus ATTN_ERR_WORKSPACE.  q, k, v and workspace must
+ * be 16-byte aligned, o and lse 4-byte aligned.
+ */
+attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H_q, int H_kv, int M, int L, int D, int causal, float scale,
+                        int n_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_partial: only the local half of attn_decode: the partial result
+ * of every key split, for a caller that merges them itself (attn_lse_merge, or
+ * a merge across devices).  Split s covers keys [32*floor(s*nb/n_splits),
+ * 32*floor((s+1)*nb/n_splits)) with nb = ceil(L/32); n_splits must be in
+ * [1, nb].
+ *
+ * o_part   device pointer, fp32 [B*H_q*M, n_splits, D], 16-byte aligned,
+ *          written: each split's softmax-weighted mean of V over its allowed
+ *          keys (0 where it has none).
+ * lse_part device pointer, fp32 [B*H_q*M, n_splits], written: each split's
+ *          natural-log LSE (-inf where it has no allowed key).
+ * Other arguments as for attn_decode.
+ */
+attn_status attn_decode_partial(const void* q, const void* k, const void* v, float* o_part,
+                                float* lse_part, int B, int H_q, int H_kv, int M, int L, int D,
+                                int causal, float scale, int n_splits, void* stream);
+
+/* attn_decode_splits: the number of key splits attn_decode uses for these
+ * arguments (n_splits <= 0: the library's choice), or 0 if they are invalid.
+ * Host-only arithmetic. */
+int attn_decode_splits(int B, int H_q, int H_kv, int M, int L, int D, int n_splits);
+
+/* attn_decode_workspace_bytes: bytes of workspace attn_decode needs for these
+ * arguments (0 if they are invalid).  Host-only arithmetic. */
+size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int M, int L, int D, int n_splits);
+
+/*
+ * attn_lse_merge: combine partial attention results over disjoint key sets,
+ * exactly: LSE = ln sum_p exp(LSE_p) and O = sum_p exp(LSE_p - LSE) O_p (the
+ * QiMeng page, section 3.1.1: the global reduction of local results).  This is
+ * also the step that merges per-GPU partials when keys are sharded.
+ *
+ * o_part   device pointer, fp32 [rows, n_parts, D], 16-byte aligned.
+ * lse_part device pointer, fp32 [rows, n_parts]; -inf marks a part with no keys
+ *          (its O_p must be finite; it gets weight 0).
+ * o        device pointer, bf16 [rows, D], written (round to nearest even).
+ * lse      device pointer, fp32 [rows], written, or NULL.  A row whose parts
+ *          are all empty gets O = 0 and LSE = -inf.
+ * D        128 in this build.
+ */
+attn_status attn_lse_merge(const float* o_part, const float* lse_part, int rows, int n_parts,
+                           int D, void* o, float* lse, void* stream);
+
+/* attn_decode_flops: 4 * D flops per allowed (row, key) pair, summed over
+ * B * H_q heads.  Host-only arithmetic. */
+double attn_decode_flops(int B, int H_q, int M, int L, int D, int causal);
 
 /* attn_status_string: a static, human-readable description of a status code. */
 const char* attn_status_string(int status);

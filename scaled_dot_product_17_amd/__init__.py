@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GQA",
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
-                7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE"}
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_string",
-            "attn_fwd_flops", "attn_bwd_flops")
+                7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE",
+                10: "ATTN_ERR_WORKSPACE"}
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
+            "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
+            "attn_fwd_flops", "attn_bwd_flops", "attn_decode_flops")
 
 _lock = threading.Lock()
 _lib = None
@@ -58,6 +60,22 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_bwd_dkdv.restype = ctypes.c_int
             lib.attn_bwd_dkdv.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
                 ctypes.c_float, ctypes.c_void_p]
+            lib.attn_decode.restype = ctypes.c_int
+            lib.attn_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            lib.attn_decode_partial.restype = ctypes.c_int
+            lib.attn_decode_partial.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+            lib.attn_decode_splits.restype = ctypes.c_int
+            lib.attn_decode_splits.argtypes = [ctypes.c_int] * 7
+            lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+            lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int] * 7
+            lib.attn_lse_merge.restype = ctypes.c_int
+            lib.attn_lse_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+            lib.attn_decode_flops.restype = ctypes.c_double
+            lib.attn_decode_flops.argtypes = [ctypes.c_int] * 6
             lib.attn_bwd_flops.restype = ctypes.c_double
             lib.attn_bwd_flops.argtypes = [ctypes.c_int] * 5
             _lib = lib
@@ -211,3 +229,102 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     if st != ATTN_OK:
         raise AttnError(st, status_string(st))
     return dq, dk, dv, delta
+
+
+def attn_decode(q, k, v, o, lse, B, H_q, H_kv, M, L, D, causal, scale, n_splits, workspace,
+                workspace_bytes, stream) -> int:
+    """Direct C-ABI call with raw device pointers (ints); returns the status code."""
+    return load().attn_decode(q, k, v, o, lse, int(B), int(H_q), int(H_kv), int(M), int(L),
+                              int(D), int(bool(causal)), float(scale), int(n_splits), workspace,
+                              int(workspace_bytes), stream)
+
+
+def attn_decode_partial(q, k, v, o_part, lse_part, B, H_q, H_kv, M, L, D, causal, scale,
+                        n_splits, stream) -> int:
+    """Direct C-ABI call (the split kernel alone); returns the status code."""
+    return load().attn_decode_partial(q, k, v, o_part, lse_part, int(B), int(H_q), int(H_kv),
+                                      int(M), int(L), int(D), int(bool(causal)), float(scale),
+                                      int(n_splits), stream)
+
+
+def attn_decode_splits(B, H_q, H_kv, M, L, D, n_splits=0) -> int:
+    return int(load().attn_decode_splits(int(B), int(H_q), int(H_kv), int(M), int(L), int(D),
+                                         int(n_splits)))
+
+
+def attn_decode_workspace_bytes(B, H_q, H_kv, M, L, D, n_splits=0) -> int:
+    return int(load().attn_decode_workspace_bytes(int(B), int(H_q), int(H_kv), int(M), int(L),
+                                                  int(D), int(n_splits)))
+
+
+def attn_lse_merge(o_part, lse_part, rows, n_parts, D, o, lse, stream) -> int:
+    """Direct C-ABI call with raw device pointers (ints); returns the status code."""
+    return load().attn_lse_merge(o_part, lse_part, int(rows), int(n_parts), int(D), o, lse,
+                                 stream)
+
+
+def attn_decode_flops(B, H_q, M, L, D, causal) -> float:
+    return load().attn_decode_flops(int(B), int(H_q), int(M), int(L), int(D), int(bool(causal)))
+
+
+def decode(q, k, v, causal: bool = False, scale: float | None = None, n_splits: int = 0,
+           out=None, lse=None, workspace=None):
+    """O, LSE of M query rows against an L-key cache, on q's current stream.
+
+    q: bf16 [B, H_q, M, D]; k, v: bf16 [B, H_kv, L, D].  With ``causal`` row i
+    sees keys 0..L-M+i.  ``workspace``: optional uint8 device tensor of at least
+    attn_decode_workspace_bytes(...) bytes.  Returns (o, lse).
+    """
+    import torch
+
+    _check_bf16("q", q)
+    B, Hq, M, D = q.shape
+    _check_bf16("k", k, device=q.device)
+    Hkv, L = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v must be [B, H_kv, L, D] with q's B and D")
+    _check_bf16("v", v, k.shape, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, M), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, M) or \
+            not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 [B, H_q, M] tensor on q's device")
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, M, L, D, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), B, Hq, Hkv, M, L, D, causal, scale, n_splits,
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_string(st))
+    return out, lse
+
+
+def lse_merge(o_part, lse_part, out=None, lse=None):
+    """Merge fp32 partials o_part [rows, P, D], lse_part [rows, P] into bf16
+    O [rows, D] and fp32 LSE [rows] on the current stream."""
+    import torch
+
+    if o_part.dtype != torch.float32 or o_part.dim() != 3 or not o_part.is_contiguous() \
+            or not o_part.is_cuda:
+        raise ValueError("o_part must be a contiguous fp32 [rows, P, D] GPU tensor")
+    rows, P, D = o_part.shape
+    if lse_part.dtype != torch.float32 or tuple(lse_part.shape) != (rows, P) or \
+            not lse_part.is_contiguous() or lse_part.device != o_part.device:
+        raise ValueError("lse_part must be a contiguous fp32 [rows, P] tensor on o_part's device")
+    out = torch.empty((rows, D), dtype=torch.bfloat16, device=o_part.device) if out is None else out
+    lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device) if lse is None else lse
+    with torch.cuda.device(o_part.device):
+        stream = torch.cuda.current_stream(o_part.device).cuda_stream
+        st = attn_lse_merge(o_part.data_ptr(), lse_part.data_ptr(), rows, P, D, out.data_ptr(),
+                            lse.data_ptr(), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_string(st))
+    return out, lse

@@ -7,7 +7,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in
+        ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "status.hip")]
 HDR = os.path.join(ROOT, "include", "attn.h")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"

@@ -55,7 +55,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
 constexpr int BR = 256;                    // query rows per workgroup
-constexpr int BC = 64;                     // keys per tile (one LDS refill, one barrier)
 constexpr int NWAVE = 8;                   // waves per workgroup
 constexpr int NTHREAD = NWAVE * 64;
 constexpr int DMA_PER_WAVE = 32 / (4 * NWAVE);   // 4-row DMA instructions per wave per key block
@@ -546,22 +545,6 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
         hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
     return ATTN_OK;
-}
-
-extern "C" const char* attn_status_string(int status) {
-    switch (status) {
-        case ATTN_OK: return "ok";
-        case ATTN_ERR_NULL: return "a required pointer is NULL";
-        case ATTN_ERR_SHAPE: return "B, H_q, H_kv, N and D must be positive and the sizes must fit";
-        case ATTN_ERR_GQA: return "H_q must be a multiple of H_kv";
-        case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (this build supports D = 128)";
-        case ATTN_ERR_SCALE: return "scale must be finite";
-        case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-        case ATTN_ERR_ALIAS: return "an output overlaps an input or the other output";
-        case ATTN_ERR_LAUNCH: return "kernel launch failed";
-        case ATTN_ERR_DEVICE: return "the current device is not a gfx950 GPU";
-        default: return "unknown status";
-    }
 }
 
 extern "C" double attn_fwd_flops(int B, int H_q, int N, int D, int causal) {

@@ -182,3 +182,65 @@ WORKLOADS = {w.name: w for w in [
 
 # The headline workload: non-causal MHA, B=2, N=16384, 16 heads, d=128.
 HEADLINE = "mha_noncausal_b2_h16_n16384"
+
+
+# --------------------------------------------------------------------------
+# Decode workloads: M new query rows per (batch, query head) against a cache
+# of L keys and values (the last M positions of the sequence).  Same seeding
+# rule: Q, K, V use seed_base + 0, + 1, + 2.
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H_q: int
+    H_kv: int
+    M: int
+    L: int
+    D: int = 128
+    causal: bool = False
+    seed_base: int = 0
+    scale: float = field(default=float(np.float32(1.0 / math.sqrt(128.0))))
+
+    @property
+    def pairs(self) -> int:
+        """Allowed (query row, key) pairs."""
+        per_head = self.M * self.L - (self.M * (self.M - 1) // 2 if self.causal else 0)
+        return self.B * self.H_q * per_head
+
+    @property
+    def flops(self) -> float:
+        return 4.0 * self.D * self.pairs
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: K and V read once, Q read once, O written once
+        (bf16) and LSE written once (fp32)."""
+        kv = 2 * self.B * self.H_kv * self.L * self.D * 2
+        qo = 2 * self.B * self.H_q * self.M * self.D * 2
+        return kv + qo + self.B * self.H_q * self.M * 4
+
+    def shapes(self):
+        return ((self.B, self.H_q, self.M, self.D), (self.B, self.H_kv, self.L, self.D))
+
+    def generate(self):
+        """(q, k, v) as uint16 bf16 bit arrays: q [B, H_q, M, D], k, v [B, H_kv, L, D]."""
+        qs, ks = self.shapes()
+        return (normal_bf16(self.seed_base + 0, qs), normal_bf16(self.seed_base + 1, ks),
+                normal_bf16(self.seed_base + 2, ks))
+
+
+DECODE_WORKLOADS = {w.name: w for w in [
+    # one new token, the pages' GQA head shape (16 query heads, 8 per K/V head),
+    # batch 8, a 32K-token cache: 256 MiB of K/V per step
+    DecodeWorkload("decode_gqa_b8_hq16_hkv2_m1_l32768", 8, 16, 2, 1, 32768, seed_base=6000),
+    # four new tokens (causal among themselves), same shape
+    DecodeWorkload("decode_gqa_b8_hq16_hkv2_m4_l32768", 8, 16, 2, 4, 32768, causal=True,
+                   seed_base=6010),
+    # MHA decode, batch 8, 8K cache: 512 MiB of K/V
+    DecodeWorkload("decode_mha_b8_h16_m1_l8192", 8, 16, 16, 1, 8192, seed_base=6020),
+    # MQA, one sequence, 32K cache
+    DecodeWorkload("decode_mqa_b1_hq16_hkv1_m1_l32768", 1, 16, 1, 1, 32768, seed_base=6030),
+]}
+
+DECODE_HEADLINE = "decode_gqa_b8_hq16_hkv2_m1_l32768"

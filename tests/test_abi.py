@@ -202,3 +202,80 @@ def test_bwd_split_calls_without_gpu_report_device(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: this case would launch on fake pointers")
     assert call_dq() == 9 and call_dkdv() == 9
+
+
+# attn_decode / attn_lse_merge (fake, far-apart addresses; validation only)
+DC = dict(q=0x100000, k=0x200000000, v=0x400000000, o=0x600000000, lse=0x800000000, B=8,
+          H_q=16, H_kv=2, M=1, L=32768, D=128, causal=0, scale=1 / math.sqrt(128), n_splits=0,
+          ws=0xA00000000, ws_bytes=1 << 30, stream=None)
+
+
+def call_dec(**kw):
+    a = dict(DC)
+    a.update(kw)
+    return sdpa.attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H_q"], a["H_kv"],
+                            a["M"], a["L"], a["D"], a["causal"], a["scale"], a["n_splits"], a["ws"],
+                            a["ws_bytes"], a["stream"])
+
+
+def test_decode_workspace_bytes(lib):
+    # 16 K/V heads x 1 column block -> 64 splits of 512 keys; partial O and LSE
+    # of 128 rows: 128*64*128*4 bytes, then 128*64*4 bytes at a 256-byte boundary
+    assert sdpa.attn_decode_workspace_bytes(8, 16, 2, 1, 32768, 128) == 128 * 64 * 128 * 4 + 128 * 64 * 4
+    # explicit split count; capped at one split per 32-key block
+    assert sdpa.attn_decode_workspace_bytes(1, 4, 1, 2, 1000, 128, 7) == 8 * 7 * 128 * 4 + 8 * 7 * 4
+    assert sdpa.attn_decode_workspace_bytes(1, 4, 1, 2, 40, 128, 50) == 8 * 2 * 128 * 4 + 8 * 2 * 4
+    assert sdpa.attn_decode_workspace_bytes(1, 3, 2, 1, 40, 128) == 0   # invalid -> 0
+    assert sdpa.attn_decode_splits(8, 16, 2, 1, 32768, 128) == 64
+    assert sdpa.attn_decode_splits(1, 16, 1, 1, 32768, 128) == 256   # L / (8 g M) cap
+    assert sdpa.attn_decode_splits(1, 4, 1, 2, 1000, 128, 7) == 7
+    assert sdpa.attn_decode_splits(1, 4, 1, 2, 40, 128, 50) == 2
+    assert sdpa.attn_decode_splits(1, 4, 1, 2, 40, 64, 5) == 0
+    assert sdpa.attn_decode_flops(2, 4, 3, 10, 128, False) == 4.0 * 2 * 4 * 128 * 30
+    assert sdpa.attn_decode_flops(2, 4, 3, 10, 128, True) == 4.0 * 2 * 4 * 128 * (8 + 9 + 10)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(ws=None), 1), (dict(o=None), 1),
+    (dict(M=0), 2), (dict(L=0), 2), (dict(causal=1, M=5, L=4), 2), (dict(L=1 << 23), 2),
+    (dict(H_q=15), 3), (dict(D=64), 4), (dict(scale=float("nan")), 5),
+    (dict(k=0x200000008), 6), (dict(ws=0xA00000004), 6), (dict(lse=0x800000002), 6),
+    (dict(o=0x100000 + 64), 7), (dict(ws=0x400000000 + 4096), 7), (dict(lse=0x600000000 + 32), 7),
+    (dict(ws_bytes=1000), 10),
+])
+def test_decode_argument_errors(lib, kw, code):
+    assert call_dec(**kw) == code
+
+
+def test_decode_valid_arguments_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_dec() == 9 and call_dec(lse=None) == 9
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 0x200000000, 10, 4, 128, 0x400000000, 0x600000000), 1),
+    ((0x100000, 0x200000000, -1, 4, 128, 0x400000000, 0x600000000), 2),
+    ((0x100000, 0x200000000, 10, 0, 128, 0x400000000, 0x600000000), 2),
+    ((0x100000, 0x200000000, 10, 4, 64, 0x400000000, 0x600000000), 4),
+    ((0x100008, 0x200000000, 10, 4, 128, 0x400000000, 0x600000000), 6),
+    ((0x100000, 0x200000000, 10, 4, 128, 0x100000 + 256, 0x600000000), 7),
+    ((0x100000, 0x200000000, 10, 4, 128, 0x400000000, 0x400000000 + 8), 7),
+])
+def test_lse_merge_argument_errors(lib, args, code):
+    assert sdpa.attn_lse_merge(*args, None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(op=None), 1), (dict(n_splits=0), 2), (dict(n_splits=1025), 2),
+    (dict(M=0), 2), (dict(H_kv=3), 3), (dict(D=96), 4), (dict(op=0x600000004), 6),
+    (dict(op=0x200000000 + 512), 7), (dict(lp=0x600000000 + 128), 7),
+])
+def test_decode_partial_argument_errors(lib, kw, code):
+    a = dict(q=0x100000, k=0x200000000, v=0x400000000, op=0x600000000, lp=0x800000000, B=8,
+             H_q=16, H_kv=2, M=1, L=32768, D=128, causal=0, scale=0.1, n_splits=7)
+    a.update(kw)
+    assert sdpa.attn_decode_partial(a["q"], a["k"], a["v"], a["op"], a["lp"], a["B"], a["H_q"],
+                                    a["H_kv"], a["M"], a["L"], a["D"], a["causal"], a["scale"],
+                                    a["n_splits"], None) == code
