@@ -63,7 +63,7 @@ constexpr int DQ_LDS = 8 * BLK_BYTES;      // 64 KiB
 // attn_bwd_dkdv: 8 waves = 4 pairs x 32 keys.  In a pair, wave A (waves 0-3)
 // computes S, P and dV; wave B (waves 4-7) computes dP, dS and dK one tile
 // later, reading A's P from LDS.  Three stages of (Q, dO, LSE, delta) x 64
-// rows (A's tile, B's tile, the tile in flight) and two sets of P slots.
+// rows (A's tile, B's tile, the tile in flight), each with its set of P slots.
 constexpr int KV_PAIRS = 4;
 constexpr int KV_WAVES = 2 * KV_PAIRS;
 constexpr int KV_THREADS = KV_WAVES * 64;
@@ -77,7 +77,7 @@ constexpr int KV_NSTAGE = 3;
 constexpr int KV_PSUB = 2 * 1024;                       // bf16 P of one 32x32 sub-block
 constexpr int KV_PSET = KV_PAIRS * (KV_QROWS / 32) * KV_PSUB;
 constexpr int KV_P = KV_NSTAGE * KV_STAGE;              // offset of the P slots
-constexpr int KV_LDS = KV_P + 2 * KV_PSET;
+constexpr int KV_LDS = KV_P + KV_NSTAGE * KV_PSET;   // P slots per stage
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *o, *dout;
@@ -434,14 +434,17 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
                                                                   __builtin_bit_cast(bf16x8, w[kk]),
                                                                   acc[db], 0, 0, 0);
     };
-    // P slot of (iteration parity, pair, sub-block): lane-major, two 16-byte halves
-    auto pslot = [&](int it, int sb) {
-        return (uint32_t)(KV_P + (it & 1) * KV_PSET + (pair * 2 + sb) * KV_PSUB + 16 * lane);
+    // P slot of (stage, pair, sub-block): lane-major, two 16-byte halves
+    auto pslot = [&](uint32_t stage, int sb) {
+        return (uint32_t)(KV_P + stage * KV_PSET + (pair * 2 + sb) * KV_PSUB + 16 * lane);
     };
 
-    // Wave A, one tile: S -> P (bf16, also to LDS for wave B) -> dV^T += dO^T P.
-    auto tile_a = [&](bool masked, int it, int rt) __attribute__((always_inline)) {
-        const uint32_t st = (uint32_t)(it % KV_NSTAGE) * KV_STAGE;
+    // Wave A, one tile in LDS stage STAGE: S -> P (bf16, also to LDS for wave
+    // B) -> dV^T += dO^T P.  MASKED: rows past N, or (causal) before this lane's key.
+    auto tile_a = [&](auto stage_t, auto mask_t, int rt) __attribute__((always_inline)) {
+        constexpr uint32_t STAGE = decltype(stage_t)::value;
+        constexpr bool MASKED = decltype(mask_t)::value;
+        constexpr uint32_t st = STAGE * KV_STAGE;
         f32x16 s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -449,8 +452,8 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
             const uint32_t ls = st + KV_LSE + (uint32_t)(32 * sb * 4);
             // register r holds row base + 8(r/4) + r%4 with base = rt + 32sb + 4hh; the
             // allowed rows are [myk (causal) or 0, N), i.e. offsets [lo, lo + span]
-            int lo = -(1 << 20), span = 1 << 21;
-            if (masked) {
+            int lo = 0, span = 0;
+            if constexpr (MASKED) {
                 const int base = rt + 32 * sb + 4 * hh;
                 lo = CAUSAL ? myk - base : -base;
                 span = (N - 1 - base) - lo;
@@ -465,27 +468,28 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float e = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * a + i], c, -l4[i] * LOG2E));
-                    e = (uint32_t)(8 * a + i - lo) <= (uint32_t)span ? e : 0.f;
+                    if constexpr (MASKED) e = (uint32_t)(8 * a + i - lo) <= (uint32_t)span ? e : 0.f;
                     pv[i] = e;
                 }
                 pw[a >> 1][2 * (a & 1)] = pack_bf16(pv[0], pv[1]);
                 pw[a >> 1][2 * (a & 1) + 1] = pack_bf16(pv[2], pv[3]);
             }
-            const uint32_t ps = pslot(it, sb);
+            const uint32_t ps = pslot(STAGE, sb);
             *(u32x4*)(lds + ps) = pw[0];
             *(u32x4*)(lds + ps + 1024) = pw[1];
             accumulate(st + KV_TILE + (uint32_t)(32 * sb * ROW_BYTES), pw);
         }
     };
-    // Wave B, one tile (A's tile of the previous iteration): dP, then
-    // dS = P (dP - delta) with A's bf16 P, then dK^T += Q^T dS.
-    auto tile_b = [&](int it) __attribute__((always_inline)) {
-        const uint32_t st = (uint32_t)(it % KV_NSTAGE) * KV_STAGE;
+    // Wave B, one tile in LDS stage STAGE (A's tile of the previous iteration):
+    // dP, then dS = P (dP - delta) with A's bf16 P, then dK^T += Q^T dS.
+    auto tile_b = [&](auto stage_t) __attribute__((always_inline)) {
+        constexpr uint32_t STAGE = decltype(stage_t)::value;
+        constexpr uint32_t st = STAGE * KV_STAGE;
         f32x16 dp[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             rows_x_kv(st + KV_TILE + 32 * sb * ROW_BYTES, dp[sb]);
-            const uint32_t ps = pslot(it, sb);
+            const uint32_t ps = pslot(STAGE, sb);
             const u32x4 pw[2] = {*(const u32x4*)(lds + ps), *(const u32x4*)(lds + ps + 1024)};
             const uint32_t ls = st + KV_DELTA + (uint32_t)(32 * sb * 4);
             u32x4 dsw[2];
@@ -509,25 +513,48 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
 
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    // Iteration it: the DMA fills tile it+1, wave A works on tile it and wave B
-    // on tile it-1; one extra iteration drains wave B.
-    // (each role runs its own copy of the loop; both pass the same n_it + 1 barriers)
+    // Iteration it: the DMA fills tile it+1 (stage (it+1)%3), wave A works on
+    // tile it (stage it%3) and wave B on tile it-1 (stage (it-1)%3); one extra
+    // iteration drains wave B.  The loop is unrolled by 3 so that every LDS
+    // offset is a constant.  Each role runs its own copy of the loop (one shared
+    // loop made the register allocator keep both roles' temporaries); both pass
+    // the same n_it + 1 barriers.
+    using S0 = std::integral_constant<uint32_t, 0>;
+    using S1 = std::integral_constant<uint32_t, 1>;
+    using S2 = std::integral_constant<uint32_t, 2>;
     if (is_a) {
-        for (int it = 0; it <= n_it; ++it) {
+        auto iter_a = [&](auto stage_t, int it) __attribute__((always_inline)) {
             issue(it + 1);
             if (it < n_it) {
                 const int rt = tile_row(it);
-                if (tile_live(rt)) tile_a(tile_mask(rt), it, rt);
+                if (tile_live(rt)) {
+                    if (tile_mask(rt)) tile_a(stage_t, std::true_type{}, rt);
+                    else tile_a(stage_t, std::false_type{}, rt);
+                }
             }
             wait_dma();
             __syncthreads();
+        };
+        for (int it = 0; it <= n_it; it += 3) {
+            iter_a(S0{}, it);
+            if (it + 1 > n_it) break;
+            iter_a(S1{}, it + 1);
+            if (it + 2 > n_it) break;
+            iter_a(S2{}, it + 2);
         }
     } else {
-        for (int it = 0; it <= n_it; ++it) {
+        auto iter_b = [&](auto prev_stage_t, int it) __attribute__((always_inline)) {
             issue(it + 1);
-            if (it > 0 && tile_live(tile_row(it - 1))) tile_b(it - 1);
+            if (it > 0 && tile_live(tile_row(it - 1))) tile_b(prev_stage_t);
             wait_dma();
             __syncthreads();
+        };
+        for (int it = 0; it <= n_it; it += 3) {
+            iter_b(S2{}, it);
+            if (it + 1 > n_it) break;
+            iter_b(S0{}, it + 1);
+            if (it + 2 > n_it) break;
+            iter_b(S1{}, it + 2);
         }
     }
 
