@@ -8,6 +8,8 @@ links or calls anything here, and nothing here imports the product package.
 softmax(scale * Q K^T [causal]) V and its log-sum-exp, in double precision).
 ``attn_bwd_ref`` wraps ``attn_bwd_ref.c`` (the chain rule through that
 definition: dQ, dK, dV for a given dO, in double precision).
+``attn_varlen_ref`` wraps ``attn_varlen_ref.c`` (a packed batch of variable-length
+sequences with an optional sliding window).
 ``attn_decode_ref`` and ``attn_lse_merge_ref`` wrap ``attn_decode_ref.c`` (M
 query rows against an L-key cache, and the exact merge of partial results by
 their log-sum-exp).
@@ -22,8 +24,8 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "attn_ref.c"), os.path.join(_HERE, "attn_bwd_ref.c"),
-         os.path.join(_HERE, "attn_decode_ref.c")]
+_SRCS = [os.path.join(_HERE, n) for n in
+         ("attn_ref.c", "attn_bwd_ref.c", "attn_decode_ref.c", "attn_varlen_ref.c")]
 _LIB = os.path.join(_HERE, "libattn_ref.so")
 _lock = threading.Lock()
 _lib = None
@@ -56,6 +58,10 @@ def _bind(path: str):
         bk.restype = ctypes.c_int
         bk.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64]
+    if hasattr(lib, "attn_varlen_ref_f64"):
+        vl = lib.attn_varlen_ref_f64
+        vl.restype = ctypes.c_int
+        vl.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 7 + [ctypes.c_double]
     if hasattr(lib, "attn_decode_ref_f64"):
         dc = lib.attn_decode_ref_f64
         dc.restype = ctypes.c_int
@@ -245,4 +251,33 @@ def call_merge_lib(lib, o_part, lse_part):
                                     o.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise ValueError(f"attn_lse_merge_ref_f64 failed with code {rc}")
+    return o, lse
+
+
+def attn_varlen_ref(q, k, v, cu_seqlens, causal: bool, scale: float, left: int = -1,
+                    right: int = -1):
+    """Oracle forward over a packed batch: q bf16 bits [H_q, total, D], k, v
+    [H_kv, total, D], cu_seqlens int32 [n_seq + 1]; row i sees keys j of its own
+    sequence with i-left <= j <= i+right (negative: unbounded) and, with
+    ``causal``, j <= i.  Returns (o, lse) as float64 [H_q, total, D], [H_q, total]."""
+    return call_varlen_lib(_load(), q, k, v, cu_seqlens, causal, scale, left, right)
+
+
+def call_varlen_lib(lib, q, k, v, cu_seqlens, causal, scale, left=-1, right=-1):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("q must be [H_q, total, D], k and v [H_kv, total, D]")
+    Hq, total, D = q.shape
+    if cu.ndim != 1 or cu.size < 2 or cu[-1] != total:
+        raise ValueError("cu_seqlens must be [n_seq + 1] ending at total")
+    o = np.empty((Hq, total, D))
+    lse = np.empty((Hq, total))
+    rc = lib.attn_varlen_ref_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                 lse.ctypes.data, cu.ctypes.data, cu.size - 1, Hq, k.shape[0], D,
+                                 int(bool(causal)), int(left), int(right), float(scale))
+    if rc != 0:
+        raise ValueError(f"attn_varlen_ref_f64 failed with code {rc}")
     return o, lse
