@@ -14,10 +14,14 @@ the merge kernel) on a decode workload: M new query rows per head against an
 L-key cache, seeded N(0,1) data resident in HBM.  GB/s = algorithmic bytes
 (K and V read once, Q read once, O and LSE written once) / time.
 
+Varlen (--op varlen): one step = one attn_fwd_varlen launch over a packed batch
+of variable-length sequences, optionally with a sliding window.  TFLOPS =
+4*D*(allowed (row, key) pairs) / time.
+
 Prints ONE JSON line on stdout, with the roofline of the dominant kernel and
 the oracle's CPU rate on a bounded sample as a reported baseline.
 
-  python bench.py [--op fwd|bwd|decode] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--op fwd|bwd|decode|varlen] [--steps K] [--warmup W] [--workload NAME]
                   [--sweep] [--no-cpu-baseline]
 
 ``--sweep`` also times every workload of the catalogue and prints a table on
@@ -41,6 +45,8 @@ import numpy as np  # noqa: E402
 import synth  # noqa: E402
 
 METRIC = "attention fwd TFLOPS (bf16, d=128) and % of MI355X dense BF16 MFMA peak"
+METRIC_VARLEN = ("packed variable-length attention fwd TFLOPS (bf16, d=128; 4*D per allowed "
+                 "(row, key) pair) and % of MI355X dense BF16 MFMA peak")
 METRIC_DECODE = "decode attention HBM GB/s (bf16, d=128) and % of MI355X HBM bandwidth"
 PEAK_HBM_GBS = 8000.0
 METRIC_BWD = ("attention bwd TFLOPS (bf16, d=128; 10*B*H*N^2*D flops) and % of MI355X "
@@ -410,14 +416,112 @@ def main_decode(args, w):
     print(json.dumps(res), flush=True)
 
 
+def main_varlen(args, w):
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    log(f"[bench varlen] {w.name}: H_q={w.H_q} H_kv={w.H_kv} total={w.total} "
+        f"sequences={len(w.lengths())} causal={w.causal} window=({w.left}, {w.right})")
+    q, k, v = w.generate()
+    qg, kg, vg = upload(q), upload(k), upload(v)
+    del q, k, v
+    cu = torch.from_numpy(w.cu_seqlens()).cuda()
+    max_len = int(w.lengths().max())
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.H_q, w.total), dtype=torch.float32, device=qg.device)
+    stream = torch.cuda.current_stream()
+    a = (qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), o.data_ptr(), lse.data_ptr(), cu.data_ptr(),
+         len(w.lengths()), max_len, w.total, w.H_q, w.H_kv, w.D, w.causal, w.left, w.right,
+         w.scale, stream.cuda_stream)
+
+    def step():
+        st = sdpa.attn_fwd_varlen(*a)
+        assert st == 0, st
+
+    for _ in range(args.warmup):
+        step()
+    ms_step, per, mean = _event_loop(step, args.steps, stream)
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE in the benchmark output"
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    achieved = w.flops / (mean * 1e-3) / 1e12
+    log(f"[bench varlen] {ms_step:.3f} ms/step: {tflops:.1f} TFLOPS = "
+        f"{100 * tflops / PEAK_TFLOPS:.1f}% of peak")
+    res = {
+        "metric": METRIC_VARLEN, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 and seeded sequence lengths)",
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "config": {"workload": w.name, "op": "varlen", "H_q": w.H_q, "H_kv": w.H_kv,
+                   "total": w.total, "sequences": len(w.lengths()), "causal": w.causal,
+                   "window": [w.left, w.right], "D": w.D, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fwd_kernel<varlen>",
+                     "launch_ms_mean": round(mean, 4),
+                     "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
+                                           round(float(np.percentile(per, 90)), 4)]},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        log(f"{'workload':40s} {'ms':>8s} {'TFLOPS':>8s} {'%peak':>6s}")
+        for name, x in synth.VARLEN_WORKLOADS.items():
+            qq, kk, vv = x.generate()
+            qx, kx, vx = upload(qq), upload(kk), upload(vv)
+            cx = torch.from_numpy(x.cu_seqlens()).cuda()
+            ox = torch.empty_like(qx)
+            lx = torch.empty((x.H_q, x.total), dtype=torch.float32, device=qx.device)
+            ax = (qx.data_ptr(), kx.data_ptr(), vx.data_ptr(), ox.data_ptr(), lx.data_ptr(),
+                  cx.data_ptr(), len(x.lengths()), int(x.lengths().max()), x.total, x.H_q, x.H_kv,
+                  x.D, x.causal, x.left, x.right, x.scale, stream.cuda_stream)
+            fn = lambda: sdpa.attn_fwd_varlen(*ax)
+            for _ in range(3):
+                fn()
+            ms, _, _ = _event_loop(fn, max(5, args.steps // 5), stream)
+            tf = x.flops / (ms * 1e-3) / 1e12
+            log(f"{name:40s} {ms:8.3f} {tf:8.1f} {100 * tf / PEAK_TFLOPS:6.1f}")
+    if not args.no_cpu_baseline:
+        log("[bench varlen] timing the varlen oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_varlen(w)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_varlen(w, target_s: float = 10.0):
+    """The varlen oracle as it stands (one thread): sequences of the workload
+    from the shortest up, on the first query head, until about 10 s of CPU work;
+    rate in the metric's unit (4*D flops per allowed pair)."""
+    import oracle
+    oracle.build(force=False)
+    q, k, v = w.generate()
+    cu = w.cu_seqlens()
+    lens = np.diff(cu)
+    g = w.H_q // w.H_kv
+    done_pairs, t0 = 0, time.perf_counter()
+    used = []
+    for s in np.argsort(lens, kind="stable"):
+        a, b = int(cu[s]), int(cu[s + 1])
+        oracle.attn_varlen_ref(q[:g, a:b], k[:1, a:b], v[:1, a:b], np.array([0, b - a], np.int32),
+                               w.causal, w.scale, w.left, w.right)
+        sub = synth.VarlenWorkload("s", g, 1, b - a, b - a, b - a, w.causal, w.left, w.right)
+        done_pairs += sub.pairs
+        used.append(b - a)
+        if time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_pairs * 4 * w.D / dt / 1e12, "unit": "TFLOPS", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 oracle on {len(used)} sequence(s) of {w.name} (lengths {used}), "
+                      f"{g} query head(s) of K/V head 0, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode"), default="fwd")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen"), default="fwd")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    choices=sorted(synth.WORKLOADS) + sorted(synth.DECODE_WORKLOADS),
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.DECODE_WORKLOADS)
+                    + sorted(synth.VARLEN_WORKLOADS),
                     help="default: the headline workload of the op")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -449,6 +553,12 @@ def main():
         return
     sdpa.load()
 
+    if args.op == "varlen":
+        name = args.workload or "varlen_causal_h16_t32768"
+        if name not in synth.VARLEN_WORKLOADS:
+            sys.exit(f"{name} is not a varlen workload")
+        main_varlen(args, synth.VARLEN_WORKLOADS[name])
+        return
     if args.op == "decode":
         name = args.workload or synth.DECODE_HEADLINE
         if name not in synth.DECODE_WORKLOADS:

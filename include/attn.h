@@ -80,6 +80,36 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      void* stream);
 
 /*
+ * attn_fwd_varlen: attn_fwd over a packed batch of variable-length sequences,
+ * with an optional sliding window.
+ *
+ * The operation.  Sequences are concatenated along the token axis and never
+ * attend across a boundary (variable sequence lengths: future work on the AVO
+ * page, section 6).  Row i of a sequence sees key j of the same sequence when
+ * i - window_left <= j <= i + window_right (a negative bound is unbounded), and
+ * with `causal` also j <= i: the local-window and band attention of page
+ * "注意力机制的本质与计算挑战", section 2.1.  Each row's O and LSE are attn_fwd's
+ * over those keys.
+ *
+ * q, o     device pointers, bf16 [H_q, total, D] (head-major: the dense layout
+ *          with B = 1 and N = total).
+ * k, v     device pointers, bf16 [H_kv, total, D].
+ * lse      device pointer, fp32 [H_q, total], or NULL.
+ * cu_seqlens device pointer, int32 [n_seq + 1]: cu_seqlens[0] = 0, non-decreasing,
+ *          cu_seqlens[n_seq] = total; sequence s is tokens cu[s] .. cu[s+1]-1.
+ *          Every sequence must be at most max_seqlen tokens long: rows past
+ *          max_seqlen are not written.  Offsets are clamped to [0, total], so
+ *          malformed offsets cannot make the kernel access memory out of range.
+ * window_left, window_right   the window (negative: no bound on that side).
+ * Other arguments, precision, ownership and errors as for attn_fwd; cu_seqlens
+ * must be 4-byte aligned and must not overlap o or lse.
+ */
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens, int n_seq, int max_seqlen, int total,
+                            int H_q, int H_kv, int D, int causal, int window_left,
+                            int window_right, float scale, void* stream);
+
+/*
  * attn_bwd: enqueue the attention backward pass on `stream`: the gradients of
  * a scalar loss with respect to q, k and v, given its gradient dout with
  * respect to the forward output.

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE",
                 10: "ATTN_ERR_WORKSPACE"}
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
+EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
             "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
             "attn_fwd_flops", "attn_bwd_flops", "attn_decode_flops")
 
@@ -60,6 +60,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_bwd_dkdv.restype = ctypes.c_int
             lib.attn_bwd_dkdv.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
                 ctypes.c_float, ctypes.c_void_p]
+            lib.attn_fwd_varlen.restype = ctypes.c_int
+            lib.attn_fwd_varlen.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 9 + [
+                ctypes.c_float, ctypes.c_void_p]
             lib.attn_decode.restype = ctypes.c_int
             lib.attn_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -90,6 +93,14 @@ def attn_fwd(q, k, v, o, lse, B, H_q, H_kv, N, D, causal, scale, stream) -> int:
     """Direct C-ABI call with raw device pointers (ints); returns the status code."""
     return load().attn_fwd(q, k, v, o, lse, int(B), int(H_q), int(H_kv), int(N), int(D),
                            int(bool(causal)), float(scale), stream)
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, n_seq, max_seqlen, total, H_q, H_kv, D, causal,
+                    window_left, window_right, scale, stream) -> int:
+    """Direct C-ABI call with raw device pointers (ints); returns the status code."""
+    return load().attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, int(n_seq), int(max_seqlen),
+                                  int(total), int(H_q), int(H_kv), int(D), int(bool(causal)),
+                                  int(window_left), int(window_right), float(scale), stream)
 
 
 def attn_fwd_flops(B, H_q, N, D, causal) -> float:
@@ -325,6 +336,42 @@ def lse_merge(o_part, lse_part, out=None, lse=None):
         stream = torch.cuda.current_stream(o_part.device).cuda_stream
         st = attn_lse_merge(o_part.data_ptr(), lse_part.data_ptr(), rows, P, D, out.data_ptr(),
                             lse.data_ptr(), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_string(st))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
+               scale: float | None = None, window=(-1, -1), out=None, lse=None):
+    """O, LSE of a packed batch: q bf16 [H_q, total, D], k, v bf16 [H_kv, total, D],
+    cu_seqlens int32 [n_seq + 1] on the same GPU.  ``window`` = (left, right):
+    row i sees keys i-left .. i+right of its sequence (negative: unbounded).
+    Returns (o, lse) with lse fp32 [H_q, total]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 3 \
+                or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D bf16 GPU tensor")
+    Hq, total, D = q.shape
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:] or k.device != q.device or \
+            v.device != q.device:
+        raise ValueError("k, v must be [H_kv, total, D] like q, on q's device")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or \
+            cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or cu_seqlens.device != q.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 [n_seq + 1] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                             max_seqlen, total, Hq, k.shape[0], D, causal, window[0], window[1],
+                             scale, stream)
     if st != ATTN_OK:
         raise AttnError(st, status_string(st))
     return out, lse

@@ -81,6 +81,10 @@ struct Params {
     int q_mode;       // 0: Q as given, 1: Q negated, 2: Q replaced by zeros
     float c;          // |scale| * log2(e), always > 0
     float lse_scale;  // |scale|
+    // packed variable-length batch (VARLEN kernels only): B = 1 and N = tokens
+    const int* cu;    // n_seq + 1 token offsets
+    int n_seq;
+    int left, right;  // window: row i sees keys i-left .. i+right (< 0: unbounded)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -156,7 +160,7 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
@@ -166,7 +170,8 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     const int l32 = lane & 31;   // query column owned by this lane
     const int hh = lane >> 5;    // which half of the wave
 
-    // ---- which (batch, head, query tile) this workgroup computes
+    // ---- which (batch, head, query tile) this workgroup computes.  VARLEN: the
+    // batch index is the sequence of a packed batch (B = 1, N = all tokens).
     const int logical = xcd_remap(blockIdx.x, p.total);
     const int bh = logical / p.n_qtiles;
     int qt = logical % p.n_qtiles;
@@ -175,25 +180,61 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
     const int N = p.N;
-    const int q0 = qt * BR;
+    // rows [s0, s1) of the panel form this tile's sequence (the whole panel when dense)
+    int s0 = 0, s1 = N;
+    if constexpr (VARLEN) {
+        s0 = min(max(p.cu[b], 0), N);
+        s1 = min(max(p.cu[b + 1], s0), N);
+        if (qt * BR >= s1 - s0) return;   // past this sequence's end: whole workgroup, no barrier yet
+    }
+    const int q0 = s0 + qt * BR;
     const int wq0 = q0 + wave * 32;       // first query row of this wave
     const int myq = wq0 + l32;            // query row of this lane
 
-    const size_t qo_panel = ((size_t)b * p.Hq + h) * (size_t)N * HD;
-    const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
-    const uint16_t* kbase = p.k + kv_panel;
-    const uint16_t* vbase = p.v + kv_panel;
+    const int pbat = VARLEN ? 0 : b;      // batch index of the panels
+    const size_t qo_panel = ((size_t)pbat * p.Hq + h) * (size_t)N * HD;
+    const size_t kv_panel = ((size_t)pbat * p.Hkv + kvh) * (size_t)N * HD;
 
-    // ---- key blocks of 32: n_blk_wg streamed through LDS, n_blk used by this wave.
-    // Causal: a wave's 32 rows start on a block boundary, so every block before
-    // its diagonal block is fully visible and only its last block is masked.
-    const int n_blk_all = (N + KB - 1) / KB;
-    int n_blk_wg = n_blk_all, n_blk = n_blk_all;
-    if (CAUSAL) {
-        n_blk_wg = min(n_blk_all, (min(q0 + BR, N) - 1) / KB + 1);
-        n_blk = min(n_blk_all, wq0 / KB + 1);
+    // ---- key blocks of 32 from key kb0: n_blk_wg streamed through LDS, n_blk used
+    // by this wave.  Dense causal: a wave's 32 rows start on a block boundary, so
+    // every block before its diagonal block is fully visible and only its last
+    // block is masked.  VARLEN: each row i sees keys [lo_i, hi_i] of its sequence
+    // (window and causal bounds); blocks before a wave's window are fully masked.
+    int kb0 = 0, n_blk_wg, n_blk;
+    int lo_i = 0, hi_i = N - 1;           // this lane's allowed keys (VARLEN)
+    int lo_max = 0, hi_min = N - 1;       // keys every valid row of the wave allows (VARLEN)
+    if constexpr (VARLEN) {
+        const int r_end = min(q0 + BR, s1);
+        kb0 = p.left >= 0 ? max(s0, q0 - p.left) : s0;
+        int khi = s1 - 1;
+        if (CAUSAL) khi = min(khi, r_end - 1);
+        if (p.right >= 0) khi = min(khi, r_end - 1 + p.right);
+        n_blk_wg = (khi - kb0) / KB + 1;
+        auto row_lo = [&](int i) { return p.left >= 0 ? max(s0, i - p.left) : s0; };
+        auto row_hi = [&](int i) {
+            int x = s1 - 1;
+            if (CAUSAL) x = min(x, i);
+            if (p.right >= 0) x = min(x, i + p.right);
+            return x;
+        };
+        lo_i = row_lo(myq);
+        hi_i = row_hi(myq);
+        const int wlast = min(wq0 + 31, s1 - 1);
+        lo_max = row_lo(wlast);
+        hi_min = row_hi(wq0);
+        n_blk = wq0 < s1 ? min(n_blk_wg, (row_hi(wlast) - kb0) / KB + 1) : 0;
+    } else {
+        const int n_blk_all = (N + KB - 1) / KB;
+        n_blk_wg = n_blk_all;
+        n_blk = n_blk_all;
+        if (CAUSAL) {
+            n_blk_wg = min(n_blk_all, (min(q0 + BR, N) - 1) / KB + 1);
+            n_blk = min(n_blk_all, wq0 / KB + 1);
+        }
+        if (wq0 >= N) n_blk = 0;   // a wave of padding rows past the end computes nothing
     }
-    if (wq0 >= N) n_blk = 0;   // a wave of padding rows past the end computes nothing
+    const uint16_t* kbase = p.k + kv_panel + (size_t)kb0 * HD;
+    const uint16_t* vbase = p.v + kv_panel + (size_t)kb0 * HD;
 
     // ---- LDS rings: K block g lives in slot g % 4 of the K ring, V block g in
     // slot g % 4 of the V ring.  Each wave copies rows 8*wave .. 8*wave+7 of a
@@ -211,7 +252,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     }
     auto dma_block = [&](const uint16_t* panel, const uint32_t* voff, int ring, int g) {
         if (g < n_blk_wg) {
-            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW_BYTES);
+            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - kb0 - g * KB) * ROW_BYTES);
             const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 4 * DMA_PER_WAVE * wave * ROW_BYTES;
 #pragma unroll
             for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
@@ -236,7 +277,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     }
 
     // ---- prologue: K blocks 0-2 and V block 0 in flight, then Q into VGPRs
-    if (N % KB != 0) {
+    if (VARLEN || N % KB != 0) {
         // rows past N of the tail block must read as zeros, not stale LDS
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -280,13 +321,19 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     };
     // key >= N (ragged tail) or key > query (causal) -> -inf
     auto needs_mask = [&](int g) {
+        if constexpr (VARLEN) {
+            const int kb = kb0 + g * KB;
+            return kb < lo_max || kb + KB - 1 > hi_min;
+        }
         return (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
     };
     auto apply_mask = [&](f32x16& s, int g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key = g * KB + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool bad = (key >= N) || (CAUSAL && key > myq);
+            const int key = kb0 + g * KB + 8 * (r >> 2) + 4 * hh + (r & 3);
+            bool bad;
+            if constexpr (VARLEN) bad = key < lo_i || key > hi_i;
+            else bad = (key >= N) || (CAUSAL && key > myq);
             s[r] = bad ? -INFINITY : s[r];
         }
     };
@@ -369,7 +416,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         // keep P_g ahead of the branch below (not sunk into its fall-through
         // path), so its VALU work interleaves with the MFMAs issued above
         asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(ls), "+v"(lbs));
-        const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM));
+        // VARLEN: a row whose window has not started yet keeps m = -inf; it moves
+        // its reference (through the rare path) at its first allowed key
+        const bool no_ref = VARLEN && m == -INFINITY && myq < s1;
+        const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM) || no_ref);
         if (valid && over != 0) {
             const float m_new = fmaxf(m, row_max(s));
             const bool move = m_new > m;
@@ -449,7 +499,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     // actually applied makes the rounding of a dominant weight cancel.
     const float l_tot = wave_swap_sum(l);
     const float inv = 1.0f / wave_swap_sum(lb);
-    if (myq < N) {
+    if (myq < s1) {
         uint16_t* orow = p.o + qo_panel + (size_t)myq * HD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -461,7 +511,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
                 *(bf16x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = ov;
             }
         if (p.lse != nullptr && hh == 0) {
-            const size_t li = ((size_t)b * p.Hq + h) * (size_t)N + myq;
+            const size_t li = ((size_t)pbat * p.Hq + h) * (size_t)N + myq;
             p.lse[li] = m * p.lse_scale + logf(l_tot);
         }
     }
@@ -488,6 +538,23 @@ bool device_is_gfx950(int dev) {
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
+}
+
+void set_scale(Params& p, float scale) {
+    const float mag = std::fabs(scale);
+    p.q_mode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
+    p.c = (float)((double)(mag > 0.f ? mag : 1.0f) * 1.4426950408889634);
+    p.lse_scale = mag;
+}
+
+template <bool VARLEN>
+attn_status launch_fwd(const Params& p, bool causal, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (causal)
+        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -520,7 +587,7 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
 
-    Params p;
+    Params p = {};
     p.q = (const uint16_t*)q;
     p.k = (const uint16_t*)k;
     p.v = (const uint16_t*)v;
@@ -533,18 +600,60 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     p.group = H_q / H_kv;
     p.n_qtiles = (int)n_qtiles;
     p.total = (int)total;
-    const float mag = std::fabs(scale);
-    p.q_mode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
-    p.c = (float)((double)(mag > 0.f ? mag : 1.0f) * 1.4426950408889634);
-    p.lse_scale = mag;
+    set_scale(p, scale);
+    return launch_fwd<false>(p, causal != 0, stream);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    if (causal)
-        hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
-    else
-        hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
-    return ATTN_OK;
+extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const int* cu_seqlens, int n_seq,
+                                       int max_seqlen, int total, int H_q, int H_kv, int D,
+                                       int causal, int window_left, int window_right, float scale,
+                                       void* stream) {
+    if (!q || !k || !v || !o || !cu_seqlens) return ATTN_ERR_NULL;
+    if (n_seq <= 0 || max_seqlen <= 0 || total <= 0 || H_q <= 0 || H_kv <= 0 || D <= 0)
+        return ATTN_ERR_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_GQA;
+    if (D != HD) return ATTN_ERR_HEAD_DIM;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if ((int64_t)total * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    const int64_t n_qtiles = ((int64_t)max_seqlen + BR - 1) / BR;
+    const int64_t grid = (int64_t)n_seq * H_q * n_qtiles;
+    if (grid > INT32_MAX || n_seq == INT32_MAX) return ATTN_ERR_SHAPE;
+    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
+    if (mis != 0 || (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) != 0) return ATTN_ERR_ALIGN;
+    const size_t qo_bytes = (size_t)H_q * total * HD * 2;
+    const size_t kv_bytes = (size_t)H_kv * total * HD * 2;
+    const size_t lse_bytes = lse ? (size_t)H_q * total * 4 : 0;
+    const size_t cu_bytes = (size_t)(n_seq + 1) * 4;
+    const void* ins[4] = {q, k, v, cu_seqlens};
+    const size_t in_bytes[4] = {qo_bytes, kv_bytes, kv_bytes, cu_bytes};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(o, qo_bytes, ins[i], in_bytes[i]) || (lse && overlaps(lse, lse_bytes, ins[i], in_bytes[i])))
+            return ATTN_ERR_ALIAS;
+    if (lse && overlaps(lse, lse_bytes, o, qo_bytes)) return ATTN_ERR_ALIAS;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
+
+    Params p = {};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    p.B = n_seq;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.N = total;
+    p.group = H_q / H_kv;
+    p.n_qtiles = (int)n_qtiles;
+    p.total = (int)grid;
+    p.cu = cu_seqlens;
+    p.n_seq = n_seq;
+    p.left = window_left < 0 ? -1 : window_left;
+    p.right = window_right < 0 ? -1 : window_right;
+    set_scale(p, scale);
+    return launch_fwd<true>(p, causal != 0, stream);
 }
 
 extern "C" double attn_fwd_flops(int B, int H_q, int N, int D, int causal) {

@@ -244,3 +244,83 @@ DECODE_WORKLOADS = {w.name: w for w in [
 ]}
 
 DECODE_HEADLINE = "decode_gqa_b8_hq16_hkv2_m1_l32768"
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length batches: sequences concatenated along the token axis
+# (q [H_q, total, D], k, v [H_kv, total, D]) with an optional sliding window.
+# Lengths come from the same counter-based generator (seed_base + 3), so the
+# batch is reproducible.  Q, K, V use seed_base + 0, + 1, + 2.
+# --------------------------------------------------------------------------
+def _seq_lengths(seed: int, total: int, lo: int, hi: int) -> np.ndarray:
+    """Lengths in [lo, hi] summing exactly to ``total``, drawn from uniforms
+    derived from the generator's bf16 normals (|z| mapped through exp)."""
+    z = bf16_bits_to_f32(normal_bf16(seed, (4096,))).astype(np.float64)
+    u = 1.0 - np.exp(-np.abs(z))          # in [0, 1), deterministic
+    out, acc, t = [], 0, 0
+    while acc < total:
+        n = int(lo + u[t % u.size] * (hi - lo + 1))
+        n = min(max(n, lo), hi, total - acc)
+        out.append(n)
+        acc += n
+        t += 1
+    return np.array(out, dtype=np.int32)
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    H_q: int
+    H_kv: int
+    total: int
+    min_len: int
+    max_len: int
+    causal: bool = True
+    left: int = -1
+    right: int = -1
+    D: int = 128
+    seed_base: int = 0
+    scale: float = field(default=float(np.float32(1.0 / math.sqrt(128.0))))
+
+    def lengths(self) -> np.ndarray:
+        return _seq_lengths(self.seed_base + 3, self.total, self.min_len, self.max_len)
+
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths())]).astype(np.int32)
+
+    @property
+    def pairs(self) -> int:
+        """Allowed (row, key) pairs of one head, times H_q."""
+        tot = 0
+        for n in self.lengths().tolist():
+            i = np.arange(n, dtype=np.int64)
+            lo = np.maximum(0, i - self.left) if self.left >= 0 else np.zeros(n, np.int64)
+            hi = np.full(n, n - 1, np.int64)
+            if self.causal:
+                hi = np.minimum(hi, i)
+            if self.right >= 0:
+                hi = np.minimum(hi, i + self.right)
+            tot += int(np.maximum(hi - lo + 1, 0).sum())
+        return tot * self.H_q
+
+    @property
+    def flops(self) -> float:
+        return 4.0 * self.D * self.pairs
+
+    def generate(self):
+        """(q, k, v) as uint16 bf16 bits: q [H_q, total, D], k, v [H_kv, total, D]."""
+        qs, ks = (self.H_q, self.total, self.D), (self.H_kv, self.total, self.D)
+        return (normal_bf16(self.seed_base + 0, qs), normal_bf16(self.seed_base + 1, ks),
+                normal_bf16(self.seed_base + 2, ks))
+
+
+VARLEN_WORKLOADS = {w.name: w for w in [
+    # 32768 tokens in sequences of 512..8192 tokens, 16 heads, causal
+    VarlenWorkload("varlen_causal_h16_t32768", 16, 16, 32768, 512, 8192, seed_base=7000),
+    # same tokens, GQA (8 query heads per K/V head), causal with a 4096-token window
+    VarlenWorkload("varlen_swa4096_gqa_hq16_hkv2_t32768", 16, 2, 32768, 512, 16384, left=4096,
+                   seed_base=7010),
+    # one 32768-token sequence, 16 heads, a symmetric local window of 1024 tokens
+    VarlenWorkload("local1024_h16_t32768", 16, 16, 32768, 32768, 32768, causal=False, left=1024,
+                   right=1024, seed_base=7020),
+]}

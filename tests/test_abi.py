@@ -279,3 +279,34 @@ def test_decode_partial_argument_errors(lib, kw, code):
     assert sdpa.attn_decode_partial(a["q"], a["k"], a["v"], a["op"], a["lp"], a["B"], a["H_q"],
                                     a["H_kv"], a["M"], a["L"], a["D"], a["causal"], a["scale"],
                                     a["n_splits"], None) == code
+
+
+# attn_fwd_varlen (fake, far-apart addresses; validation only)
+VL = dict(q=0x100000, k=0x200000000, v=0x400000000, o=0x600000000, lse=0x800000000,
+          cu=0xA00000000, n_seq=4, max_seqlen=1000, total=3000, H_q=8, H_kv=2, D=128, causal=1,
+          left=-1, right=-1, scale=0.1, stream=None)
+
+
+def call_varlen(**kw):
+    a = dict(VL)
+    a.update(kw)
+    return sdpa.attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["n_seq"],
+                                a["max_seqlen"], a["total"], a["H_q"], a["H_kv"], a["D"],
+                                a["causal"], a["left"], a["right"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), 1), (dict(q=None), 1), (dict(n_seq=0), 2), (dict(max_seqlen=0), 2),
+    (dict(total=0), 2), (dict(total=1 << 23), 2), (dict(H_q=7), 3), (dict(D=64), 4),
+    (dict(scale=float("inf")), 5), (dict(cu=0xA00000002), 6), (dict(v=0x400000008), 6),
+    (dict(o=0xA00000000 - 64), 7), (dict(lse=0x100000 + 128), 7), (dict(lse=0x600000000 + 16), 7),
+])
+def test_varlen_argument_errors(lib, kw, code):
+    assert call_varlen(**kw) == code
+
+
+def test_varlen_valid_arguments_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_varlen() == 9 and call_varlen(left=100, right=0, lse=None) == 9
