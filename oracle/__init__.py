@@ -13,6 +13,9 @@ sequences with an optional sliding window).
 ``attn_decode_ref`` and ``attn_lse_merge_ref`` wrap ``attn_decode_ref.c`` (M
 query rows against an L-key cache, and the exact merge of partial results by
 their log-sum-exp).
+``attn_fp8_ref`` wraps ``attn_fp8_ref.c`` (the forward on e4m3 inputs with
+per-tensor scales, evaluated exactly on the values the codes stand for) and
+``e4m3_decode`` its code-to-value rule.
 """
 from __future__ import annotations
 
@@ -25,7 +28,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, n) for n in
-         ("attn_ref.c", "attn_bwd_ref.c", "attn_decode_ref.c", "attn_varlen_ref.c")]
+         ("attn_ref.c", "attn_bwd_ref.c", "attn_decode_ref.c", "attn_varlen_ref.c",
+          "attn_fp8_ref.c")]
 _LIB = os.path.join(_HERE, "libattn_ref.so")
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +66,14 @@ def _bind(path: str):
         vl = lib.attn_varlen_ref_f64
         vl.restype = ctypes.c_int
         vl.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 7 + [ctypes.c_double]
+    if hasattr(lib, "attn_fp8_ref_f64"):
+        f8 = lib.attn_fp8_ref_f64
+        f8.restype = ctypes.c_int
+        f8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_double] * 3 + [ctypes.c_void_p] * 3 + [
+            ctypes.c_int] * 6 + [ctypes.c_double] * 3 + [ctypes.c_void_p, ctypes.c_int64]
+        dec = lib.e4m3_decode
+        dec.restype = ctypes.c_double
+        dec.argtypes = [ctypes.c_uint8]
     if hasattr(lib, "attn_decode_ref_f64"):
         dc = lib.attn_decode_ref_f64
         dc.restype = ctypes.c_int
@@ -281,3 +293,60 @@ def call_varlen_lib(lib, q, k, v, cu_seqlens, causal, scale, left=-1, right=-1):
     if rc != 0:
         raise ValueError(f"attn_varlen_ref_f64 failed with code {rc}")
     return o, lse
+
+
+def e4m3_decode(codes):
+    """Values (float64) of e4m3 codes (uint8 array), by the oracle's decode rule."""
+    return call_e4m3_decode(_load(), codes)
+
+
+def call_e4m3_decode(lib, codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib.e4m3_decode(i) for i in range(256)])
+    return table[c]
+
+
+def attn_fp8_ref(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, causal: bool,
+                 scale: float, rows=None, mags=None):
+    """Oracle forward on e4m3 inputs: q8 uint8 codes [B, H_q, N, D], k8, v8
+    [B, H_kv, N, D]; the tensors are descale_x * value(code).  ``rows``: optional
+    int64 flat row ids ((b*H_q + h)*N + i).  ``mags``: optional (w_rel, w_floor),
+    then the error-scale sums of the weight rounding are returned too.
+
+    Returns (o, lse) or (o, lse, mag) as float64, shaped [B, H_q, N, D] and
+    [B, H_q, N], or [len(rows), D] and [len(rows)].
+    """
+    return call_fp8_lib(_load(), q8, k8, v8, descale_q, descale_k, descale_v, causal, scale,
+                        rows, mags)
+
+
+def call_fp8_lib(lib, q8, k8, v8, descale_q, descale_k, descale_v, causal, scale, rows=None,
+                 mags=None):
+    q8 = np.ascontiguousarray(q8, dtype=np.uint8)
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    v8 = np.ascontiguousarray(v8, dtype=np.uint8)
+    if q8.ndim != 4 or k8.ndim != 4 or v8.shape != k8.shape:
+        raise ValueError("q8 must be [B,H_q,N,D], k8 and v8 [B,H_kv,N,D]")
+    B, Hq, N, D = q8.shape
+    Hkv = k8.shape[1]
+    if k8.shape[0] != B or k8.shape[2] != N or k8.shape[3] != D:
+        raise ValueError("shape mismatch between q8 and k8/v8")
+    if rows is None:
+        o = np.empty((B, Hq, N, D))
+        lse = np.empty((B, Hq, N))
+        rows_p, n_rows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        o = np.empty((rows.size, D))
+        lse = np.empty((rows.size,))
+        rows_p, n_rows = rows.ctypes.data, rows.size
+    mag = np.empty_like(o) if mags is not None else None
+    w_rel, w_floor = mags if mags is not None else (0.0, 0.0)
+    rc = lib.attn_fp8_ref_f64(q8.ctypes.data, k8.ctypes.data, v8.ctypes.data, float(descale_q),
+                              float(descale_k), float(descale_v), o.ctypes.data, lse.ctypes.data,
+                              None if mag is None else mag.ctypes.data, B, Hq, Hkv, N, D,
+                              int(bool(causal)), float(scale), float(w_rel), float(w_floor),
+                              rows_p, n_rows)
+    if rc != 0:
+        raise ValueError(f"attn_fp8_ref_f64 failed with code {rc}")
+    return (o, lse, mag) if mags is not None else (o, lse)

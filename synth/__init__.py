@@ -185,6 +185,106 @@ HEADLINE = "mha_noncausal_b2_h16_n16384"
 
 
 # --------------------------------------------------------------------------
+# FP8 (e4m3) inputs.  e4m3 (the OCP 8-bit format): sign, 4 exponent bits with
+# bias 7, 3 mantissa bits, subnormals at exponent field 0, no infinities, codes
+# 0x7F and 0xFF are NaN, largest finite value 448.  Inputs are drawn as
+# normals z, divided by a per-tensor descale factor s and rounded to the nearest
+# e4m3 value (ties to the even code, saturating at +-448): the tensor the codes
+# stand for is s * value(code).
+# --------------------------------------------------------------------------
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the codes 0x00 .. 0x7E (increasing)."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8.0 + m) * np.exp2(e - 10.0))
+
+
+_E4M3_POS = _e4m3_positive_values()
+
+
+def f64_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """float64 -> e4m3 codes (uint8), round to nearest with ties to the even code,
+    saturating at +-448.  NaN inputs are not produced by this module."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def _fill_e4m3(out: np.ndarray, seed: int, pos: int, cnt: int, inv_descale: float) -> None:
+    z = normal_f64(seed, pos // 2, (cnt + 1) // 2)[:cnt]
+    out[pos:pos + cnt] = f64_to_e4m3(z * inv_descale)
+
+
+def normal_e4m3(seed: int, shape, descale: float) -> np.ndarray:
+    """e4m3 codes of ``z / descale`` for iid standard normals z, C-order ``shape``
+    (same element-to-stream rule as ``normal_bf16``)."""
+    total = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(total, dtype=np.uint8)
+    inv = 1.0 / float(descale)
+    jobs = [(p, min(_CHUNK, total - p)) for p in range(0, total, _CHUNK)]
+    if len(jobs) <= 1:
+        for p, c in jobs:
+            _fill_e4m3(out, seed, p, c, inv)
+    else:
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(lambda j: _fill_e4m3(out, seed, j[0], j[1], inv), jobs))
+    return out.reshape(shape)
+
+
+# Descale of the FP8 workloads: unit normals up to |z| = 6 map onto the full
+# e4m3 range (per-tensor amax scaling with amax taken as 6).
+FP8_DESCALE = float(np.float32(6.0 / 448.0))
+
+
+@dataclass(frozen=True)
+class Fp8Workload:
+    name: str
+    B: int
+    H_q: int
+    H_kv: int
+    N: int
+    D: int = 128
+    causal: bool = False
+    seed_base: int = 0
+    scale: float = field(default=float(np.float32(1.0 / math.sqrt(128.0))))
+    descale_q: float = FP8_DESCALE
+    descale_k: float = FP8_DESCALE
+    descale_v: float = FP8_DESCALE
+
+    @property
+    def flops(self) -> float:
+        f = 4.0 * self.B * self.H_q * self.N * self.N * self.D
+        return f / 2 if self.causal else f
+
+    def shapes(self):
+        return ((self.B, self.H_q, self.N, self.D), (self.B, self.H_kv, self.N, self.D))
+
+    def generate(self):
+        """(q8, k8, v8) as uint8 e4m3 codes in [B, H, N, D] layout."""
+        qs, ks = self.shapes()
+        return (normal_e4m3(self.seed_base + 0, qs, self.descale_q),
+                normal_e4m3(self.seed_base + 1, ks, self.descale_k),
+                normal_e4m3(self.seed_base + 2, ks, self.descale_v))
+
+
+FP8_WORKLOADS = {w.name: w for w in [
+    Fp8Workload("fp8_mha_tiny_b1_h2_n256", 1, 2, 2, 256, seed_base=8000),
+    Fp8Workload("fp8_gqa_b8_hq16_hkv2_n2048", 8, 16, 2, 2048, seed_base=8010),
+    Fp8Workload("fp8_mha_noncausal_b2_h16_n16384", 2, 16, 16, 16384, seed_base=8020),
+    Fp8Workload("fp8_mha_causal_b2_h16_n16384", 2, 16, 16, 16384, causal=True, seed_base=8030),
+]}
+
+# The FP8 counterpart of the headline workload (non-causal MHA, B=2, N=16384).
+FP8_HEADLINE = "fp8_mha_noncausal_b2_h16_n16384"
+
+
+# --------------------------------------------------------------------------
 # Decode workloads: M new query rows per (batch, query head) against a cache
 # of L keys and values (the last M positions of the sequence).  Same seeding
 # rule: Q, K, V use seed_base + 0, + 1, + 2.

@@ -58,3 +58,29 @@ def test_workload_catalogue():
     assert all(x.H_q % x.H_kv == 0 for x in synth.WORKLOADS.values())
     seeds = [s for x in synth.WORKLOADS.values() for s in (x.seed_base, x.seed_base + 2)]
     assert len(set(seeds)) == len(seeds)
+
+
+def test_e4m3_encoder_matches_torch_and_ties_to_even():
+    """f64_to_e4m3 against torch's float8_e4m3fn cast on a dense grid (in range),
+    exact midpoints (ties to the even code) and saturation at 448."""
+    x = np.concatenate([np.linspace(-448, 448, 400001), np.linspace(-0.02, 0.02, 40001)])
+    x = x.astype(np.float32).astype(np.float64)   # torch's cast goes through float32
+    got = synth.f64_to_e4m3(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    # midpoints 1.0625 (between 1.0 = 0x38 and 1.125 = 0x39) and 1.1875 (0x39 / 0x3A)
+    assert list(synth.f64_to_e4m3(np.array([1.0625, 1.1875, -1.0625]))) == [0x38, 0x3A, 0xB8]
+    assert list(synth.f64_to_e4m3(np.array([500.0, -1e9]))) == [0x7E, 0xFE]
+
+
+def test_e4m3_normals():
+    w = synth.FP8_WORKLOADS["fp8_mha_tiny_b1_h2_n256"]
+    q8, k8, v8 = w.generate()
+    assert q8.dtype == np.uint8 and q8.shape == (1, 2, 256, 128)
+    again = synth.normal_e4m3(w.seed_base, q8.shape, w.descale_q)
+    assert np.array_equal(q8, again)
+    z = synth.normal_f64(w.seed_base, 0, 8)
+    assert np.array_equal(q8.reshape(-1)[:16], synth.f64_to_e4m3(z / w.descale_q))
+    vals = torch.from_numpy(k8).view(torch.float8_e4m3fn).double().numpy() * w.descale_k
+    assert abs(vals.mean()) < 0.02 and abs(vals.std() - 1.0) < 0.02
+    assert not np.isnan(vals).any()
