@@ -18,10 +18,14 @@ Varlen (--op varlen): one step = one attn_fwd_varlen launch over a packed batch
 of variable-length sequences, optionally with a sliding window.  TFLOPS =
 4*D*(allowed (row, key) pairs) / time.
 
+FP8 (--op fp8): one step = one attn_fwd_fp8 launch over the FP8 counterpart of
+the headline workload (e4m3 Q, K, V with per-tensor descales, bf16 O).  TFLOPS
+= 4*B*H*N^2*D / time (halved for causal), against the dense FP8 MFMA peak.
+
 Prints ONE JSON line on stdout, with the roofline of the dominant kernel and
 the oracle's CPU rate on a bounded sample as a reported baseline.
 
-  python bench.py [--op fwd|bwd|decode|varlen] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--op fwd|bwd|decode|varlen|fp8] [--steps K] [--warmup W] [--workload NAME]
                   [--sweep] [--no-cpu-baseline]
 
 ``--sweep`` also times every workload of the catalogue and prints a table on
@@ -54,10 +58,16 @@ METRIC_BWD = ("attention bwd TFLOPS (bf16, d=128; 10*B*H*N^2*D flops) and % of M
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU (v_mfma 32x32x16 bf16:
 # 32768 flop per 32 clocks per SIMD, 4 SIMDs) x 2.4 GHz = 2516.6 TFLOP/s.
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+# dense e4m3 MFMA peak: v_mfma_scale 32x32x64 f8 does 131072 flop per 64 clocks
+# per SIMD, twice the bf16 rate: 5033.2 TFLOP/s.
+PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS
+METRIC_FP8 = ("attention fwd TFLOPS (FP8 e4m3 Q/K/V with per-tensor descales, bf16 O, d=128) "
+              "and % of MI355X dense FP8 MFMA peak")
 CSRC = os.path.join(ROOT, "scaled_dot_product_17_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "attn_fwd.hip")
 BWD_SRC = os.path.join(CSRC, "attn_bwd.hip")
 DECODE_SRC = os.path.join(CSRC, "attn_decode.hip")
+FP8_SRC = os.path.join(CSRC, "attn_fwd_fp8.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -513,15 +523,107 @@ def cpu_baseline_varlen(w, target_s: float = 10.0):
                       f"{g} query head(s) of K/V head 0, {dt:.1f} s"}
 
 
+def main_fp8(args, w):
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    log(f"[bench fp8] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} D={w.D} "
+        f"causal={w.causal} descales=({w.descale_q:.6g}, {w.descale_k:.6g}, {w.descale_v:.6g})")
+    q8, k8, v8 = w.generate()
+    qg, kg, vg = (torch.from_numpy(x).cuda() for x in (q8, k8, v8))
+    del q8, k8, v8
+    o = torch.empty((w.B, w.H_q, w.N, w.D), dtype=torch.bfloat16, device=qg.device)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=qg.device)
+    stream = torch.cuda.current_stream()
+    a = (qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H_q,
+         w.H_kv, w.N, w.D, w.causal, w.scale, w.descale_q, w.descale_k, w.descale_v,
+         stream.cuda_stream)
+
+    def step():
+        st = sdpa.attn_fwd_fp8(*a)
+        assert st == 0, st
+
+    for _ in range(args.warmup):
+        step()
+    ms_step, per, mean = _event_loop(step, args.steps, stream)
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE in the benchmark output"
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    achieved = w.flops / (mean * 1e-3) / 1e12
+    log(f"[bench fp8] {ms_step:.3f} ms/step: {tflops:.1f} TFLOPS = "
+        f"{100 * tflops / PEAK_FP8_TFLOPS:.1f}% of the FP8 peak "
+        f"({100 * tflops / PEAK_TFLOPS:.1f}% of the bf16 peak)")
+    res = {
+        "metric": METRIC_FP8, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic (seeded N(0,1) rounded to e4m3 with a per-tensor descale)",
+        "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+        "config": {"workload": w.name, "op": "fp8", "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "N": w.N, "D": w.D, "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_FP8_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": stored_traffic(w.name, "attn_fwd_fp8", FP8_SRC),
+                     "kernel": "attn_fwd_fp8_kernel", "launch_ms_mean": round(mean, 4),
+                     "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
+                                           round(float(np.percentile(per, 90)), 4)]},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        log(f"{'workload':40s} {'ms':>8s} {'TFLOPS':>8s} {'%fp8peak':>8s}")
+        for name, x in synth.FP8_WORKLOADS.items():
+            xs = [torch.from_numpy(t).cuda() for t in x.generate()]
+            ox = torch.empty((x.B, x.H_q, x.N, x.D), dtype=torch.bfloat16, device=qg.device)
+            lx = torch.empty((x.B, x.H_q, x.N), dtype=torch.float32, device=qg.device)
+            ax = (xs[0].data_ptr(), xs[1].data_ptr(), xs[2].data_ptr(), ox.data_ptr(),
+                  lx.data_ptr(), x.B, x.H_q, x.H_kv, x.N, x.D, x.causal, x.scale, x.descale_q,
+                  x.descale_k, x.descale_v, stream.cuda_stream)
+            fn = lambda: sdpa.attn_fwd_fp8(*ax)
+            for _ in range(3):
+                fn()
+            ms, _, _ = _event_loop(fn, max(5, args.steps // 5), stream)
+            tf = x.flops / (ms * 1e-3) / 1e12
+            log(f"{name:40s} {ms:8.3f} {tf:8.1f} {100 * tf / PEAK_FP8_TFLOPS:8.1f}")
+    if not args.no_cpu_baseline:
+        log("[bench fp8] timing the FP8 oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_fp8(w)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_fp8(w, target_s: float = 10.0):
+    """The FP8 oracle as it stands (one thread) over a bounded sample of query
+    rows of the same workload; rate in the metric's unit (4*D flops per pair)."""
+    import oracle
+    oracle.build(force=False)
+    q8, k8, v8 = w.generate()
+    rng = np.random.default_rng(2)
+    total_rows = w.B * w.H_q * w.N
+
+    def run(n):
+        rows = np.sort(rng.choice(total_rows, n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_fp8_ref(q8, k8, v8, w.descale_q, w.descale_k, w.descale_v, w.causal,
+                            w.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        i = rows % w.N
+        keys = (i + 1) if w.causal else np.full(n, w.N)
+        return dt, float(keys.sum()) * 4 * w.D
+    dt, fl = run(4)
+    n = int(min(total_rows, max(4, 4 * target_s / max(dt, 1e-3))))
+    dt, fl = run(n)
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{n} random query rows of {w.name} (all allowed keys each, fp64, "
+                      f"one thread), {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen"), default="fwd")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "fp8"), default="fwd")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
                     choices=sorted(synth.WORKLOADS) + sorted(synth.DECODE_WORKLOADS)
-                    + sorted(synth.VARLEN_WORKLOADS),
+                    + sorted(synth.VARLEN_WORKLOADS) + sorted(synth.FP8_WORKLOADS),
                     help="default: the headline workload of the op")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -558,6 +660,12 @@ def main():
         if name not in synth.VARLEN_WORKLOADS:
             sys.exit(f"{name} is not a varlen workload")
         main_varlen(args, synth.VARLEN_WORKLOADS[name])
+        return
+    if args.op == "fp8":
+        name = args.workload or synth.FP8_HEADLINE
+        if name not in synth.FP8_WORKLOADS:
+            sys.exit(f"{name} is not an FP8 workload")
+        main_fp8(args, synth.FP8_WORKLOADS[name])
         return
     if args.op == "decode":
         name = args.workload or synth.DECODE_HEADLINE

@@ -1,6 +1,6 @@
 /*
- * attn.h: C ABI of the MI355X (gfx950) fused attention library (forward and
- * backward).
+ * attn.h: C ABI of the MI355X (gfx950) fused attention library (forward in bf16
+ * and FP8, backward, decode).
  *
  * The operation.  Scaled dot-product attention forward with the log-sum-exp
  * of every score row:
@@ -108,6 +108,34 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             const int* cu_seqlens, int n_seq, int max_seqlen, int total,
                             int H_q, int H_kv, int D, int causal, int window_left,
                             int window_right, float scale, void* stream);
+
+/*
+ * attn_fwd_fp8: attn_fwd on FP8 (e4m3) inputs with per-tensor descales.
+ *
+ * The operation.  q8, k8 and v8 hold OCP e4m3 codes (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals, NaN at 0x7F/0xFF, largest finite
+ * value 448); the tensors they stand for are Q = descale_q * q8, K = descale_k *
+ * k8, V = descale_v * v8.  O and LSE are attn_fwd's on those tensors.  Both
+ * matrix products run in FP8 with fp32 accumulation and the softmax runs in
+ * fp32 (page "注意力机制的本质与计算挑战", section 3: FP16/FP8 matrix products,
+ * fp32 softmax and accumulation; page "GPU注意力算子性能优化" (QiMeng-Attention),
+ * section 3.1.1; FP8 storage with wider accumulation: page "从硬件视角看注意力
+ * 机制优化", section 2.3).  The softmax weights are rounded to e4m3 for the
+ * second product and O is normalised by the sum of the rounded weights; the
+ * LSE uses the fp32 weights.
+ *
+ * q8       device pointer, uint8 [B, H_q, N, D] codes, contiguous row-major.
+ * k8, v8   device pointers, uint8 [B, H_kv, N, D] codes.
+ * o        device pointer, bf16 [B, H_q, N, D], written.
+ * lse      device pointer, fp32 [B, H_q, N], or NULL.
+ * descale_q, descale_k, descale_v   finite fp32 factors (ATTN_ERR_SCALE
+ *          otherwise, or when |scale * descale_q * descale_k| overflows fp32).
+ * Other arguments, ownership and errors as for attn_fwd (D must be 128; q8,
+ * k8, v8, o 16-byte aligned, lse 4-byte aligned).
+ */
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
+                         int B, int H_q, int H_kv, int N, int D, int causal, float scale,
+                         float descale_q, float descale_k, float descale_v, void* stream);
 
 /*
  * attn_bwd: enqueue the attention backward pass on `stream`: the gradients of

@@ -69,7 +69,7 @@ def _bind(path: str):
     if hasattr(lib, "attn_fp8_ref_f64"):
         f8 = lib.attn_fp8_ref_f64
         f8.restype = ctypes.c_int
-        f8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_double] * 3 + [ctypes.c_void_p] * 3 + [
+        f8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_double] * 3 + [ctypes.c_void_p] * 4 + [
             ctypes.c_int] * 6 + [ctypes.c_double] * 3 + [ctypes.c_void_p, ctypes.c_int64]
         dec = lib.e4m3_decode
         dec.restype = ctypes.c_double
@@ -311,9 +311,10 @@ def attn_fp8_ref(q8, k8, v8, descale_q: float, descale_k: float, descale_v: floa
     """Oracle forward on e4m3 inputs: q8 uint8 codes [B, H_q, N, D], k8, v8
     [B, H_kv, N, D]; the tensors are descale_x * value(code).  ``rows``: optional
     int64 flat row ids ((b*H_q + h)*N + i).  ``mags``: optional (w_rel, w_floor),
-    then the error-scale sums of the weight rounding are returned too.
+    then the error-scale sum and its quadrature (rms) counterpart for that
+    weight rounding are returned too.
 
-    Returns (o, lse) or (o, lse, mag) as float64, shaped [B, H_q, N, D] and
+    Returns (o, lse) or (o, lse, mag, rms) as float64, shaped [B, H_q, N, D] and
     [B, H_q, N], or [len(rows), D] and [len(rows)].
     """
     return call_fp8_lib(_load(), q8, k8, v8, descale_q, descale_k, descale_v, causal, scale,
@@ -341,12 +342,14 @@ def call_fp8_lib(lib, q8, k8, v8, descale_q, descale_k, descale_v, causal, scale
         lse = np.empty((rows.size,))
         rows_p, n_rows = rows.ctypes.data, rows.size
     mag = np.empty_like(o) if mags is not None else None
+    rms = np.empty_like(o) if mags is not None else None
     w_rel, w_floor = mags if mags is not None else (0.0, 0.0)
     rc = lib.attn_fp8_ref_f64(q8.ctypes.data, k8.ctypes.data, v8.ctypes.data, float(descale_q),
                               float(descale_k), float(descale_v), o.ctypes.data, lse.ctypes.data,
-                              None if mag is None else mag.ctypes.data, B, Hq, Hkv, N, D,
+                              None if mag is None else mag.ctypes.data,
+                              None if rms is None else rms.ctypes.data, B, Hq, Hkv, N, D,
                               int(bool(causal)), float(scale), float(w_rel), float(w_floor),
                               rows_p, n_rows)
     if rc != 0:
         raise ValueError(f"attn_fp8_ref_f64 failed with code {rc}")
-    return (o, lse, mag) if mags is not None else (o, lse)
+    return (o, lse, mag, rms) if mags is not None else (o, lse)

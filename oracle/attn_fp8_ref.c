@@ -27,7 +27,12 @@
  *
  *     mag_d = sum_j max(w_rel p_j, min(p_j, w_floor)) |V_jd - O_d| / l
  *
- * is returned per output element.
+ * is returned per output element.  With independent roundings of at most
+ * that size, the typical size of the change is the quadrature sum
+ *
+ *     rms_d = sqrt( sum_j (max(w_rel p_j, min(p_j, w_floor)) |V_jd - O_d|)^2 ) / l
+ *
+ * which is returned too (optional).
  *
  * Pins live in tests/oracle_fp8_pins.py.
  */
@@ -48,12 +53,12 @@ double e4m3_decode(uint8_t c)
  * q8: [B, H_q, N, D] codes; k8, v8: [B, H_kv, N, D] codes (host).
  * rows: optional flat row ids ((b * H_q + h) * N + i), n_rows of them; then o,
  * lse and mag hold just those rows ([n_rows, D], [n_rows]), else all rows
- * (o: [B, H_q, N, D], lse: [B, H_q, N]).  mag: optional, like o (w_rel and
- * w_floor are only read when mag is given).
+ * (o: [B, H_q, N, D], lse: [B, H_q, N]).  mag, rms: optional, like o (w_rel
+ * and w_floor are only read when one of them is given).
  * Returns 0, -1 on bad arguments, -2 on allocation failure.
  */
 int attn_fp8_ref_f64(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, double s_q,
-                     double s_k, double s_v, double *o, double *lse, double *mag, int B, int H_q,
+                     double s_k, double s_v, double *o, double *lse, double *mag, double *rms, int B, int H_q,
                      int H_kv, int N, int D, int causal, double scale, double w_rel,
                      double w_floor, const int64_t *rows, int64_t n_rows)
 {
@@ -99,15 +104,23 @@ int attn_fp8_ref_f64(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, do
             for (int d = 0; d < D; ++d) orow[d] += p[j] * (s_v * e4m3_decode(vp[(size_t)j * D + d]));
         for (int d = 0; d < D; ++d) orow[d] /= l;
         lse[t] = m + log(l);
-        if (mag) {
-            double *mrow = mag + (size_t)t * D;
-            for (int d = 0; d < D; ++d) mrow[d] = 0.0;
+        if (mag || rms) {
+            double *mrow = mag ? mag + (size_t)t * D : NULL;
+            double *rrow = rms ? rms + (size_t)t * D : NULL;
+            for (int d = 0; d < D; ++d) {
+                if (mrow) mrow[d] = 0.0;
+                if (rrow) rrow[d] = 0.0;
+            }
             for (int j = 0; j < nkeys; ++j) {
                 const double small = p[j] < w_floor ? p[j] : w_floor;
                 const double w = (w_rel * p[j] > small ? w_rel * p[j] : small) / l;
-                for (int d = 0; d < D; ++d)
-                    mrow[d] += w * fabs(s_v * e4m3_decode(vp[(size_t)j * D + d]) - orow[d]);
+                for (int d = 0; d < D; ++d) {
+                    const double dev = w * fabs(s_v * e4m3_decode(vp[(size_t)j * D + d]) - orow[d]);
+                    if (mrow) mrow[d] += dev;
+                    if (rrow) rrow[d] += dev * dev;
+                }
             }
+            for (int d = 0; rrow && d < D; ++d) rrow[d] = sqrt(rrow[d]);
         }
     }
     free(p);

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) fused scaled dot-product attention, forward and backward.
+"""MI355X (gfx950) fused scaled dot-product attention: forward (bf16 and FP8),
+backward, packed variable-length forward and split-KV decode.
 
 Thin Python binding over the C ABI declared in ``include/attn.h``: argument
 marshalling only.  Every step of the computation runs in the HIP kernels of
@@ -21,7 +22,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE",
                 10: "ATTN_ERR_WORKSPACE"}
-EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
+EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
             "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
             "attn_fwd_flops", "attn_bwd_flops", "attn_decode_flops")
 
@@ -63,6 +64,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_varlen.restype = ctypes.c_int
             lib.attn_fwd_varlen.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 9 + [
                 ctypes.c_float, ctypes.c_void_p]
+            lib.attn_fwd_fp8.restype = ctypes.c_int
+            lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+                ctypes.c_float] * 4 + [ctypes.c_void_p]
             lib.attn_decode.restype = ctypes.c_int
             lib.attn_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -93,6 +97,14 @@ def attn_fwd(q, k, v, o, lse, B, H_q, H_kv, N, D, causal, scale, stream) -> int:
     """Direct C-ABI call with raw device pointers (ints); returns the status code."""
     return load().attn_fwd(q, k, v, o, lse, int(B), int(H_q), int(H_kv), int(N), int(D),
                            int(bool(causal)), float(scale), stream)
+
+
+def attn_fwd_fp8(q8, k8, v8, o, lse, B, H_q, H_kv, N, D, causal, scale, descale_q, descale_k,
+                 descale_v, stream) -> int:
+    """Direct C-ABI call with raw device pointers (ints); returns the status code."""
+    return load().attn_fwd_fp8(q8, k8, v8, o, lse, int(B), int(H_q), int(H_kv), int(N), int(D),
+                               int(bool(causal)), float(scale), float(descale_q),
+                               float(descale_k), float(descale_v), stream)
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, n_seq, max_seqlen, total, H_q, H_kv, D, causal,
@@ -191,6 +203,51 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       lse.data_ptr() if lse is not None else None, B, Hq, Hkv, N, D,
                       causal, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_string(st))
+    return out, lse
+
+
+def fwd_fp8(q8, k8, v8, descale_q: float = 1.0, descale_k: float = 1.0, descale_v: float = 1.0,
+            causal: bool = False, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True):
+    """O, LSE = attention(descale_q*q8, descale_k*k8, descale_v*v8) on the current
+    torch stream, with q8, k8, v8 e4m3 codes (torch.uint8 or torch.float8_e4m3fn,
+    [B, H_q, N, D] and [B, H_kv, N, D], contiguous, on one GPU).  O is bf16
+    [B, H_q, N, D], lse fp32 [B, H_q, N].  ``scale`` defaults to 1/sqrt(D)."""
+    import torch
+
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or \
+                t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must be a 4-D torch.uint8 or torch.float8_e4m3fn tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k8.shape != v8.shape:
+        raise ValueError("k8 and v8 must have the same shape")
+    B, Hq, N, D = q8.shape
+    if k8.shape[0] != B or k8.shape[2] != N or k8.shape[3] != D:
+        raise ValueError("k8/v8 must be [B, H_kv, N, D] with q8's B, N and D")
+    if not (q8.device == k8.device == v8.device):
+        raise ValueError("q8, k8 and v8 must be on the same device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, N, D), dtype=torch.bfloat16, device=q8.device)
+    else:
+        _check_bf16("out", out, (B, Hq, N, D), q8.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    elif lse is not None and (lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+                              or not lse.is_contiguous() or lse.device != q8.device):
+        raise ValueError("lse must be a contiguous fp32 [B, H_q, N] tensor on q8's device")
+    with torch.cuda.device(q8.device):
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+        st = attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, B, Hq, k8.shape[1], N, D,
+                          causal, scale, descale_q, descale_k, descale_v, stream)
     if st != ATTN_OK:
         raise AttnError(st, status_string(st))
     return out, lse

@@ -8,7 +8,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", n) for n in
-        ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "status.hip")]
+        ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_decode.hip", "status.hip")]
 HDR = os.path.join(ROOT, "include", "attn.h")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"

@@ -1,0 +1,472 @@
+// Fused attention forward on FP8 (e4m3) Q, K, V with per-tensor descales, for
+// MI355X (gfx950, CDNA4).
+//
+// Q = dq * Q8, K = dk * K8, V = dv * V8 (Q8, K8, V8 hold OCP e4m3 codes);
+// O = softmax(scale * Q K^T [causal]) V in bf16 and the per-row natural-log LSE.
+//   * formula: page "GPU注意力算子性能优化" (QiMeng-Attention), section 1;
+//   * precision split: both matrix products in FP8, softmax and accumulation in
+//     fp32 (page "注意力机制的本质与计算挑战", section 3; the QiMeng page,
+//     section 3.1.1); the probabilities are stored in FP8 for the second
+//     product and the sums are kept wider (page "从硬件视角看注意力机制优化",
+//     section 2.3);
+//   * tiling, online softmax across key tiles and the shared K/V of a GQA group
+//     as in the bf16 forward (same pages, sections cited there).
+//
+// Matrix core: v_mfma_scale_f32_32x32x64_f8f6f4 with both block scales at the
+// neutral exponent (2^0), i.e. a plain e4m3 x e4m3 product with fp32
+// accumulation, 64 contraction values per lane pair.
+//
+// Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
+//   * each wave owns 32 query rows; its Q rows (128 bytes each) stay in VGPRs as
+//     the B operand of S^T = K Q^T;
+//   * key blocks of 64 rows of K and V (8 KiB each) are copied HBM -> LDS by the
+//     buffer unit's LDS DMA; K runs one block ahead of V so the score MFMAs of
+//     block g+1 and the PV MFMAs of block g-1 overlap the softmax of block g;
+//   * scores are computed transposed (each lane owns one query column); the
+//     fp32 scores become e4m3 weights packed in the order the accumulator
+//     holds them, and that packing is directly the B operand of O^T += V^T P^T;
+//   * the A operand V^T is read from the row-major V tile with the gfx950
+//     transposing byte read ds_read_b64_tr_b8: in a 16-lane group every lane
+//     names one 8-byte row piece and receives one byte column, so each lane
+//     can fetch exactly the 8 keys its P bytes stand for;
+//   * O's divisor is the sum of the e4m3 weights the MFMA actually applied,
+//     taken by one more MFMA against a tile of ones (exact fp32 sums of
+//     products), so the rounding of a dominant weight cancels in O; the LSE
+//     uses the fp32 weights;
+//   * softmax in base 2 against a lagging reference m: e = 2^(s*c - m*c + PS),
+//     c = |scale*dq*dk|*log2(e).  The weights are kept at most 2^8.75 < 448 (the
+//     largest e4m3 value): a lane whose 32 weights of a block sum above 448 checks
+//     its largest one, and only when some weight could pass 2^8.75 does the wave
+//     move every row to its running max (rare, wave-uniform branch).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "attn.h"
+#include "cdna4.h"
+
+namespace {
+
+using namespace cdna4;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int HD = 128;                      // head dimension handled by this kernel
+constexpr int ROW8 = HD;                     // bytes per e4m3 row
+constexpr int BR = 256;                      // query rows per workgroup
+constexpr int NWAVE = 8;
+constexpr int NTHREAD = NWAVE * 64;
+constexpr int KB = 64;                       // keys per pipeline step (one MFMA k extent)
+constexpr int BLK_BYTES = KB * ROW8;         // 8 KiB per K or V block
+constexpr int K_RING = 0;                    // LDS: a ring of 4 K blocks, then 4 V blocks
+constexpr int V_RING = 4 * BLK_BYTES;
+constexpr int LDS_BYTES = 8 * BLK_BYTES;     // 64 KiB
+constexpr float PS = 6.0f;                   // weights carry a factor 2^PS (room below 448)
+constexpr float SUM_CHECK = 448.0f;          // a lane's block sum above this checks its max
+constexpr float MAX_EXP = 8.75f;             // log2 of the largest weight allowed
+constexpr int ONE4 = 0x38383838;             // four e4m3 ones
+constexpr float LN2 = 0.693147180559945309f;
+
+struct Params {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    uint16_t* o;
+    float* lse;
+    int B, Hq, Hkv, N;
+    int group;        // Hq / Hkv
+    int n_qtiles;     // ceil(N / BR)
+    int total;        // B * Hq * n_qtiles workgroups
+    int q_mode;       // 0: Q as given, 1: Q negated, 2: Q replaced by zeros
+    float c;          // |scale*dq*dk| * log2(e), > 0
+    float lse_scale;  // |scale*dq*dk|
+    float dv;         // V descale, applied to O
+};
+
+// 16-byte chunk c of row r of a K tile sits at chunk position c ^ ((r >> 1) & 7):
+// the 16 rows one read phase touches (same logical chunk) then cover all 16
+// 16-byte bank groups of a 256-byte LDS line.
+__device__ __forceinline__ int k_swz(int r) { return (r >> 1) & 7; }
+// V tile: chunk c of row r at c ^ (2*((r>>1)&1) + 4*((r>>3)&1) + ((r>>2)&1)).
+// A transposing read names 8 rows {b, b+1, b+2, b+3, b+8, .., b+11} (b = 16t +
+// 4*half) in two adjacent chunks; this spreads them over distinct bank groups.
+__device__ __forceinline__ int v_swz(int r) {
+    return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
+}
+
+__device__ __forceinline__ float wave_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                              false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* lds, uint32_t off) {
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds + off));
+}
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    // format 0 (e4m3) for both operands, block scales 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(NTHREAD, 1) void attn_fwd_fp8_kernel(Params p) {
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;   // query column owned by this lane
+    const int hh = lane >> 5;    // which half of the wave
+
+    const int logical = xcd_remap(blockIdx.x, p.total);
+    const int bh = logical / p.n_qtiles;
+    int qt = logical % p.n_qtiles;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
+    const int b = bh / p.Hq;
+    const int h = bh % p.Hq;
+    const int kvh = h / p.group;
+    const int N = p.N;
+    const int q0 = qt * BR;
+    const int wq0 = q0 + wave * 32;
+    const int myq = wq0 + l32;
+
+    const size_t q_panel = ((size_t)b * p.Hq + h) * (size_t)N * HD;     // elements (bytes for Q8)
+    const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
+
+    // key blocks: n_blk_wg streamed through LDS, n_blk used by this wave (a
+    // causal wave stops at the block holding its last row's diagonal)
+    const int n_blk_all = (N + KB - 1) / KB;
+    int n_blk_wg = n_blk_all, n_blk = n_blk_all;
+    if (CAUSAL) {
+        n_blk_wg = min(n_blk_all, (min(q0 + BR, N) - 1) / KB + 1);
+        n_blk = min(n_blk_all, (wq0 + 31) / KB + 1);
+    }
+    if (wq0 >= N) n_blk = 0;
+    const uint8_t* kbase = p.k + kv_panel;
+    const uint8_t* vbase = p.v + kv_panel;
+
+    // ---- LDS DMA: each wave copies rows 8*wave .. 8*wave+7 of a block with one
+    // instruction (64 lanes x 16 bytes, lane order); lane L fetches the logical
+    // chunk that belongs at its physical position.
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    uint32_t k_dma, v_dma;
+    {
+        const int row = 8 * wave + (lane >> 3);
+        const int pc = lane & 7;
+        k_dma = (uint32_t)(row * ROW8 + ((pc ^ k_swz(row)) << 4));
+        v_dma = (uint32_t)(row * ROW8 + ((pc ^ v_swz(row)) << 4));
+    }
+    auto dma_block = [&](const uint8_t* panel, uint32_t voff, int ring, int g) {
+        if (g < n_blk_wg) {
+            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW8);
+            lds_dma16(r, lds_base + ring + (g & 3) * BLK_BYTES + 8 * wave * ROW8, voff);
+        }
+    };
+
+    // ---- per-lane LDS read offsets (relative to a block slot)
+    // K: rows 32*sb + l32, chunks 4*ks + 2*hh + u (u = 0, 1) -> bytes 64ks+32hh.. of d
+    uint32_t k_rd[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            k_rd[ks][u] = (uint32_t)(l32 * ROW8 + (((4 * ks + 2 * hh + u) ^ k_swz(l32)) << 4));
+    // V: transposing reads t = 0..3 of d block db.  In each 16-lane group lane
+    // lam names row piece jj = lam/2 (8 bytes at column d0 + 8*(lam&1)); the
+    // piece's row is the key that byte jj of P's read t stands for:
+    // key(t, jj) = 16t + 8*(jj/4) + 4*hh + jj%4.  t only adds 16 rows (2 KiB).
+    uint32_t v_rd[4];
+    {
+        const int lam = lane & 15;
+        const int jj = lam >> 1;
+        const int row = 8 * (jj >> 2) + 4 * hh + (jj & 3);
+        const int gh = (lane >> 4) & 1;   // which 16 columns of the 32-column d block
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            v_rd[db] = (uint32_t)(row * ROW8 + (((2 * db + gh) ^ v_swz(row)) << 4) + 8 * (lam & 1));
+    }
+
+    // ---- prologue
+    if (N % KB != 0) {
+        // never-written rows of a tail block must read as zeros, not stale LDS
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < LDS_BYTES / (16 * NTHREAD); ++i)
+            *(u32x4*)(lds + 16 * (tid + NTHREAD * i)) = z;
+        __syncthreads();
+    }
+    dma_block(kbase, k_dma, K_RING, 0);
+    dma_block(vbase, v_dma, V_RING, 0);
+    dma_block(kbase, k_dma, K_RING, 1);
+    dma_block(kbase, k_dma, K_RING, 2);
+
+    i32x8 qf[2];   // B operand of S^T: head dims 64ks + 32hh + 0..31 of this lane's row
+    {
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + q_panel, (uint32_t)N * ROW8);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 lo = buf_load16(qr, (uint32_t)myq * ROW8 + 64 * ks + 32 * hh);
+            const u32x4 hi = buf_load16(qr, (uint32_t)myq * ROW8 + 64 * ks + 32 * hh + 16);
+            qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    }
+    // a negative score scale is applied as |scale| on -Q (sign bits flipped,
+    // exact) and a zero one as zero scores
+    if (p.q_mode != 0) {
+        const int flip = p.q_mode == 1 ? (int)0x80808080u : 0;
+        const int keep = p.q_mode == 1 ? -1 : 0;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qf[ks][i] = (qf[ks][i] & keep) ^ flip;
+    }
+    const float c = p.c;
+    const i32x8 ones = {ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4};
+
+    // S^T of one 64-key block (two 32-key halves), from a K ring slot
+    auto scores = [&](f32x16 (&s)[2], uint32_t kslot) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            s[sb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t base = kslot + sb * 32 * ROW8;
+                const u32x4 lo = *(const u32x4*)(lds + base + k_rd[ks][0]);
+                const u32x4 hi = *(const u32x4*)(lds + base + k_rd[ks][1]);
+                const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                s[sb] = mfma8(a, qf[ks], s[sb]);
+            }
+        }
+    };
+    auto needs_mask = [&](int g) {
+        return (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
+    };
+    auto apply_mask = [&](f32x16 (&s)[2], int g) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = g * KB + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool bad = (key >= N) || (CAUSAL && key > myq);
+                s[sb][r] = bad ? -INFINITY : s[sb][r];
+            }
+    };
+
+    f32x16 o[4];          // O^T: 4 blocks of 32 head dims x 32 query columns
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    f32x16 ol = {};       // every row: sum of the e4m3 weights applied (O's divisor)
+    float m = -INFINITY;  // reference: raw score q8.k8 of this lane's row
+    float mb = 0.f;       // m * c - PS
+    float l = 0.f;        // this lane's partial sum of the fp32 weights (the LSE)
+
+    // O^T += V^T P^T for one block: A = V^T bytes in the key order of P's bytes
+    auto pv = [&](const i32x8& pw, uint32_t vslot) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const i32x2 r0 = lds_read_tr8(lds, vslot + v_rd[db]);
+            const i32x2 r1 = lds_read_tr8(lds, vslot + v_rd[db] + 16 * ROW8);
+            const i32x2 r2 = lds_read_tr8(lds, vslot + v_rd[db] + 32 * ROW8);
+            const i32x2 r3 = lds_read_tr8(lds, vslot + v_rd[db] + 48 * ROW8);
+            const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+            o[db] = mfma8(a, pw, o[db]);
+        }
+        ol = mfma8(ones, pw, ol);
+    };
+    // weights e = 2^(s*c - mb) as e4m3, byte 16*sb + r = key 32sb + 8(r/4) + 4hh + r%4
+    auto probs = [&](const f32x16 (&s)[2], i32x8& pw, float& ls) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 0], c, -mb));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 1], c, -mb));
+                const float e2 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 2], c, -mb));
+                const float e3 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 3], c, -mb));
+                a0 += e0 + e2;
+                a1 += e1 + e3;
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, pk, true);
+                pw[4 * sb + w] = pk;
+            }
+        ls = a0 + a1;
+    };
+    auto lane_max = [&](const f32x16 (&s)[2]) {
+        float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+        return mx;
+    };
+
+    // Key block g (valid while g < n_blk; g == n_blk only drains the last PV).
+    auto step = [&](auto first_t, auto ks_t, auto vs_t, int g, f32x16 (&s)[2], f32x16 (&sn)[2],
+                    const i32x8& pp, i32x8& pc) {
+        constexpr bool FIRST = decltype(first_t)::value;
+        constexpr uint32_t KS = K_RING + decltype(ks_t)::value * BLK_BYTES;
+        constexpr uint32_t VS = V_RING + decltype(vs_t)::value * BLK_BYTES;
+        const bool valid = g < n_blk;
+        if (!FIRST && valid && needs_mask(g)) apply_mask(s, g);
+        scores(sn, KS);
+        if constexpr (!FIRST) pv(pp, VS);
+        float ls;
+        probs(s, pc, ls);
+        asm volatile("" : "+v"(pc), "+v"(ls));
+        if (valid && __builtin_amdgcn_ballot_w64(!(ls <= SUM_CHECK)) != 0) {
+            // some lane's weights sum past 448: check the largest weights
+            const float mx = lane_max(s);
+            if (__builtin_amdgcn_ballot_w64(!(fmaf(mx, c, -mb) <= MAX_EXP)) != 0) {
+                const float m_new = fmaxf(m, wave_swap_max(mx));
+                const float alpha = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
+                m = m_new;
+                mb = (m == -INFINITY) ? -PS : m * c - PS;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ol[r] *= alpha;
+                probs(s, pc, ls);
+            }
+        }
+        if (valid) l += ls;
+    };
+
+    f32x16 sa[2], sb2[2];   // scores of even / odd key blocks
+    i32x8 pa = {}, pb = {};  // e4m3 weights of even / odd key blocks
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q loads and the first DMA done
+    __syncthreads();
+    if (n_blk > 0) {
+        scores(sa, K_RING);
+        if (needs_mask(0)) apply_mask(sa, 0);
+        m = wave_swap_max(lane_max(sa));
+        mb = (m == -INFINITY) ? -PS : m * c - PS;
+    }
+    __syncthreads();   // K slot 0 is refilled in the first tile
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using F = std::false_type;
+
+    // Tile j = steps 2j and 2j+1.  Step g reads K block g+1 (slot (g+1)%4) and
+    // V block g-1 (slot (g-1)%4), so during tile j the workgroup refills K
+    // blocks 2j+3, 2j+4 and V blocks 2j+1, 2j+2 into slots freed by tile j-1.
+    const int n_tiles = n_blk_wg / 2 + 1;
+    auto refill = [&](int j) {
+        dma_block(kbase, k_dma, K_RING, 2 * j + 3);
+        dma_block(kbase, k_dma, K_RING, 2 * j + 4);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 1);
+        dma_block(vbase, v_dma, V_RING, 2 * j + 2);
+    };
+    refill(0);
+    if (0 <= n_blk) step(std::true_type{}, I1{}, I3{}, 0, sa, sb2, pb, pa);
+    if (1 <= n_blk) step(F{}, I2{}, I0{}, 1, sb2, sa, pa, pb);
+    wait_dma();
+    __syncthreads();
+    for (int j = 1; j < n_tiles; j += 2) {
+        refill(j);
+        if (2 * j <= n_blk) step(F{}, I3{}, I1{}, 2 * j, sa, sb2, pb, pa);
+        if (2 * j + 1 <= n_blk) step(F{}, I0{}, I2{}, 2 * j + 1, sb2, sa, pa, pb);
+        wait_dma();
+        __syncthreads();
+        if (j + 1 >= n_tiles) break;
+        refill(j + 1);
+        if (2 * j + 2 <= n_blk) step(F{}, I1{}, I3{}, 2 * j + 2, sa, sb2, pb, pa);
+        if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb2, sa, pa, pb);
+        wait_dma();
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = dv * O^T / sum(e4m3 weights) in bf16;
+    // LSE = m*|scale dq dk| + ln(sum of fp32 weights) - PS*ln 2
+    const float l_tot = wave_swap_sum(l);
+    const float inv = p.dv / ol[0];
+    if (myq < N) {
+        uint16_t* orow = p.o + q_panel + (size_t)myq * HD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                bf16x4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[db][4 * r4 + i] * inv);
+                *(bf16x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = ov;
+            }
+        if (p.lse != nullptr && hh == 0) {
+            const size_t li = ((size_t)b * p.Hq + h) * (size_t)N + myq;
+            p.lse[li] = m * p.lse_scale + (logf(l_tot) - PS * LN2);
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o,
+                                    float* lse, int B, int H_q, int H_kv, int N, int D, int causal,
+                                    float scale, float descale_q, float descale_k, float descale_v,
+                                    void* stream) {
+    if (!q8 || !k8 || !v8 || !o) return ATTN_ERR_NULL;
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_GQA;
+    if (D != HD) return ATTN_ERR_HEAD_DIM;
+    if (!std::isfinite(scale) || !std::isfinite(descale_q) || !std::isfinite(descale_k) ||
+        !std::isfinite(descale_v))
+        return ATTN_ERR_SCALE;
+    const double prod = (double)scale * (double)descale_q * (double)descale_k;
+    const float mag = (float)std::fabs(prod);
+    if (!std::isfinite(mag)) return ATTN_ERR_SCALE;
+    if ((int64_t)N * HD * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    const int64_t n_qtiles = ((int64_t)N + BR - 1) / BR;
+    const int64_t total = (int64_t)B * H_q * n_qtiles;
+    if (total > INT32_MAX || (int64_t)B * H_q > INT32_MAX) return ATTN_ERR_SHAPE;
+    const uintptr_t mis = ((uintptr_t)q8 | (uintptr_t)k8 | (uintptr_t)v8 | (uintptr_t)o) & 15;
+    if (mis != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_ALIGN;
+    const size_t q_bytes = (size_t)B * H_q * N * HD;
+    const size_t kv_bytes = (size_t)B * H_kv * N * HD;
+    const size_t o_bytes = 2 * q_bytes;
+    const size_t lse_bytes = lse ? (size_t)B * H_q * N * 4 : 0;
+    const void* ins[3] = {q8, k8, v8};
+    const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+    for (int i = 0; i < 3; ++i)
+        if (ranges_overlap(o, o_bytes, ins[i], in_bytes[i]) ||
+            ranges_overlap(lse, lse_bytes, ins[i], in_bytes[i]))
+            return ATTN_ERR_ALIAS;
+    if (ranges_overlap(lse, lse_bytes, o, o_bytes)) return ATTN_ERR_ALIAS;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
+
+    Params p = {};
+    p.q = (const uint8_t*)q8;
+    p.k = (const uint8_t*)k8;
+    p.v = (const uint8_t*)v8;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.N = N;
+    p.group = H_q / H_kv;
+    p.n_qtiles = (int)n_qtiles;
+    p.total = (int)total;
+    p.q_mode = mag == 0.f ? 2 : (prod > 0 ? 0 : 1);
+    p.c = (float)((double)(mag > 0.f ? mag : 1.0f) * 1.4426950408889634);
+    p.lse_scale = mag;
+    p.dv = descale_v;
+    hipStream_t s = (hipStream_t)stream;
+    if (causal)
+        hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
+    else
+        hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

@@ -123,21 +123,26 @@ def pin_rows_subset(fref, dec):
                   _codes(1902, (B, Hkv, N, D)))
     rows = np.array([0, 5, 22, 23, 91, 183, 100], np.int64)
     for causal in (False, True):
-        o, lse, mag = fref(q8, k8, v8, 0.3, 0.2, 1.1, causal, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
-        so, sl, sm = fref(q8, k8, v8, 0.3, 0.2, 1.1, causal, SCALE, rows=rows,
-                          mags=(2.0 ** -4, 2.0 ** -16))
+        o, lse, mag, rms = fref(q8, k8, v8, 0.3, 0.2, 1.1, causal, SCALE,
+                                mags=(2.0 ** -4, 2.0 ** -16))
+        so, sl, sm, sr = fref(q8, k8, v8, 0.3, 0.2, 1.1, causal, SCALE, rows=rows,
+                              mags=(2.0 ** -4, 2.0 ** -16))
         assert np.array_equal(so, o.reshape(-1, D)[rows]) and np.array_equal(sl, lse.reshape(-1)[rows])
         assert np.array_equal(sm, mag.reshape(-1, D)[rows])
+        assert np.array_equal(sr, rms.reshape(-1, D)[rows])
 
 
 # ---------------------------------------------------------------- error scale
 def pin_error_scale_closed_forms(fref, dec):
-    """The error-scale sum in three cases with closed forms:
-    * every V row equal: O = that row and the sum is 0 (up to the rounding of O);
-    * two keys with equal scores: weights 1/2 each, sum = w_rel * |v1 - v2| / 2;
+    """The error-scale sum (and its quadrature counterpart) in cases with closed
+    forms:
+    * every V row equal: O = that row and both are 0 (up to the rounding of O);
+    * two keys with equal scores: weights 1/2 each, sum = w_rel * |v1 - v2| / 2,
+      quadrature sum = w_rel * |v1 - v2| * sqrt(2) / 4;
     * two keys whose scores differ by 30 (w_rel = 0, floor 1e-6): the sum is
-      (1e-6 |v1 - O| + e^-30 |v2 - O|) / (1 + e^-30).
-    Causal row 0 sees one key: O = V[0] and the sum is 0."""
+      (1e-6 |v1 - O| + e^-30 |v2 - O|) / (1 + e^-30), the quadrature sum
+      sqrt((1e-6 |v1 - O|)^2 + (e^-30 |v2 - O|)^2) / (1 + e^-30).
+    Causal row 0 sees one key: O = V[0] and both are 0."""
     D = 8
     one = 0x38
     # (a) constant V
@@ -145,18 +150,21 @@ def pin_error_scale_closed_forms(fref, dec):
     k8 = _codes(2001, (1, 1, 9, D))
     row = _codes(2002, (1, 1, 1, D))
     v8 = np.repeat(row, 9, axis=2)
-    o, lse, mag = fref(q8, k8, v8, 0.5, 0.25, 0.75, False, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
+    o, lse, mag, rms = fref(q8, k8, v8, 0.5, 0.25, 0.75, False, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
     vrow = 0.75 * dec(row[0, 0, 0])
     close(o[0, 0], np.broadcast_to(vrow, (9, D)), tol=1e-15, what="constant V")
     assert np.all(mag <= 1e-15 * np.abs(vrow)), "constant V: error scale not zero"
+    assert np.all(rms <= 1e-15 * np.abs(vrow)), "constant V: quadrature scale not zero"
     # (b) equal scores
     k8 = np.repeat(_codes(2003, (1, 1, 1, D)), 2, axis=2)
     v8 = _codes(2004, (1, 1, 2, D))
     q8 = _codes(2005, (1, 1, 2, D))
-    o, lse, mag = fref(q8, k8, v8, 1.0, 1.0, 1.0, False, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
+    o, lse, mag, rms = fref(q8, k8, v8, 1.0, 1.0, 1.0, False, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
     v = dec(v8[0, 0])
     close(o[0, 0, 0], (v[0] + v[1]) / 2, tol=1e-15, what="equal scores: mean of V")
     close(mag[0, 0, 0], 2.0 ** -4 * np.abs(v[0] - v[1]) / 2, tol=1e-15, what="equal scores: error scale")
+    close(rms[0, 0, 0], 2.0 ** -4 * np.abs(v[0] - v[1]) * math.sqrt(2) / 4, tol=1e-15,
+          what="equal scores: quadrature scale")
     # (c) scores 30 apart: q = e_0, k1 = (a, 0, ...), k2 = (b, 0, ...)
     q8 = np.zeros((1, 1, 2, D), np.uint8)
     q8[..., 0] = one
@@ -164,18 +172,21 @@ def pin_error_scale_closed_forms(fref, dec):
     k8[0, 0, 0, 0] = 0x70   # 128
     k8[0, 0, 1, 0] = 0x38   # 1
     scale = 30.0 / 127.0
-    o, lse, mag = fref(q8, k8, v8, 1.0, 1.0, 1.0, False, scale, mags=(0.0, 1e-6))
+    o, lse, mag, rms = fref(q8, k8, v8, 1.0, 1.0, 1.0, False, scale, mags=(0.0, 1e-6))
     t = math.exp(-30.0)
     eo = (v[0] + t * v[1]) / (1 + t)
     close(o[0, 0, 0], eo, tol=1e-15, what="scores 30 apart: O")
     close(lse[0, 0, 0], 128 * scale + math.log1p(t), tol=1e-15, what="scores 30 apart: LSE")
     emag = (1e-6 * np.abs(v[0] - eo) + t * np.abs(v[1] - eo)) / (1 + t)
     close(mag[0, 0, 0], emag, tol=1e-12, what="scores 30 apart: error scale")
+    erms = np.hypot(1e-6 * np.abs(v[0] - eo), t * np.abs(v[1] - eo)) / (1 + t)
+    close(rms[0, 0, 0], erms, tol=1e-12, what="scores 30 apart: quadrature scale")
     # causal row 0
     q8, k8, v8 = _codes(2006, (1, 2, 5, D)), _codes(2007, (1, 2, 5, D)), _codes(2008, (1, 2, 5, D))
-    o, lse, mag = fref(q8, k8, v8, 0.5, 0.5, 0.5, True, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
+    o, lse, mag, rms = fref(q8, k8, v8, 0.5, 0.5, 0.5, True, SCALE, mags=(2.0 ** -4, 2.0 ** -16))
     close(o[0, :, 0], 0.5 * dec(v8[0, :, 0]), tol=1e-15, what="causal row 0")
     assert np.all(mag[0, :, 0] == 0.0), "causal row 0: error scale not zero"
+    assert np.all(rms[0, :, 0] == 0.0), "causal row 0: quadrature scale not zero"
 
 
 ALL_PINS = [pin_decode_matches_torch, pin_decode_format_values, pin_equals_bf16_oracle,

@@ -122,3 +122,76 @@ def bwd_compare(g_gpu, g_ref, mag):
 def bwd_check(m, what=""):
     assert m["finite"], f"{what}: non-finite gradient {m}"
     assert m["n_over"] == 0, f"{what}: error over U|g| + {BWD_KAPPA}U*mag {m}"
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) forward bar, derived from the arithmetic of the path:
+#   * each softmax weight is rounded to e4m3 after scaling so that the row's
+#     reference weight is 2^6: relative rounding 2^-4 in the normal range and
+#     an absolute rounding of at most 2^-10 * 2^-6 = 2^-16 (in units of the
+#     row's largest weight) below it -> the oracle's error-scale sum with
+#     (w_rel, w_floor) = (2^-4 + score_err, 2^-16); O is normalised by the
+#     sum of the rounded weights, which is what that sum bounds to first order;
+#   * the FP8 matrix core accumulates the 64-term products with an error
+#     below 2^-14 of sum |q_d k_d| <= 2^-14 ||q|| ||k|| (measured on gfx950 at
+#     about 2^-18.6); times |scale dq dk| this is score_err (natural-log units),
+#     which moves each weight by a relative score_err and the LSE by at most
+#     score_err;
+#   * bf16 output rounding (2^-9 relative) and fp32 arithmetic: 2^-8 |O| and a
+#     factor 1.3 on the first-order sum (its second-order remainder, the
+#     e4m3 weight sum's own rounding and the bf16 rounding of the error);
+#   * LSE: fp32 sums of up to n_keys weights (n_keys * 2^-24 relative), the
+#     score error and 2^-16 (1 + |LSE|) for exp2/log/fp32 products.
+# That bound holds however the roundings line up; on diffuse rows it is far
+# above the error independent roundings actually leave, so a second, typical-
+# size check uses the oracle's quadrature sum rms (the standard deviation of
+# the first-order change when every weight's rounding is independent with at
+# most the stated size): the mean over all compared elements of
+# |err| / (rms + 2^-9 |O| + 2^-40) must stay below FP8_MEAN_Z = 1 (zero-mean
+# roundings give about 0.5 or less; a misplaced weight or key gives >> 1).
+FP8_W_REL = 2.0 ** -4
+FP8_W_FLOOR = 2.0 ** -16
+FP8_KAPPA = 1.3
+FP8_MFMA_REL = 2.0 ** -14
+FP8_MEAN_Z = 1.0
+
+
+def fp8_score_err(qvals, kvals, scale, dq, dk) -> float:
+    """Bound on the error of one scaled score: qvals/kvals are decoded e4m3
+    values (any shape with D last) of the rows involved."""
+    qn = float(np.sqrt((np.asarray(qvals, np.float64) ** 2).sum(-1)).max()) if np.size(qvals) else 0.0
+    kn = float(np.sqrt((np.asarray(kvals, np.float64) ** 2).sum(-1)).max()) if np.size(kvals) else 0.0
+    return abs(scale * dq * dk) * FP8_MFMA_REL * qn * kn
+
+
+def fp8_mags(score_err: float):
+    """(w_rel, w_floor) to pass to the FP8 oracle's error-scale sum."""
+    return (FP8_W_REL + score_err, FP8_W_FLOOR)
+
+
+def fp8_compare(o_gpu, lse_gpu, o_ref, lse_ref, mag, rms, score_err, n_keys):
+    o_gpu = np.asarray(o_gpu, np.float64)
+    err = np.abs(o_gpu - o_ref)
+    tol = 2.0 ** -8 * np.abs(o_ref) + FP8_KAPPA * mag
+    ratio = err / np.maximum(tol, 1e-300)
+    z = err / (rms + 2.0 ** -9 * np.abs(o_ref) + 2.0 ** -40)
+    m = {"max_abs": float(err.max()) if err.size else 0.0,
+         "mean_abs": float(err.mean()) if err.size else 0.0,
+         "max_err_over_tol": float(ratio.max()) if err.size else 0.0,
+         "mean_tol": float(tol.mean()) if tol.size else 0.0,
+         "n_over": int((err > tol).sum()),
+         "mean_z": float(z.mean()) if z.size else 0.0,
+         "finite": bool(np.all(np.isfinite(o_gpu)))}
+    if lse_gpu is not None:
+        le = np.abs(np.asarray(lse_gpu, np.float64) - lse_ref)
+        lt = 2.0 ** -16 * (1 + np.abs(lse_ref)) + score_err + n_keys * 2.0 ** -24
+        m["lse_max_abs"] = float(le.max()) if le.size else 0.0
+        m["lse_n_over"] = int((le > lt).sum())
+    return m
+
+
+def fp8_check(m, what=""):
+    assert m["finite"], f"{what}: non-finite output"
+    assert m["n_over"] == 0, f"{what}: {m['n_over']} outputs beyond the FP8 bound ({m})"
+    assert m["mean_z"] <= FP8_MEAN_Z, f"{what}: typical error above the rounding scale ({m})"
+    assert m.get("lse_n_over", 0) == 0, f"{what}: LSE beyond the FP8 bound ({m})"

@@ -310,3 +310,46 @@ def test_varlen_valid_arguments_without_gpu_report_device(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: this case would launch on fake pointers")
     assert call_varlen() == 9 and call_varlen(left=100, right=0, lse=None) == 9
+
+
+# attn_fwd_fp8 (fake, far-apart addresses; validation only)
+F8 = dict(OK_ARGS, dq=0.02, dk=0.03, dv=0.5)
+
+
+def call_fp8(**kw):
+    a = dict(F8)
+    a.update(kw)
+    return sdpa.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H_q"],
+                             a["H_kv"], a["N"], a["D"], a["causal"], a["scale"], a["dq"], a["dk"],
+                             a["dv"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(N=0), 2), (dict(N=1 << 23), 2), (dict(H_q=3, H_kv=2), 3),
+    (dict(D=64), 4),
+    (dict(scale=float("nan")), 5), (dict(dq=float("inf")), 5), (dict(dk=float("nan")), 5),
+    (dict(dv=float("-inf")), 5), (dict(scale=1e30, dq=1e30), 5),
+    (dict(q=Q + 8), 6), (dict(k=K + 1), 6), (dict(o=O + 2), 6), (dict(lse=L + 2), 6),
+    (dict(o=Q), 7), (dict(o=K + 4096), 7), (dict(lse=O + 64), 7), (dict(lse=V), 7),
+    (dict(lse=O + 65536 - 4), 7),
+])
+def test_fp8_argument_errors(lib, kw, code):
+    assert call_fp8(**kw) == code
+
+
+def test_fp8_valid_arguments_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_fp8() == 9 and call_fp8(lse=None, causal=1, scale=-0.1) == 9
+    assert call_fp8(lse=O + 65536) == 9   # o is 2 bytes per element: just past its end
+
+
+def test_python_fp8_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        sdpa.fwd_fp8(q, q, q)                       # CPU tensors
+    with pytest.raises(ValueError):
+        sdpa.fwd_fp8(q.to(torch.bfloat16), q, q)    # wrong dtype

@@ -24,7 +24,9 @@ MUTATIONS = {
     "gqa_modulo": ("const int kvh = h / group;", "const int kvh = h % H_kv;"),
     "lse_without_max": ("lse[t] = m + log(l);", "lse[t] = log(l);"),
     "causal_off_by_one": ("const int nkeys = causal ? i + 1 : N;", "const int nkeys = causal ? i : N;"),
-    "mag_signed": ("mrow[d] += w * fabs(", "mrow[d] += w * ("),
+    "mag_signed": ("const double dev = w * fabs(", "const double dev = w * ("),
+    "rms_not_squared": ("if (rrow) rrow[d] += dev * dev;", "if (rrow) rrow[d] += dev;"),
+    "rms_no_root": ("rrow[d] = sqrt(rrow[d]);", "rrow[d] = rrow[d];"),
     "mag_floor_ignored": ("const double small = p[j] < w_floor ? p[j] : w_floor;",
                           "const double small = 0.0;"),
     "mag_unnormalised": ("const double w = (w_rel * p[j] > small ? w_rel * p[j] : small) / l;",
