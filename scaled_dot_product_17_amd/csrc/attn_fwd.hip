@@ -12,14 +12,14 @@
 //     into the softmax, double-buffered tile staging and look-ahead prefetch:
 //     page "AVO算法优化Transformer注意力机制性能解析", sections 2.2, 3.1, 3.2, 5.1.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
 //   * each wave owns 32 query rows; its Q rows live in VGPRs as the B operand
 //     of v_mfma_f32_32x32x16_bf16 for the whole kernel;
-//   * key tiles of 64 rows of K and V are copied HBM -> LDS by the buffer
-//     unit's LDS DMA (no VGPR staging).  K runs one tile ahead of V: while a
-//     wave turns the scores of tile j into probabilities and multiplies them
-//     into V_j, the MFMAs of the scores of tile j+1 are already in flight, so
-//     the softmax VALU work overlaps matrix-core work inside every wave;
+//   * key blocks of 32 rows of K and V are copied HBM -> LDS by the buffer
+//     unit's LDS DMA (no VGPR staging).  K runs one block ahead of V: while a
+//     wave turns the scores of block j into probabilities, the MFMAs of the
+//     scores of block j+1 and of O += V_{j-1}^T P_{j-1}^T are already in
+//     flight, so the softmax VALU work overlaps matrix-core work in every wave;
 //   * scores are computed transposed, S^T = K Q^T, so each lane owns one query
 //     column: the row max and row sum are in-lane reductions plus one
 //     permlane32 swap, and the output rescale is a per-lane scalar;
@@ -173,9 +173,22 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     // ---- which (batch, head, query tile) this workgroup computes.  VARLEN: the
     // batch index is the sequence of a packed batch (B = 1, N = all tokens).
     const int logical = xcd_remap(blockIdx.x, p.total);
-    const int bh = logical / p.n_qtiles;
-    int qt = logical % p.n_qtiles;
-    if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
+    int bh, qt;
+    if (VARLEN && p.n_seq > 1) {
+        // several sequences: tile-major, largest tile index first.  Tiles far
+        // into a sequence exist only for long sequences and carry the most keys
+        // (causal, windowed or not), so the heaviest work starts first and short
+        // tiles fill the tail (longest-processing-time-first order).
+        const int per = p.B * p.Hq;
+        qt = p.n_qtiles - 1 - logical / per;
+        bh = logical % per;
+    } else {
+        // one (batch, head) after another, so a head's tiles share K/V in the
+        // L2 of one XCD
+        bh = logical / p.n_qtiles;
+        qt = logical % p.n_qtiles;
+        if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
+    }
     const int b = bh / p.Hq;
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
