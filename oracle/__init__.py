@@ -16,6 +16,8 @@ their log-sum-exp).
 ``attn_fp8_ref`` wraps ``attn_fp8_ref.c`` (the forward on e4m3 inputs with
 per-tensor scales, evaluated exactly on the values the codes stand for) and
 ``e4m3_decode`` its code-to-value rule.
+``attn_blocksparse_ref`` wraps ``attn_blocksparse_ref.c`` (the forward with a
+block-sparse mask given as per-query-block lists of key blocks).
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, n) for n in
          ("attn_ref.c", "attn_bwd_ref.c", "attn_decode_ref.c", "attn_varlen_ref.c",
-          "attn_fp8_ref.c")]
+          "attn_fp8_ref.c", "attn_blocksparse_ref.c")]
 _LIB = os.path.join(_HERE, "libattn_ref.so")
 _lock = threading.Lock()
 _lib = None
@@ -74,6 +76,11 @@ def _bind(path: str):
         dec = lib.e4m3_decode
         dec.restype = ctypes.c_double
         dec.argtypes = [ctypes.c_uint8]
+    if hasattr(lib, "attn_blocksparse_ref_f64"):
+        bs = lib.attn_blocksparse_ref_f64
+        bs.restype = ctypes.c_int
+        bs.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_void_p,
+                                                                     ctypes.c_int64]
     if hasattr(lib, "attn_decode_ref_f64"):
         dc = lib.attn_decode_ref_f64
         dc.restype = ctypes.c_int
@@ -353,3 +360,48 @@ def call_fp8_lib(lib, q8, k8, v8, descale_q, descale_k, descale_v, causal, scale
     if rc != 0:
         raise ValueError(f"attn_fp8_ref_f64 failed with code {rc}")
     return (o, lse, mag, rms) if mags is not None else (o, lse)
+
+
+def attn_blocksparse_ref(q, k, v, kb_ptr, kb_idx, block: int, causal: bool, scale: float,
+                         rows=None):
+    """Oracle forward with a block-sparse mask: q bf16 bits [B, H_q, N, D], k, v
+    [B, H_kv, N, D]; kb_ptr int32 [mask_heads * n_qb + 1] and kb_idx int32 list
+    the key blocks (of ``block`` tokens) each query block of each mask head sees
+    (mask_heads = 1: shared by all heads).  Rows that see no key get O = 0 and
+    LSE = -inf.  Returns (o, lse) as float64, all rows or the flat ``rows``."""
+    return call_blocksparse_lib(_load(), q, k, v, kb_ptr, kb_idx, block, causal, scale, rows)
+
+
+def call_blocksparse_lib(lib, q, k, v, kb_ptr, kb_idx, block, causal, scale, rows=None):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    ptr = np.ascontiguousarray(kb_ptr, dtype=np.int32)
+    idx = np.ascontiguousarray(kb_idx, dtype=np.int32)
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,H_q,N,D], k and v [B,H_kv,N,D]")
+    B, Hq, N, D = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
+        raise ValueError("shape mismatch between q and k/v")
+    n_qb = -(-N // int(block))
+    if ptr.ndim != 1 or (ptr.size - 1) % n_qb != 0:
+        raise ValueError("kb_ptr must hold mask_heads * ceil(N / block) + 1 offsets")
+    mask_heads = (ptr.size - 1) // n_qb
+    if rows is None:
+        o = np.empty((B, Hq, N, D))
+        lse = np.empty((B, Hq, N))
+        rows_p, n_rows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        o = np.empty((rows.size, D))
+        lse = np.empty((rows.size,))
+        rows_p, n_rows = rows.ctypes.data, rows.size
+    rc = lib.attn_blocksparse_ref_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                      lse.ctypes.data, ptr.ctypes.data,
+                                      idx.ctypes.data if idx.size else None, mask_heads,
+                                      int(block), B, Hq, k.shape[1], N, D, int(bool(causal)),
+                                      float(scale), rows_p, n_rows)
+    if rc != 0:
+        raise ValueError(f"attn_blocksparse_ref_f64 failed with code {rc}")
+    return o, lse
+

@@ -285,6 +285,103 @@ FP8_HEADLINE = "fp8_mha_noncausal_b2_h16_n16384"
 
 
 # --------------------------------------------------------------------------
+# Block-sparse masks: per (mask head, query block) lists of key blocks, in
+# block-compressed-row form (kb_ptr offsets, kb_idx indices).
+# --------------------------------------------------------------------------
+def lists_to_csr(lists):
+    """[[key blocks of list 0], [.. of list 1], ...] -> (kb_ptr, kb_idx) int32."""
+    ptr = np.zeros(len(lists) + 1, np.int32)
+    ptr[1:] = np.cumsum([len(x) for x in lists], dtype=np.int64)
+    idx = np.array([j for x in lists for j in x], np.int32)
+    return ptr, idx
+
+
+def sparse_pattern(seed: int, n_blocks: int, mask_heads: int, local: int, n_global: int,
+                   n_random: int, causal: bool):
+    """Lists of key blocks for each (mask head, query block): the `local` blocks
+    ending at the diagonal block, the first `n_global` blocks, and `n_random`
+    seeded random blocks (at or below the diagonal when causal), sorted, unique."""
+    rng = np.random.default_rng(seed)
+    lists = []
+    for _ in range(mask_heads):
+        for qb in range(n_blocks):
+            hi = qb if causal else n_blocks - 1
+            s = set(range(max(0, qb - local + 1), qb + 1)) if local > 0 else set()
+            s |= set(range(min(n_global, hi + 1)))
+            if n_random > 0 and hi >= 0:
+                s |= set(rng.integers(0, hi + 1, n_random).tolist())
+            lists.append(sorted(s))
+    return lists
+
+
+@dataclass(frozen=True)
+class SparseWorkload:
+    """Block-sparse forward: 128 x 128 blocks, local + global + random pattern."""
+    name: str
+    B: int
+    H_q: int
+    H_kv: int
+    N: int
+    local: int
+    n_global: int
+    n_random: int
+    causal: bool = False
+    per_head: bool = False
+    D: int = 128
+    block: int = 128
+    seed_base: int = 0
+    scale: float = field(default=float(np.float32(1.0 / math.sqrt(128.0))))
+
+    def lists(self):
+        nb = -(-self.N // self.block)
+        return sparse_pattern(self.seed_base + 7, nb, self.H_q if self.per_head else 1, self.local,
+                              self.n_global, self.n_random, self.causal)
+
+    def csr(self):
+        return lists_to_csr(self.lists())
+
+    def pairs(self) -> int:
+        """Allowed (query, key) pairs, exact."""
+        nb = -(-self.N // self.block)
+        lists = self.lists()
+        total = 0
+        for h in range(self.H_q):
+            for qb in range(nb):
+                ls = lists[(h if self.per_head else 0) * nb + qb]
+                q0, q1 = qb * self.block, min(self.N, (qb + 1) * self.block)
+                for kb in ls:
+                    k0, k1 = kb * self.block, min(self.N, (kb + 1) * self.block)
+                    if not self.causal or k1 <= q0:
+                        total += (q1 - q0) * (k1 - k0)
+                    else:   # pairs j <= i within the two ranges
+                        for i in range(q0, q1):
+                            total += max(0, min(k1, i + 1) - k0)
+        return self.B * total
+
+    @property
+    def flops(self) -> float:
+        """4*D per allowed (row, key) pair."""
+        return 4.0 * self.D * self.pairs()
+
+    def generate(self):
+        qs = (self.B, self.H_q, self.N, self.D)
+        ks = (self.B, self.H_kv, self.N, self.D)
+        return (normal_bf16(self.seed_base + 0, qs), normal_bf16(self.seed_base + 1, ks),
+                normal_bf16(self.seed_base + 2, ks))
+
+
+SPARSE_WORKLOADS = {w.name: w for w in [
+    # local window of 4 blocks + 1 global block + 2 random blocks per query block
+    SparseWorkload("bsparse_local4_global1_rand2_b2_h16_n16384", 2, 16, 16, 16384, 4, 1, 2,
+                   seed_base=9000),
+    SparseWorkload("bsparse_causal_local8_global2_b2_h16_n16384", 2, 16, 16, 16384, 8, 2, 2,
+                   causal=True, seed_base=9010),
+    SparseWorkload("bsparse_perhead_gqa_hq16_hkv2_n8192", 1, 16, 2, 8192, 3, 1, 3, per_head=True,
+                   seed_base=9020),
+]}
+
+
+# --------------------------------------------------------------------------
 # Decode workloads: M new query rows per (batch, query head) against a cache
 # of L keys and values (the last M positions of the sequence).  Same seeding
 # rule: Q, K, V use seed_base + 0, + 1, + 2.

@@ -84,3 +84,27 @@ def test_e4m3_normals():
     vals = torch.from_numpy(k8).view(torch.float8_e4m3fn).double().numpy() * w.descale_k
     assert abs(vals.mean()) < 0.02 and abs(vals.std() - 1.0) < 0.02
     assert not np.isnan(vals).any()
+
+
+def test_sparse_pattern_and_pair_count():
+    """Lists are sorted, unique, in range (at or below the diagonal when causal),
+    contain the local and global blocks, and pairs() counts the allowed pairs of
+    the expanded mask exactly."""
+    w = synth.SparseWorkload("t", 1, 2, 2, 300, local=2, n_global=1, n_random=2, causal=True,
+                             per_head=True, block=32, seed_base=5)
+    nb = -(-300 // 32)
+    lists = w.lists()
+    assert len(lists) == 2 * nb
+    for t, ls in enumerate(lists):
+        qb = t % nb
+        assert ls == sorted(set(ls)) and all(0 <= x <= qb for x in ls)
+        assert qb in ls and 0 in ls and (qb == 0 or qb - 1 in ls)
+    m = np.zeros((2, 300, 300), bool)
+    for h in range(2):
+        for qb in range(nb):
+            for kb in lists[h * nb + qb]:
+                m[h, qb * 32:(qb + 1) * 32, kb * 32:(kb + 1) * 32] = True
+    m &= np.tril(np.ones((300, 300), bool))[None]
+    assert w.pairs() == int(m.sum())
+    ptr, idx = w.csr()
+    assert ptr[0] == 0 and ptr[-1] == idx.size and np.all(np.diff(ptr) >= 0)
