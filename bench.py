@@ -22,10 +22,14 @@ FP8 (--op fp8): one step = one attn_fwd_fp8 launch over the FP8 counterpart of
 the headline workload (e4m3 Q, K, V with per-tensor descales, bf16 O).  TFLOPS
 = 4*B*H*N^2*D / time (halved for causal), against the dense FP8 MFMA peak.
 
+Block-sparse (--op sparse): one step = one attn_fwd_blocksparse launch with a
+local + global + random pattern of 128 x 128 blocks.  TFLOPS = 4*D*(allowed
+(row, key) pairs) / time.
+
 Prints ONE JSON line on stdout, with the roofline of the dominant kernel and
 the oracle's CPU rate on a bounded sample as a reported baseline.
 
-  python bench.py [--op fwd|bwd|decode|varlen|fp8] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--op fwd|bwd|decode|varlen|fp8|sparse] [--steps K] [--warmup W] [--workload NAME]
                   [--sweep] [--no-cpu-baseline]
 
 ``--sweep`` also times every workload of the catalogue and prints a table on
@@ -61,6 +65,8 @@ PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 # dense e4m3 MFMA peak: v_mfma_scale 32x32x64 f8 does 131072 flop per 64 clocks
 # per SIMD, twice the bf16 rate: 5033.2 TFLOP/s.
 PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS
+METRIC_SPARSE = ("block-sparse attention fwd TFLOPS (bf16, d=128, 128 x 128 blocks; 4*D per allowed "
+                 "(row, key) pair) and % of MI355X dense BF16 MFMA peak")
 METRIC_FP8 = ("attention fwd TFLOPS (FP8 e4m3 Q/K/V with per-tensor descales, bf16 O, d=128) "
               "and % of MI355X dense FP8 MFMA peak")
 CSRC = os.path.join(ROOT, "scaled_dot_product_17_amd", "csrc")
@@ -523,6 +529,114 @@ def cpu_baseline_varlen(w, target_s: float = 10.0):
                       f"{g} query head(s) of K/V head 0, {dt:.1f} s"}
 
 
+def main_sparse(args, w):
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    ptr, idx = w.csr()
+    log(f"[bench sparse] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} causal={w.causal} "
+        f"lists={len(ptr) - 1} entries={len(idx)} density={w.pairs() / (w.B * w.H_q * w.N * w.N):.4f}")
+    q, k, v = w.generate()
+    qg, kg, vg = upload(q), upload(k), upload(v)
+    del q, k, v
+    pg = torch.from_numpy(ptr).cuda()
+    ig = torch.from_numpy(idx).cuda()
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=qg.device)
+    stream = torch.cuda.current_stream()
+    mh = (len(ptr) - 1) // (-(-w.N // w.block))
+    a = (qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), o.data_ptr(), lse.data_ptr(), pg.data_ptr(),
+         ig.data_ptr(), len(idx), mh, w.B, w.H_q, w.H_kv, w.N, w.D, w.causal, w.scale,
+         stream.cuda_stream)
+
+    def step():
+        st = sdpa.attn_fwd_blocksparse(*a)
+        assert st == 0, st
+
+    for _ in range(args.warmup):
+        step()
+    ms_step, per, mean = _event_loop(step, args.steps, stream)
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE in the benchmark output"
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    achieved = w.flops / (mean * 1e-3) / 1e12
+    log(f"[bench sparse] {ms_step:.3f} ms/step: {tflops:.1f} TFLOPS = "
+        f"{100 * tflops / PEAK_TFLOPS:.1f}% of peak")
+    res = {
+        "metric": METRIC_SPARSE, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 and a seeded block pattern)",
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "config": {"workload": w.name, "op": "sparse", "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "N": w.N, "D": w.D, "causal": w.causal, "block": w.block,
+                   "pattern": {"local": w.local, "global": w.n_global, "random": w.n_random,
+                               "per_head": w.per_head},
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel<sparse>", "launch_ms_mean": round(mean, 4),
+                     "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
+                                           round(float(np.percentile(per, 90)), 4)]},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        log(f"{'workload':46s} {'ms':>8s} {'TFLOPS':>8s} {'%peak':>6s}")
+        for name, x in synth.SPARSE_WORKLOADS.items():
+            qq, kk, vv = x.generate()
+            xp, xi = x.csr()
+            qx, kx, vx = upload(qq), upload(kk), upload(vv)
+            px, ix = torch.from_numpy(xp).cuda(), torch.from_numpy(xi).cuda()
+            ox = torch.empty_like(qx)
+            lx = torch.empty((x.B, x.H_q, x.N), dtype=torch.float32, device=qx.device)
+            mhx = (len(xp) - 1) // (-(-x.N // x.block))
+            ax = (qx.data_ptr(), kx.data_ptr(), vx.data_ptr(), ox.data_ptr(), lx.data_ptr(),
+                  px.data_ptr(), ix.data_ptr(), len(xi), mhx, x.B, x.H_q, x.H_kv, x.N, x.D,
+                  x.causal, x.scale, stream.cuda_stream)
+            fn = lambda: sdpa.attn_fwd_blocksparse(*ax)
+            for _ in range(3):
+                fn()
+            ms, _, _ = _event_loop(fn, max(5, args.steps // 5), stream)
+            tf = x.flops / (ms * 1e-3) / 1e12
+            log(f"{name:46s} {ms:8.3f} {tf:8.1f} {100 * tf / PEAK_TFLOPS:6.1f}")
+    if not args.no_cpu_baseline:
+        log("[bench sparse] timing the block-sparse oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_sparse(w)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_sparse(w, target_s: float = 10.0):
+    """The block-sparse oracle as it stands (one thread) over a bounded sample of
+    query rows; rate in the metric's unit (4*D flops per allowed pair)."""
+    import oracle
+    oracle.build(force=False)
+    q, k, v = w.generate()
+    ptr, idx = w.csr()
+    lists = w.lists()
+    nb = -(-w.N // w.block)
+    rng = np.random.default_rng(3)
+    total_rows = w.B * w.H_q * w.N
+
+    def pairs_of(rows):
+        n = 0
+        for r in rows:
+            i, h = int(r % w.N), int((r // w.N) % w.H_q)
+            for kb in lists[(h if w.per_head else 0) * nb + i // w.block]:
+                k0, k1 = kb * w.block, min(w.N, (kb + 1) * w.block)
+                n += max(0, min(k1, i + 1) - k0) if w.causal else k1 - k0
+        return n
+
+    def run(n):
+        rows = np.sort(rng.choice(total_rows, n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_blocksparse_ref(q, k, v, ptr, idx, w.block, w.causal, w.scale, rows=rows)
+        return time.perf_counter() - t0, pairs_of(rows) * 4.0 * w.D
+    dt, fl = run(16)
+    n = int(min(total_rows, max(16, 16 * target_s / max(dt, 1e-3))))
+    dt, fl = run(n)
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{n} random query rows of {w.name} (their listed keys, fp64, one thread), "
+                      f"{dt:.1f} s"}
+
+
 def main_fp8(args, w):
     import torch
     import scaled_dot_product_17_amd as sdpa
@@ -618,12 +732,14 @@ def cpu_baseline_fp8(w, target_s: float = 10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "fp8"), default="fwd")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen", "fp8", "sparse"),
+                    default="fwd")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
                     choices=sorted(synth.WORKLOADS) + sorted(synth.DECODE_WORKLOADS)
-                    + sorted(synth.VARLEN_WORKLOADS) + sorted(synth.FP8_WORKLOADS),
+                    + sorted(synth.VARLEN_WORKLOADS) + sorted(synth.FP8_WORKLOADS)
+                    + sorted(synth.SPARSE_WORKLOADS),
                     help="default: the headline workload of the op")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -660,6 +776,12 @@ def main():
         if name not in synth.VARLEN_WORKLOADS:
             sys.exit(f"{name} is not a varlen workload")
         main_varlen(args, synth.VARLEN_WORKLOADS[name])
+        return
+    if args.op == "sparse":
+        name = args.workload or next(iter(synth.SPARSE_WORKLOADS))
+        if name not in synth.SPARSE_WORKLOADS:
+            sys.exit(f"{name} is not a block-sparse workload")
+        main_sparse(args, synth.SPARSE_WORKLOADS[name])
         return
     if args.op == "fp8":
         name = args.workload or synth.FP8_HEADLINE

@@ -110,6 +110,37 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int window_right, float scale, void* stream);
 
 /*
+ * attn_fwd_blocksparse: attn_fwd with a block-sparse mask.
+ *
+ * The operation.  Query rows and keys are cut into blocks of 128 (the last may
+ * be short).  Query block qb of mask head mh attends to the key blocks listed in
+ * kb_idx[kb_ptr[mh * n_blk + qb] .. kb_ptr[mh * n_blk + qb + 1] - 1], with
+ * n_blk = ceil(N / 128), in block-compressed-row form (block-sparse patterns and
+ * a compressed storage format for them: future work on page "AVO算法优化
+ * Transformer注意力机制性能解析", section 6).  Row i of query head h sees key j
+ * when j's block is listed for i's block of mask head (mask_heads == 1 ? 0 : h)
+ * and, with `causal`, j <= i.  O and LSE are attn_fwd's over those keys; a row
+ * that sees no key gets O = 0 and LSE = -inf.  Indices outside [0, n_blk) are
+ * ignored and an index listed twice counts once.  The mask is shared by all
+ * batch entries.
+ *
+ * kb_ptr   device pointer, int32 [mask_heads * n_blk + 1], non-decreasing
+ *          offsets into kb_idx; they are clamped to [0, nnz] on the device, so
+ *          malformed offsets cannot make the kernel read out of range.
+ * kb_idx   device pointer, int32 [nnz] key-block indices (may be NULL if nnz = 0).
+ * nnz      number of entries of kb_idx.
+ * mask_heads  1 (one mask for every head) or H_q (one per query head).
+ * Other arguments, precision, ownership and errors as for attn_fwd.  N may be
+ * at most 2048 * 128 = 262144 (ATTN_ERR_SHAPE otherwise, as for mask_heads not
+ * 1 or H_q and nnz < 0); kb_ptr, kb_idx must be 4-byte aligned and must not
+ * overlap o or lse.
+ */
+attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int* kb_ptr, const int* kb_idx, int nnz, int mask_heads,
+                                 int B, int H_q, int H_kv, int N, int D, int causal, float scale,
+                                 void* stream);
+
+/*
  * attn_fwd_fp8: attn_fwd on FP8 (e4m3) inputs with per-tensor descales.
  *
  * The operation.  q8, k8 and v8 hold OCP e4m3 codes (1 sign, 4 exponent bits

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE",
                 10: "ATTN_ERR_WORKSPACE"}
-EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
+EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_fwd_blocksparse", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
             "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
             "attn_fwd_flops", "attn_bwd_flops", "attn_decode_flops")
 
@@ -64,6 +64,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_varlen.restype = ctypes.c_int
             lib.attn_fwd_varlen.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 9 + [
                 ctypes.c_float, ctypes.c_void_p]
+            lib.attn_fwd_blocksparse.restype = ctypes.c_int
+            lib.attn_fwd_blocksparse.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 8 + [
+                ctypes.c_float, ctypes.c_void_p]
             lib.attn_fwd_fp8.restype = ctypes.c_int
             lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
                 ctypes.c_float] * 4 + [ctypes.c_void_p]
@@ -97,6 +100,60 @@ def attn_fwd(q, k, v, o, lse, B, H_q, H_kv, N, D, causal, scale, stream) -> int:
     """Direct C-ABI call with raw device pointers (ints); returns the status code."""
     return load().attn_fwd(q, k, v, o, lse, int(B), int(H_q), int(H_kv), int(N), int(D),
                            int(bool(causal)), float(scale), stream)
+
+
+def attn_fwd_blocksparse(q, k, v, o, lse, kb_ptr, kb_idx, nnz, mask_heads, B, H_q, H_kv, N, D,
+                         causal, scale, stream) -> int:
+    """Direct C-ABI call with raw device pointers (ints); returns the status code."""
+    return load().attn_fwd_blocksparse(q, k, v, o, lse, kb_ptr, kb_idx, int(nnz), int(mask_heads),
+                                       int(B), int(H_q), int(H_kv), int(N), int(D),
+                                       int(bool(causal)), float(scale), stream)
+
+
+SPARSE_BLOCK = 128
+
+
+def fwd_blocksparse(q, k, v, kb_ptr, kb_idx, causal: bool = False, scale: float | None = None,
+                    out=None, lse=None):
+    """O, LSE = attention(q, k, v) restricted to the listed 128 x 128 blocks.
+
+    q: bf16 [B, H_q, N, D]; k, v: bf16 [B, H_kv, N, D].  kb_ptr, kb_idx: int32
+    device tensors in block-compressed-row form, one list per (mask head,
+    query block of 128 rows); the number of mask heads (1 or H_q) follows from
+    kb_ptr's length.  Rows that see no key get O = 0 and LSE = -inf.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    B, Hq, N, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
+        raise ValueError("k/v must be [B, H_kv, N, D] with q's B, N and D")
+    for name, t in (("kb_ptr", kb_ptr), ("kb_idx", kb_idx)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 \
+                or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor on q's device")
+    n_blk = -(-N // SPARSE_BLOCK)
+    if (kb_ptr.numel() - 1) % n_blk != 0 or kb_ptr.numel() < 2:
+        raise ValueError("kb_ptr must hold mask_heads * ceil(N / 128) + 1 offsets")
+    mask_heads = (kb_ptr.numel() - 1) // n_blk
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), kb_ptr.data_ptr(),
+                                  kb_idx.data_ptr() if kb_idx.numel() else None, kb_idx.numel(),
+                                  mask_heads, B, Hq, k.shape[1], N, D, causal, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_string(st))
+    return out, lse
 
 
 def attn_fwd_fp8(q8, k8, v8, o, lse, B, H_q, H_kv, N, D, causal, scale, descale_q, descale_k,

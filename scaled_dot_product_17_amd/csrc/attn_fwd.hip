@@ -67,6 +67,12 @@ constexpr int LDS_BYTES = 8 * BLK_BYTES;   // 64 KiB
 constexpr float MOVE_SUM = 18446744073709551616.0f;  // 2^64: a lane's block sum of p above
                                                       // this moves the softmax reference
 constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
+// block-sparse masks: blocks of SP_BLOCK query rows x SP_BLOCK keys; a workgroup's
+// 256 rows are two query blocks.  The union of their key-block lists is kept in
+// LDS past the rings, one 16-bit entry per key block (index | 2 membership bits).
+constexpr int SP_BLOCK = 128;
+constexpr int SP_MAX = 2048;               // key blocks a mask may have (N <= 262144)
+constexpr int SP_BYTES = 2 * SP_MAX + 64;  // union list + per-wave counts
 
 struct Params {
     const uint16_t* q;
@@ -85,6 +91,13 @@ struct Params {
     const int* cu;    // n_seq + 1 token offsets
     int n_seq;
     int left, right;  // window: row i sees keys i-left .. i+right (< 0: unbounded)
+    // block-sparse mask (SPARSE kernels only): lists of SP_BLOCK-key blocks per
+    // (mask head, SP_BLOCK-row query block), block-compressed-row form
+    const int* kb_ptr;  // mask_heads * n_sblk + 1 offsets into kb_idx
+    const int* kb_idx;  // nnz key-block indices
+    int nnz;
+    int mask_heads;     // 1 (shared by all heads) or Hq
+    int n_sblk;         // ceil(N / SP_BLOCK)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -160,9 +173,9 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
 }
 
-template <bool CAUSAL, bool VARLEN>
+template <bool CAUSAL, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SPARSE ? SP_BYTES : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -216,7 +229,66 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     int kb0 = 0, n_blk_wg, n_blk;
     int lo_i = 0, hi_i = N - 1;           // this lane's allowed keys (VARLEN)
     int lo_max = 0, hi_min = N - 1;       // keys every valid row of the wave allows (VARLEN)
-    if constexpr (VARLEN) {
+    // SPARSE: the union of the two query blocks' lists, built in LDS (the rings
+    // serve as scratch before the first copy); stream block g is 32-key part
+    // g % 4 of union entry g / 4
+    const uint16_t* sp = (const uint16_t*)(lds + LDS_BYTES);
+    if constexpr (SPARSE) {
+        uint8_t* f0 = (uint8_t*)lds;             // key blocks listed by query block 2qt
+        uint8_t* f1 = (uint8_t*)lds + SP_MAX;    // ... and by query block 2qt+1
+        int* wsum = (int*)(lds + LDS_BYTES + 2 * SP_MAX);
+        for (int i = tid; i < 2 * SP_MAX / 4; i += NTHREAD) ((uint32_t*)lds)[i] = 0u;
+        __syncthreads();
+        const int nsb = p.n_sblk;
+        const size_t mh = p.mask_heads == 1 ? 0 : (size_t)h;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int qb = 2 * qt + half;
+            if (qb < nsb) {
+                // offsets clamped to [0, nnz]: a malformed list cannot read out of range
+                const int a = min(max(p.kb_ptr[mh * nsb + qb], 0), p.nnz);
+                const int e = min(max(p.kb_ptr[mh * nsb + qb + 1], a), p.nnz);
+                uint8_t* f = half ? f1 : f0;
+                for (int x = a + tid; x < e; x += NTHREAD) {
+                    const int kb = p.kb_idx[x];
+                    // causal: key blocks after the query block hold no visible key
+                    if (kb >= 0 && kb < nsb && (!CAUSAL || kb <= qb)) f[kb] = 1;
+                }
+            }
+        }
+        __syncthreads();
+        // compaction in key-block order: thread t owns key blocks 4t .. 4t+3
+        int bits[4], cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kb = 4 * tid + j;
+            bits[j] = kb < nsb ? (f0[kb] | (f1[kb] << 1)) : 0;
+            cnt += bits[j] != 0;
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int before = 0, n_u = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) {
+            const int c = wsum[w];
+            before += w < wave ? c : 0;
+            n_u += c;
+        }
+        int pos = before + incl - cnt;
+        uint16_t* spw = (uint16_t*)(lds + LDS_BYTES);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (bits[j] != 0) spw[pos++] = (uint16_t)((4 * tid + j) | (bits[j] << 14));
+        __syncthreads();
+        n_blk_wg = 4 * n_u;
+        n_blk = wq0 < N ? n_blk_wg : 0;
+    } else if constexpr (VARLEN) {
         const int r_end = min(q0 + BR, s1);
         kb0 = p.left >= 0 ? max(s0, q0 - p.left) : s0;
         int khi = s1 - 1;
@@ -263,9 +335,20 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         k_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ (row & 15)) << 4));
         v_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ ((row & 3) << 2)) << 4));
     }
+    // first key of stream block g, and whether this wave's query block lists it (SPARSE)
+    auto sp_key = [&](int g) {
+        const int ent = __builtin_amdgcn_readfirstlane((int)sp[g >> 2]);
+        return (ent & 0x3FFF) * SP_BLOCK + (g & 3) * KB;
+    };
+    auto sp_member = [&](int g) {
+        const int ent = __builtin_amdgcn_readfirstlane((int)sp[g >> 2]);
+        return ((ent >> (14 + (wave >> 2))) & 1) != 0;
+    };
     auto dma_block = [&](const uint16_t* panel, const uint32_t* voff, int ring, int g) {
         if (g < n_blk_wg) {
-            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - kb0 - g * KB) * ROW_BYTES);
+            const int key = SPARSE ? sp_key(g) : kb0 + g * KB;
+            if (SPARSE && key >= N) return;   // a 32-key part past the end of a short last block
+            const u32x4 r = sgpr_rsrc(panel + (size_t)(key - kb0) * HD, (uint32_t)(N - key) * ROW_BYTES);
             const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 4 * DMA_PER_WAVE * wave * ROW_BYTES;
 #pragma unroll
             for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
@@ -290,8 +373,9 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     }
 
     // ---- prologue: K blocks 0-2 and V block 0 in flight, then Q into VGPRs
-    if (VARLEN || N % KB != 0) {
-        // rows past N of the tail block must read as zeros, not stale LDS
+    if (VARLEN || SPARSE || N % KB != 0) {
+        // rows past N of the tail block must read as zeros, not stale LDS (and the
+        // union build's scratch must be gone before the first block arrives)
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < LDS_BYTES / (16 * NTHREAD); ++i)
@@ -334,6 +418,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     };
     // key >= N (ragged tail) or key > query (causal) -> -inf
     auto needs_mask = [&](int g) {
+        if constexpr (SPARSE) {
+            const int kb = sp_key(g);
+            return !sp_member(g) || (CAUSAL && kb + KB - 1 > wq0) || (kb + KB > N);
+        }
         if constexpr (VARLEN) {
             const int kb = kb0 + g * KB;
             return kb < lo_max || kb + KB - 1 > hi_min;
@@ -341,12 +429,14 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         return (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
     };
     auto apply_mask = [&](f32x16& s, int g) {
+        const int kbase_g = SPARSE ? sp_key(g) : kb0 + g * KB;
+        const bool listed = SPARSE ? sp_member(g) : true;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key = kb0 + g * KB + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int key = kbase_g + 8 * (r >> 2) + 4 * hh + (r & 3);
             bool bad;
             if constexpr (VARLEN) bad = key < lo_i || key > hi_i;
-            else bad = (key >= N) || (CAUSAL && key > myq);
+            else bad = !listed || (key >= N) || (CAUSAL && key > myq);
             s[r] = bad ? -INFINITY : s[r];
         }
     };
@@ -431,7 +521,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(ls), "+v"(lbs));
         // VARLEN: a row whose window has not started yet keeps m = -inf; it moves
         // its reference (through the rare path) at its first allowed key
-        const bool no_ref = VARLEN && m == -INFINITY && myq < s1;
+        const bool no_ref = (VARLEN || SPARSE) && m == -INFINITY && myq < s1;
         const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM) || no_ref);
         if (valid && over != 0) {
             const float m_new = fmaxf(m, row_max(s));
@@ -511,7 +601,11 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     // LSE = m*scale + ln(sum p).  Dividing by the sum of the weights the MFMA
     // actually applied makes the rounding of a dominant weight cancel.
     const float l_tot = wave_swap_sum(l);
-    const float inv = 1.0f / wave_swap_sum(lb);
+    const float lb_tot = wave_swap_sum(lb);
+    // SPARSE: a row that sees no key (its lists hold none of its keys) gets
+    // O = 0 and LSE = -inf
+    const bool empty = SPARSE && !(lb_tot > 0.f);
+    const float inv = empty ? 0.f : 1.0f / lb_tot;
     if (myq < s1) {
         uint16_t* orow = p.o + qo_panel + (size_t)myq * HD;
 #pragma unroll
@@ -525,7 +619,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
             }
         if (p.lse != nullptr && hh == 0) {
             const size_t li = ((size_t)pbat * p.Hq + h) * (size_t)N + myq;
-            p.lse[li] = m * p.lse_scale + logf(l_tot);
+            p.lse[li] = empty ? -INFINITY : m * p.lse_scale + logf(l_tot);
         }
     }
 }
@@ -560,13 +654,13 @@ void set_scale(Params& p, float scale) {
     p.lse_scale = mag;
 }
 
-template <bool VARLEN>
+template <bool VARLEN, bool SPARSE>
 attn_status launch_fwd(const Params& p, bool causal, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     if (causal)
-        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -614,7 +708,7 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     p.n_qtiles = (int)n_qtiles;
     p.total = (int)total;
     set_scale(p, scale);
-    return launch_fwd<false>(p, causal != 0, stream);
+    return launch_fwd<false, false>(p, causal != 0, stream);
 }
 
 extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
@@ -666,7 +760,65 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;
     set_scale(p, scale);
-    return launch_fwd<true>(p, causal != 0, stream);
+    return launch_fwd<true, false>(p, causal != 0, stream);
+}
+
+extern "C" attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                            float* lse, const int* kb_ptr, const int* kb_idx,
+                                            int nnz, int mask_heads, int B, int H_q, int H_kv,
+                                            int N, int D, int causal, float scale, void* stream) {
+    if (!q || !k || !v || !o || !kb_ptr || (nnz > 0 && !kb_idx)) return ATTN_ERR_NULL;
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || D <= 0 || nnz < 0) return ATTN_ERR_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_GQA;
+    if (mask_heads != 1 && mask_heads != H_q) return ATTN_ERR_SHAPE;
+    if (D != HD) return ATTN_ERR_HEAD_DIM;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    const int64_t n_sblk = ((int64_t)N + SP_BLOCK - 1) / SP_BLOCK;
+    if (n_sblk > SP_MAX) return ATTN_ERR_SHAPE;
+    const int64_t n_qtiles = ((int64_t)N + BR - 1) / BR;
+    const int64_t total = (int64_t)B * H_q * n_qtiles;
+    if (total > INT32_MAX || (int64_t)B * H_q > INT32_MAX) return ATTN_ERR_SHAPE;
+    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
+    if (mis != 0 || (((uintptr_t)lse | (uintptr_t)kb_ptr | (uintptr_t)kb_idx) & 3) != 0)
+        return ATTN_ERR_ALIGN;
+    const size_t qo_bytes = (size_t)B * H_q * N * HD * 2;
+    const size_t kv_bytes = (size_t)B * H_kv * N * HD * 2;
+    const size_t lse_bytes = lse ? (size_t)B * H_q * N * 4 : 0;
+    const size_t ptr_bytes = (size_t)(mask_heads * n_sblk + 1) * 4;
+    const size_t idx_bytes = (size_t)nnz * 4;
+    const void* ins[5] = {q, k, v, kb_ptr, kb_idx};
+    const size_t in_bytes[5] = {qo_bytes, kv_bytes, kv_bytes, ptr_bytes, idx_bytes};
+    for (int i = 0; i < 5; ++i)
+        if (ins[i] && in_bytes[i] &&
+            (overlaps(o, qo_bytes, ins[i], in_bytes[i]) ||
+             (lse && overlaps(lse, lse_bytes, ins[i], in_bytes[i]))))
+            return ATTN_ERR_ALIAS;
+    if (lse && overlaps(lse, lse_bytes, o, qo_bytes)) return ATTN_ERR_ALIAS;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
+
+    Params p = {};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.N = N;
+    p.group = H_q / H_kv;
+    p.n_qtiles = (int)n_qtiles;
+    p.total = (int)total;
+    p.kb_ptr = kb_ptr;
+    p.kb_idx = kb_idx;
+    p.nnz = nnz;
+    p.mask_heads = mask_heads;
+    p.n_sblk = (int)n_sblk;
+    set_scale(p, scale);
+    return launch_fwd<false, true>(p, causal != 0, stream);
 }
 
 extern "C" double attn_fwd_flops(int B, int H_q, int N, int D, int causal) {

@@ -353,3 +353,35 @@ def test_python_fp8_rejects_bad_tensors():
         sdpa.fwd_fp8(q, q, q)                       # CPU tensors
     with pytest.raises(ValueError):
         sdpa.fwd_fp8(q.to(torch.bfloat16), q, q)    # wrong dtype
+
+
+# attn_fwd_blocksparse (fake, far-apart addresses; validation only).  N = 64 -> one
+# 128-block: kb_ptr holds 2 offsets (mask_heads = 1).
+BS = dict(OK_ARGS, ptr=0xA00000000, idx=0xC00000000, nnz=1, mh=1)
+
+
+def call_bs(**kw):
+    a = dict(BS)
+    a.update(kw)
+    return sdpa.attn_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ptr"], a["idx"],
+                                     a["nnz"], a["mh"], a["B"], a["H_q"], a["H_kv"], a["N"],
+                                     a["D"], a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptr=None), 1), (dict(idx=None), 1), (dict(q=None), 1),
+    (dict(nnz=-1), 2), (dict(mh=2), 2), (dict(N=0), 2), (dict(N=2048 * 128 + 1), 2),
+    (dict(H_q=3), 3), (dict(D=64), 4), (dict(scale=float("nan")), 5),
+    (dict(ptr=0xA00000002), 6), (dict(idx=0xC00000001), 6), (dict(q=Q + 8), 6),
+    (dict(o=0xA00000000 - 64), 7), (dict(lse=0xC00000000), 7), (dict(o=K), 7),
+])
+def test_blocksparse_argument_errors(lib, kw, code):
+    assert call_bs(**kw) == code
+
+
+def test_blocksparse_valid_arguments_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_bs() == 9 and call_bs(idx=None, nnz=0, causal=1) == 9
+    assert call_bs(mh=4, N=256) == 9
