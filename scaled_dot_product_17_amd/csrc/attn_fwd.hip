@@ -511,9 +511,16 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         constexpr uint32_t KS = K_RING + decltype(ks_t)::value * BLK_BYTES;
         constexpr uint32_t VS = V_RING + decltype(vs_t)::value * BLK_BYTES;
         const bool valid = g < n_blk;
-        if (!FIRST && valid && needs_mask(g)) apply_mask(s, g);
-        scores(sn, KS);
-        if constexpr (!FIRST) pv(pp, VS);
+        // SPARSE: a wave skips the work of blocks its own query block does not
+        // list (wave-uniform): the scores of g+1, the softmax of g, the PV of g-1
+        const bool use_n = !SPARSE || (g + 1 < n_blk_wg && sp_member(g + 1));
+        const bool use_g = !SPARSE || (valid && sp_member(g));
+        const bool use_p = !SPARSE || (g >= 1 && sp_member(g - 1));
+        if (!FIRST && valid && use_g && needs_mask(g)) apply_mask(s, g);
+        if (use_n) scores(sn, KS);
+        if constexpr (!FIRST)
+            if (use_p) pv(pp, VS);
+        if (!use_g) return;
         float ls, lbs;
         probs(s, pc, ls, lbs);
         // keep P_g ahead of the branch below (not sunk into its fall-through
