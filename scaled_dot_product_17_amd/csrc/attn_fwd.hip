@@ -54,10 +54,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
-constexpr int BR = 256;                    // query rows per workgroup
-constexpr int NWAVE = 8;                   // waves per workgroup
-constexpr int NTHREAD = NWAVE * 64;
-constexpr int DMA_PER_WAVE = 32 / (4 * NWAVE);   // 4-row DMA instructions per wave per key block
+// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for short
+// sequences, where twice as many workgroups balance the grid better and the
+// two workgroups sharing a CU are not tied by one barrier).
+constexpr int BR = 256;                    // query rows per 8-wave workgroup
+constexpr int NWAVE = 8;
+constexpr int SHORT_N = 4096;              // dense sequences up to this length use 4 waves
 constexpr int ROW_BYTES = HD * 2;          // 256 B per K/V/Q/O row
 constexpr int KB = 32;                     // keys per pipeline step (one MFMA M block)
 constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB per K or V block
@@ -173,8 +175,12 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
 }
 
-template <bool CAUSAL, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
+template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
+    static_assert(NW == 8 || (NW == 4 && !SPARSE), "a block-sparse workgroup holds two 128-row blocks");
+    constexpr int BRW = 32 * NW;                 // query rows of this workgroup
+    constexpr int NTH = NW * 64;
+    constexpr int DMA_PER_WAVE = 32 / (4 * NW);  // 4-row DMA instructions per wave per key block
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SPARSE ? SP_BYTES : 0)];
 
     const int tid = threadIdx.x;
@@ -211,9 +217,9 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
     if constexpr (VARLEN) {
         s0 = min(max(p.cu[b], 0), N);
         s1 = min(max(p.cu[b + 1], s0), N);
-        if (qt * BR >= s1 - s0) return;   // past this sequence's end: whole workgroup, no barrier yet
+        if (qt * BRW >= s1 - s0) return;   // past this sequence's end: whole workgroup, no barrier yet
     }
-    const int q0 = s0 + qt * BR;
+    const int q0 = s0 + qt * BRW;
     const int wq0 = q0 + wave * 32;       // first query row of this wave
     const int myq = wq0 + l32;            // query row of this lane
 
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         uint8_t* f0 = (uint8_t*)lds;             // key blocks listed by query block 2qt
         uint8_t* f1 = (uint8_t*)lds + SP_MAX;    // ... and by query block 2qt+1
         int* wsum = (int*)(lds + LDS_BYTES + 2 * SP_MAX);
-        for (int i = tid; i < 2 * SP_MAX / 4; i += NTHREAD) ((uint32_t*)lds)[i] = 0u;
+        for (int i = tid; i < 2 * SP_MAX / 4; i += NTH) ((uint32_t*)lds)[i] = 0u;
         __syncthreads();
         const int nsb = p.n_sblk;
         const size_t mh = p.mask_heads == 1 ? 0 : (size_t)h;
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
                 const int a = min(max(p.kb_ptr[mh * nsb + qb], 0), p.nnz);
                 const int e = min(max(p.kb_ptr[mh * nsb + qb + 1], a), p.nnz);
                 uint8_t* f = half ? f1 : f0;
-                for (int x = a + tid; x < e; x += NTHREAD) {
+                for (int x = a + tid; x < e; x += NTH) {
                     const int kb = p.kb_idx[x];
                     // causal: key blocks after the query block hold no visible key
                     if (kb >= 0 && kb < nsb && (!CAUSAL || kb <= qb)) f[kb] = 1;
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         __syncthreads();
         int before = 0, n_u = 0;
 #pragma unroll
-        for (int w = 0; w < NWAVE; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const int c = wsum[w];
             before += w < wave ? c : 0;
             n_u += c;
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         n_blk_wg = 4 * n_u;
         n_blk = wq0 < N ? n_blk_wg : 0;
     } else if constexpr (VARLEN) {
-        const int r_end = min(q0 + BR, s1);
+        const int r_end = min(q0 + BRW, s1);
         kb0 = p.left >= 0 ? max(s0, q0 - p.left) : s0;
         int khi = s1 - 1;
         if (CAUSAL) khi = min(khi, r_end - 1);
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         n_blk_wg = n_blk_all;
         n_blk = n_blk_all;
         if (CAUSAL) {
-            n_blk_wg = min(n_blk_all, (min(q0 + BR, N) - 1) / KB + 1);
+            n_blk_wg = min(n_blk_all, (min(q0 + BRW, N) - 1) / KB + 1);
             n_blk = min(n_blk_all, wq0 / KB + 1);
         }
         if (wq0 >= N) n_blk = 0;   // a wave of padding rows past the end computes nothing
@@ -378,8 +384,8 @@ __global__ __launch_bounds__(NTHREAD, 2) void attn_fwd_kernel(Params p) {
         // union build's scratch must be gone before the first block arrives)
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < LDS_BYTES / (16 * NTHREAD); ++i)
-            *(u32x4*)(lds + 16 * (tid + NTHREAD * i)) = z;
+        for (int i = 0; i < LDS_BYTES / (16 * NTH); ++i)
+            *(u32x4*)(lds + 16 * (tid + NTH * i)) = z;
         __syncthreads();
     }
     dma_block(kbase, k_dma, K_RING, 0);
@@ -661,13 +667,13 @@ void set_scale(Params& p, float scale) {
     p.lse_scale = mag;
 }
 
-template <bool VARLEN, bool SPARSE>
+template <bool VARLEN, bool SPARSE, int NW = NWAVE>
 attn_status launch_fwd(const Params& p, bool causal, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     if (causal)
-        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW>), dim3((unsigned)p.total), dim3(NW * 64), 0, s, p);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE>), dim3((unsigned)p.total), dim3(NTHREAD), 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW>), dim3((unsigned)p.total), dim3(NW * 64), 0, s, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -683,7 +689,9 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     // one head panel is addressed with 32-bit byte offsets
     if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    const int64_t n_qtiles = ((int64_t)N + BR - 1) / BR;
+    const bool short_n = N <= SHORT_N;
+    const int br = short_n ? BR / 2 : BR;
+    const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
     const int64_t total = (int64_t)B * H_q * n_qtiles;
     if (total > INT32_MAX || (int64_t)B * H_q > INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
@@ -715,7 +723,8 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     p.n_qtiles = (int)n_qtiles;
     p.total = (int)total;
     set_scale(p, scale);
-    return launch_fwd<false, false>(p, causal != 0, stream);
+    return short_n ? launch_fwd<false, false, NWAVE / 2>(p, causal != 0, stream)
+                   : launch_fwd<false, false, NWAVE>(p, causal != 0, stream);
 }
 
 extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
