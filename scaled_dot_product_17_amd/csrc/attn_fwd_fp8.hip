@@ -56,9 +56,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int HD = 128;                      // head dimension handled by this kernel
 constexpr int ROW8 = HD;                     // bytes per e4m3 row
-constexpr int BR = 256;                      // query rows per workgroup
-constexpr int NWAVE = 8;
-constexpr int NTHREAD = NWAVE * 64;
+constexpr int BR = 256;                      // query rows per 8-wave workgroup
+constexpr int SHORT_N = 4096;                // sequences up to this length use 4-wave workgroups
 constexpr int KB = 64;                       // keys per pipeline step (one MFMA k extent)
 constexpr int BLK_BYTES = KB * ROW8;         // 8 KiB per K or V block
 constexpr int K_RING = 0;                    // LDS: a ring of 4 K blocks, then 4 V blocks
@@ -113,8 +112,13 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(NTHREAD, 1) void attn_fwd_fp8_kernel(Params p) {
+// NW waves per workgroup (8, or 4 for short sequences: twice the workgroups,
+// two per CU, not tied by one barrier)
+template <bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p) {
+    constexpr int BRW = 32 * NW;      // query rows of this workgroup
+    constexpr int NTH = NW * 64;
+    constexpr int DPW = 8 / NW;       // 8-row DMA instructions per wave per key block
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void attn_fwd_fp8_kernel(Params p) {
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
     const int N = p.N;
-    const int q0 = qt * BR;
+    const int q0 = qt * BRW;
     const int wq0 = q0 + wave * 32;
     const int myq = wq0 + l32;
 
@@ -143,28 +147,32 @@ __global__ __launch_bounds__(NTHREAD, 1) void attn_fwd_fp8_kernel(Params p) {
     const int n_blk_all = (N + KB - 1) / KB;
     int n_blk_wg = n_blk_all, n_blk = n_blk_all;
     if (CAUSAL) {
-        n_blk_wg = min(n_blk_all, (min(q0 + BR, N) - 1) / KB + 1);
+        n_blk_wg = min(n_blk_all, (min(q0 + BRW, N) - 1) / KB + 1);
         n_blk = min(n_blk_all, (wq0 + 31) / KB + 1);
     }
     if (wq0 >= N) n_blk = 0;
     const uint8_t* kbase = p.k + kv_panel;
     const uint8_t* vbase = p.v + kv_panel;
 
-    // ---- LDS DMA: each wave copies rows 8*wave .. 8*wave+7 of a block with one
-    // instruction (64 lanes x 16 bytes, lane order); lane L fetches the logical
-    // chunk that belongs at its physical position.
+    // ---- LDS DMA: each wave copies rows 8*DPW*wave .. of a block with DPW
+    // instructions of 8 rows (64 lanes x 16 bytes, lane order); lane L fetches
+    // the logical chunk that belongs at its physical position.
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-    uint32_t k_dma, v_dma;
-    {
-        const int row = 8 * wave + (lane >> 3);
+    uint32_t k_dma[DPW], v_dma[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+        const int row = 8 * DPW * wave + 8 * i + (lane >> 3);
         const int pc = lane & 7;
-        k_dma = (uint32_t)(row * ROW8 + ((pc ^ k_swz(row)) << 4));
-        v_dma = (uint32_t)(row * ROW8 + ((pc ^ v_swz(row)) << 4));
+        k_dma[i] = (uint32_t)(row * ROW8 + ((pc ^ k_swz(row)) << 4));
+        v_dma[i] = (uint32_t)(row * ROW8 + ((pc ^ v_swz(row)) << 4));
     }
-    auto dma_block = [&](const uint8_t* panel, uint32_t voff, int ring, int g) {
+    auto dma_block = [&](const uint8_t* panel, const uint32_t* voff, int ring, int g) {
         if (g < n_blk_wg) {
             const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW8);
-            lds_dma16(r, lds_base + ring + (g & 3) * BLK_BYTES + 8 * wave * ROW8, voff);
+#pragma unroll
+            for (int i = 0; i < DPW; ++i)
+                lds_dma16(r, lds_base + ring + (g & 3) * BLK_BYTES + (8 * DPW * wave + 8 * i) * ROW8,
+                          voff[i]);
         }
     };
 
@@ -196,8 +204,8 @@ __global__ __launch_bounds__(NTHREAD, 1) void attn_fwd_fp8_kernel(Params p) {
         // never-written rows of a tail block must read as zeros, not stale LDS
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < LDS_BYTES / (16 * NTHREAD); ++i)
-            *(u32x4*)(lds + 16 * (tid + NTHREAD * i)) = z;
+        for (int i = 0; i < LDS_BYTES / (16 * NTH); ++i)
+            *(u32x4*)(lds + 16 * (tid + NTH * i)) = z;
         __syncthreads();
     }
     dma_block(kbase, k_dma, K_RING, 0);
@@ -428,7 +436,9 @@ extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* 
     const float mag = (float)std::fabs(prod);
     if (!std::isfinite(mag)) return ATTN_ERR_SCALE;
     if ((int64_t)N * HD * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    const int64_t n_qtiles = ((int64_t)N + BR - 1) / BR;
+    const bool short_n = N <= SHORT_N;
+    const int br = short_n ? BR / 2 : BR;
+    const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
     const int64_t total = (int64_t)B * H_q * n_qtiles;
     if (total > INT32_MAX || (int64_t)B * H_q > INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q8 | (uintptr_t)k8 | (uintptr_t)v8 | (uintptr_t)o) & 15;
@@ -466,9 +476,13 @@ extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* 
     p.lse_scale = mag;
     p.dv = descale_v;
     hipStream_t s = (hipStream_t)stream;
-    if (causal)
-        hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
-    else
-        hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, dim3((unsigned)total), dim3(NTHREAD), 0, s, p);
+    const dim3 grid((unsigned)total);
+    if (short_n) {
+        if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4>), grid, dim3(256), 0, s, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8>), grid, dim3(512), 0, s, p);
+        else hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8>), grid, dim3(512), 0, s, p);
+    }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
