@@ -54,9 +54,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
-// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for short
-// sequences, where twice as many workgroups balance the grid better and the
-// two workgroups sharing a CU are not tied by one barrier).
+// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for short dense
+// sequences and packed batches, where twice as many workgroups balance the
+// grid better and the two workgroups sharing a CU are not tied by one barrier).
 constexpr int BR = 256;                    // query rows per 8-wave workgroup
 constexpr int NWAVE = 8;
 constexpr int SHORT_N = 4096;              // dense sequences up to this length use 4 waves
@@ -739,7 +739,10 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     if (D != HD) return ATTN_ERR_HEAD_DIM;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if ((int64_t)total * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    const int64_t n_qtiles = ((int64_t)max_seqlen + BR - 1) / BR;
+    // 4-wave workgroups: a packed or windowed tile sees few keys, and twice the
+    // workgroups balance better (as for short dense sequences)
+    const int br = BR / 2;
+    const int64_t n_qtiles = ((int64_t)max_seqlen + br - 1) / br;
     const int64_t grid = (int64_t)n_seq * H_q * n_qtiles;
     if (grid > INT32_MAX || n_seq == INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
@@ -776,7 +779,7 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;
     set_scale(p, scale);
-    return launch_fwd<true, false>(p, causal != 0, stream);
+    return launch_fwd<true, false, NWAVE / 2>(p, causal != 0, stream);
 }
 
 extern "C" attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
