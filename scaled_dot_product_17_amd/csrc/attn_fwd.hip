@@ -689,7 +689,9 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     // one head panel is addressed with 32-bit byte offsets
     if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    const bool short_n = N <= SHORT_N;
+    // measured: 4 waves win up to 4096 tokens, and causal up to 8192 (a causal
+    // tile sees half the keys on average)
+    const bool short_n = N <= SHORT_N || (causal && N <= 2 * SHORT_N);
     const int br = short_n ? BR / 2 : BR;
     const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
     const int64_t total = (int64_t)B * H_q * n_qtiles;
