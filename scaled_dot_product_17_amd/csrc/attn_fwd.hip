@@ -177,10 +177,12 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
 
 template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
-    static_assert(NW == 8 || (NW == 4 && !SPARSE), "a block-sparse workgroup holds two 128-row blocks");
+    static_assert(NW == 8 || NW == 4, "workgroups of 4 or 8 waves");
     constexpr int BRW = 32 * NW;                 // query rows of this workgroup
     constexpr int NTH = NW * 64;
     constexpr int DMA_PER_WAVE = 32 / (4 * NW);  // 4-row DMA instructions per wave per key block
+    constexpr int QB_WG = BRW / SP_BLOCK;        // SPARSE: query blocks per workgroup (1 or 2)
+    constexpr int SP_PER_T = SP_MAX / NTH;       // SPARSE: key blocks each thread compacts
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SPARSE ? SP_BYTES : 0)];
 
     const int tid = threadIdx.x;
@@ -235,21 +237,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     int kb0 = 0, n_blk_wg, n_blk;
     int lo_i = 0, hi_i = N - 1;           // this lane's allowed keys (VARLEN)
     int lo_max = 0, hi_min = N - 1;       // keys every valid row of the wave allows (VARLEN)
-    // SPARSE: the union of the two query blocks' lists, built in LDS (the rings
-    // serve as scratch before the first copy); stream block g is 32-key part
-    // g % 4 of union entry g / 4
+    // SPARSE: the union of the workgroup's query blocks' lists (one or two),
+    // built in LDS (the rings serve as scratch before the first copy); stream
+    // block g is 32-key part g % 4 of union entry g / 4
     const uint16_t* sp = (const uint16_t*)(lds + LDS_BYTES);
     if constexpr (SPARSE) {
-        uint8_t* f0 = (uint8_t*)lds;             // key blocks listed by query block 2qt
-        uint8_t* f1 = (uint8_t*)lds + SP_MAX;    // ... and by query block 2qt+1
+        uint8_t* f0 = (uint8_t*)lds;             // key blocks listed by query block QB_WG*qt
+        uint8_t* f1 = (uint8_t*)lds + SP_MAX;    // ... and by query block 2qt+1 (8 waves)
         int* wsum = (int*)(lds + LDS_BYTES + 2 * SP_MAX);
         for (int i = tid; i < 2 * SP_MAX / 4; i += NTH) ((uint32_t*)lds)[i] = 0u;
         __syncthreads();
         const int nsb = p.n_sblk;
         const size_t mh = p.mask_heads == 1 ? 0 : (size_t)h;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int qb = 2 * qt + half;
+        for (int half = 0; half < QB_WG; ++half) {
+            const int qb = QB_WG * qt + half;
             if (qb < nsb) {
                 // offsets clamped to [0, nnz]: a malformed list cannot read out of range
                 const int a = min(max(p.kb_ptr[mh * nsb + qb], 0), p.nnz);
@@ -263,11 +265,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
             }
         }
         __syncthreads();
-        // compaction in key-block order: thread t owns key blocks 4t .. 4t+3
-        int bits[4], cnt = 0;
+        // compaction in key-block order: thread t owns SP_PER_T consecutive key blocks
+        int bits[SP_PER_T], cnt = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kb = 4 * tid + j;
+        for (int j = 0; j < SP_PER_T; ++j) {
+            const int kb = SP_PER_T * tid + j;
             bits[j] = kb < nsb ? (f0[kb] | (f1[kb] << 1)) : 0;
             cnt += bits[j] != 0;
         }
@@ -289,8 +291,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         int pos = before + incl - cnt;
         uint16_t* spw = (uint16_t*)(lds + LDS_BYTES);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (bits[j] != 0) spw[pos++] = (uint16_t)((4 * tid + j) | (bits[j] << 14));
+        for (int j = 0; j < SP_PER_T; ++j)
+            if (bits[j] != 0) spw[pos++] = (uint16_t)((SP_PER_T * tid + j) | (bits[j] << 14));
         __syncthreads();
         n_blk_wg = 4 * n_u;
         n_blk = wq0 < N ? n_blk_wg : 0;
@@ -797,7 +799,10 @@ extern "C" attn_status attn_fwd_blocksparse(const void* q, const void* k, const 
     if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
     const int64_t n_sblk = ((int64_t)N + SP_BLOCK - 1) / SP_BLOCK;
     if (n_sblk > SP_MAX) return ATTN_ERR_SHAPE;
-    const int64_t n_qtiles = ((int64_t)N + BR - 1) / BR;
+    // 4-wave workgroups of 128 rows: each is one query block with one list, so
+    // no workgroup streams key blocks that only some of its waves need
+    const int br = BR / 2;
+    const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
     const int64_t total = (int64_t)B * H_q * n_qtiles;
     if (total > INT32_MAX || (int64_t)B * H_q > INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
@@ -839,7 +844,7 @@ extern "C" attn_status attn_fwd_blocksparse(const void* q, const void* k, const 
     p.mask_heads = mask_heads;
     p.n_sblk = (int)n_sblk;
     set_scale(p, scale);
-    return launch_fwd<false, true>(p, causal != 0, stream);
+    return launch_fwd<false, true, NWAVE / 2>(p, causal != 0, stream);
 }
 
 extern "C" double attn_fwd_flops(int B, int H_q, int N, int D, int causal) {
