@@ -8,6 +8,7 @@ size (finite outputs, determinism, GQA == repeated MHA, causal structure).
 """
 import math
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -70,7 +71,7 @@ def test_workload_sampled(name):
     o, lse = sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
-    rng = np.random.default_rng(abs(hash(name)) % (2 ** 32))
+    rng = np.random.default_rng(zlib.crc32(name.encode()))   # stable across processes
     rows = parity.sample_rows(w.B, w.H_q, w.N, rng, per_head=24)
     o_ref, lse_ref = oracle.attn_ref(q, k, v, w.causal, w.scale, rows=rows)
     of = o.view(-1, 128)[torch.from_numpy(rows).cuda()]
@@ -165,3 +166,25 @@ def test_errors_reported():
     with pytest.raises(sdpa.AttnError) as e:
         sdpa.fwd(ok, ok, ok, out=ok)
     assert e.value.status == 7
+
+
+def test_long_sequence_sampled():
+    """N = 262144 (causal GQA, one batch): byte offsets deep into a head panel
+    and 8192 key blocks per row stream; sampled rows across the sequence,
+    including the first and the last, against the oracle."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = 1, 2, 1, 262144
+    say(f"[long sequence] N={N}")
+    q = synth.normal_bf16(18000, (B, Hq, N, 128))
+    k = synth.normal_bf16(18001, (B, Hkv, N, 128))
+    v = synth.normal_bf16(18002, (B, Hkv, N, 128))
+    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse).all())
+    rows = np.array([0, 1, 255, 256, N // 2 + 17, N - 257, N - 1, N, N + 4095, 2 * N - 1], np.int64)
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, True, SCALE, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    m = parity.compare(bf16_to_np(o.view(-1, 128)[sel]), lse.view(-1)[sel].cpu().numpy(), o_ref, lse_ref)
+    say(f"  N={N}: {m}")
+    parity.check(m, f"N={N}")
