@@ -35,6 +35,7 @@
 //     are the same quantities whichever reference was used.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -87,6 +88,7 @@ struct Params {
     int n_qtiles;     // ceil(N / BR)
     int total;        // B * Hq * n_qtiles workgroups
     int q_mode;       // 0: Q as given, 1: Q negated, 2: Q replaced by zeros
+    int cgroup;       // dense causal: heads whose tiles are interleaved (<= 1: one head)
     float c;          // |scale| * log2(e), always > 0
     float lse_scale;  // |scale|
     // packed variable-length batch (VARLEN kernels only): B = 1 and N = tokens
@@ -203,6 +205,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         const int per = p.B * p.Hq;
         qt = p.n_qtiles - 1 - logical / per;
         bh = logical % per;
+    } else if (CAUSAL && !SPARSE) {
+        // groups of cgroup (batch, head)s one after another, so the tiles of a
+        // group share K/V in the L2 of one XCD; within a group tile-major,
+        // heaviest tile first.  A group holds at least as many tiles as an XCD
+        // has workgroup slots, so the light tiles of one group, not the heavy
+        // tiles of the next, fill the end of each XCD's share of the grid.
+        const int per = p.B * p.Hq;
+        const int G = p.cgroup > 1 ? p.cgroup : 1;
+        const int grp = logical / (G * p.n_qtiles);
+        const int r = logical - grp * G * p.n_qtiles;
+        const int gh = min(G, per - grp * G);   // heads in this group (the last may be short)
+        qt = p.n_qtiles - 1 - r / gh;
+        bh = grp * G + r % gh;
     } else {
         // one (batch, head) after another, so a head's tiles share K/V in the
         // L2 of one XCD
@@ -726,6 +741,10 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     p.group = H_q / H_kv;
     p.n_qtiles = (int)n_qtiles;
     p.total = (int)total;
+    // causal: interleave the tiles of enough heads to fill one XCD's workgroup
+    // slots (32 CUs x 2 four-wave or 1 eight-wave workgroups)
+    const int64_t slots = short_n ? 64 : 32;
+    p.cgroup = (int)std::min<int64_t>((int64_t)B * H_q, (slots + n_qtiles - 1) / n_qtiles);
     set_scale(p, scale);
     return short_n ? launch_fwd<false, false, NWAVE / 2>(p, causal != 0, stream)
                    : launch_fwd<false, false, NWAVE>(p, causal != 0, stream);

@@ -40,6 +40,7 @@
 //     move every row to its running max (rare, wave-uniform branch).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -80,6 +81,7 @@ struct Params {
     int n_qtiles;     // ceil(N / BR)
     int total;        // B * Hq * n_qtiles workgroups
     int q_mode;       // 0: Q as given, 1: Q negated, 2: Q replaced by zeros
+    int cgroup;       // causal: heads whose tiles are interleaved (<= 1: one head)
     float c;          // |scale*dq*dk| * log2(e), > 0
     float lse_scale;  // |scale*dq*dk|
     float dv;         // V descale, applied to O
@@ -128,9 +130,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
     const int hh = lane >> 5;    // which half of the wave
 
     const int logical = xcd_remap(blockIdx.x, p.total);
-    const int bh = logical / p.n_qtiles;
-    int qt = logical % p.n_qtiles;
-    if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
+    int bh, qt;
+    if (CAUSAL) {
+        // groups of cgroup heads one after another (a group's tiles share K/V in
+        // one XCD's L2), tile-major and heaviest tile first within a group; a
+        // group holds at least an XCD's worth of workgroup slots, so light tiles
+        // of one group, not heavy tiles of the next, end each XCD's share
+        const int per = p.B * p.Hq;
+        const int G = p.cgroup > 1 ? p.cgroup : 1;
+        const int grp = logical / (G * p.n_qtiles);
+        const int r = logical - grp * G * p.n_qtiles;
+        const int gh = min(G, per - grp * G);
+        qt = p.n_qtiles - 1 - r / gh;
+        bh = grp * G + r % gh;
+    } else {
+        bh = logical / p.n_qtiles;
+        qt = logical % p.n_qtiles;
+    }
     const int b = bh / p.Hq;
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
@@ -472,6 +488,10 @@ extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* 
     p.n_qtiles = (int)n_qtiles;
     p.total = (int)total;
     p.q_mode = mag == 0.f ? 2 : (prod > 0 ? 0 : 1);
+    // causal: interleave enough heads' tiles to fill one XCD's workgroup slots
+    // (32 CUs x 2 four-wave or 1 eight-wave workgroups)
+    const int64_t slots = short_n ? 64 : 32;
+    p.cgroup = (int)std::min<int64_t>((int64_t)B * H_q, (slots + n_qtiles - 1) / n_qtiles);
     p.c = (float)((double)(mag > 0.f ? mag : 1.0f) * 1.4426950408889634);
     p.lse_scale = mag;
     p.dv = descale_v;
