@@ -319,6 +319,7 @@ def cpu_baseline_bwd(w):
 
 
 def main_bwd(args, w):
+    import scaled_dot_product_17_amd as sdpa
     log(f"[bench bwd] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} D={w.D} "
         f"causal={w.causal}")
     t = time_bwd(w, args.steps, args.warmup)
@@ -352,12 +353,17 @@ def main_bwd(args, w):
         "cpu_baseline": None,
     }
     if args.sweep:
-        log(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s} {'dq ms':>8s} {'dkdv ms':>8s}")
+        # ms: the whole step as sdpa.bwd runs it (its dK/dV step split over
+        # `parts` of each group's query heads when the library chooses to);
+        # dkdv(1): the unsplit dK/dV kernel alone
+        log(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s} {'parts':>5s} {'dq ms':>8s} "
+            f"{'dkdv(1) ms':>10s}")
         for name, x in synth.WORKLOADS.items():
             tt = time_bwd(x, max(5, args.steps // 5), 3)
+            parts = sdpa.attn_bwd_splits(x.B, x.H_q, x.H_kv, x.N, x.D, 0)
             tf = 10 * x.D * bwd_pairs(x) / (tt["ms_step"] * 1e-3) / 1e12
             log(f"{name:36s} {tt['ms_step']:9.3f} {tf:9.1f} {100 * tf / PEAK_TFLOPS:7.1f} "
-                f"{tt['dq']:8.3f} {tt['dkdv']:8.3f}")
+                f"{parts:5d} {tt['dq']:8.3f} {tt['dkdv']:10.3f}")
     if not args.no_cpu_baseline:
         log("[bench bwd] timing the backward oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline_bwd(w)

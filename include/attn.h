@@ -230,6 +230,44 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const voi
                           void* stream);
 
 /*
+ * attn_bwd_ws: attn_bwd with the dK/dV step split over the query heads of
+ * each K/V head's group.  The dK/dV step runs one workgroup per 128 keys of a
+ * K/V head, so with few K/V heads (MQA, small GQA batches) it has fewer
+ * workgroups than the GPU has compute units.  Here each of n_splits parts of a
+ * group's query heads writes fp32 partial dK and dV into `workspace`, and a
+ * third kernel adds the parts in part order and rounds once to bf16.
+ *
+ * n_splits   parts per group, or <= 0 to let the library choose
+ *            (attn_bwd_splits); it is reduced to a divisor of H_q / H_kv.  With
+ *            one part this is exactly attn_bwd and `workspace` is not used (it
+ *            may be NULL).
+ * workspace  device memory of at least attn_bwd_workspace_bytes(B, H_q, H_kv,
+ *            N, D, n_splits) bytes, 16-byte aligned, owned by the caller,
+ *            disjoint from every argument, and not used by other work until
+ *            the call's work has finished.  Its contents on entry do not matter.
+ * Other arguments, layouts and errors as for attn_bwd, plus
+ * ATTN_ERR_WORKSPACE (too small).  Precision as for attn_bwd, except that dK
+ * and dV are the fp32 sums of the parts' fp32 sums, still reproducible
+ * bitwise for a given n_splits.
+ */
+attn_status attn_bwd_ws(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
+                        float scale, int n_splits, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* attn_bwd_splits: the parts attn_bwd_ws uses for these arguments (n_splits <=
+ * 0: the library's choice, the smallest divisor of H_q / H_kv that gives at
+ * least 256 dK/dV workgroups, at most 16), or 0 if they are invalid.
+ * Host-only arithmetic. */
+int attn_bwd_splits(int B, int H_q, int H_kv, int N, int D, int n_splits);
+
+/* attn_bwd_workspace_bytes: bytes of workspace attn_bwd_ws needs for these
+ * arguments: 2 * parts * B * H_kv * N * D * 4 when it splits, else 0 (also 0 if
+ * they are invalid).  Host-only arithmetic. */
+size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int n_splits);
+
+/*
  * attn_decode: enqueue split-KV decode attention on `stream`.
  *
  * The operation.  M query rows per (batch, query head) are the last M

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE",
                 10: "ATTN_ERR_WORKSPACE"}
-EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_fwd_blocksparse", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode",
+EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_fwd_blocksparse", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
+            "attn_bwd_ws", "attn_bwd_splits", "attn_bwd_workspace_bytes", "attn_decode",
             "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
             "attn_fwd_flops", "attn_bwd_flops", "attn_decode_flops")
 
@@ -61,6 +62,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_bwd_dkdv.restype = ctypes.c_int
             lib.attn_bwd_dkdv.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [
                 ctypes.c_float, ctypes.c_void_p]
+            lib.attn_bwd_ws.restype = ctypes.c_int
+            lib.attn_bwd_ws.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            lib.attn_bwd_splits.restype = ctypes.c_int
+            lib.attn_bwd_splits.argtypes = [ctypes.c_int] * 6
+            lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+            lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 6
             lib.attn_fwd_varlen.restype = ctypes.c_int
             lib.attn_fwd_varlen.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 9 + [
                 ctypes.c_float, ctypes.c_void_p]
@@ -198,6 +206,21 @@ def attn_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, H_q, H_kv, N, D, causal,
                                 stream)
 
 
+def attn_bwd_ws(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H_q, H_kv, N, D, causal, scale,
+                n_splits, workspace, workspace_bytes, stream) -> int:
+    return load().attn_bwd_ws(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H_q), int(H_kv),
+                              int(N), int(D), int(bool(causal)), float(scale), int(n_splits),
+                              workspace, int(workspace_bytes), stream)
+
+
+def attn_bwd_splits(B, H_q, H_kv, N, D, n_splits=0) -> int:
+    return load().attn_bwd_splits(int(B), int(H_q), int(H_kv), int(N), int(D), int(n_splits))
+
+
+def attn_bwd_workspace_bytes(B, H_q, H_kv, N, D, n_splits=0) -> int:
+    return load().attn_bwd_workspace_bytes(int(B), int(H_q), int(H_kv), int(N), int(D), int(n_splits))
+
+
 def attn_bwd_flops(B, H_q, N, D, causal) -> float:
     return load().attn_bwd_flops(int(B), int(H_q), int(N), int(D), int(bool(causal)))
 
@@ -311,13 +334,16 @@ def fwd_fp8(q8, k8, v8, descale_q: float = 1.0, descale_k: float = 1.0, descale_
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-        dq=None, dk=None, dv=None, delta=None):
+        dq=None, dk=None, dv=None, delta=None, n_splits: int = 0, workspace=None):
     """dQ, dK, dV of attention on the current torch stream of q's device.
 
     q, o, dout: bf16 [B, H_q, N, D]; k, v: bf16 [B, H_kv, N, D]; lse: fp32
     [B, H_q, N] from ``fwd`` with the same causal and scale.  Output buffers may
     be given to avoid allocation.  Returns (dq, dk, dv, delta) with delta the
-    fp32 [B, H_q, N] row sums dO . O.
+    fp32 [B, H_q, N] row sums dO . O.  When the library splits the dK/dV step
+    over a group's query heads (attn_bwd_splits; n_splits <= 0: its choice)
+    this calls attn_bwd_ws with `workspace` (a uint8 tensor on q's device, or
+    allocated here), else attn_bwd.
     """
     import torch
 
@@ -346,11 +372,23 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     elif delta.dtype != torch.float32 or tuple(delta.shape) != (B, Hq, N) or \
             not delta.is_contiguous() or delta.device != q.device:
         raise ValueError("delta must be a contiguous fp32 [B, H_q, N] tensor on q's device")
+    ns = attn_bwd_splits(B, Hq, Hkv, N, D, n_splits)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      delta.data_ptr(), B, Hq, Hkv, N, D, causal, scale, stream)
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                B, Hq, Hkv, N, D, causal, scale)
+        if ns > 1:
+            need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, D, ns)
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif not isinstance(workspace, torch.Tensor) or workspace.device != q.device or \
+                    not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on q's device")
+            st = attn_bwd_ws(*args, ns, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), stream)
+        else:
+            st = attn_bwd(*args, stream)
     if st != ATTN_OK:
         raise AttnError(st, status_string(st))
     return dq, dk, dv, delta

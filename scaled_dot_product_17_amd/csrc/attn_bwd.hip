@@ -35,6 +35,7 @@
 //     The two waves of a pair share a SIMD, so A's softmax overlaps B's MFMAs.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -87,7 +88,9 @@ struct BwdParams {
     int B, Hq, Hkv, N;
     int group;              // Hq / Hkv
     int n_qtiles, total_q;  // attn_bwd_dq grid: B * Hq * ceil(N / 256)
-    int n_ktiles, total_k;  // attn_bwd_dkdv grid: B * Hkv * ceil(N / 128)
+    int n_ktiles, total_k;  // attn_bwd_dkdv grid: B * Hkv * ceil(N / 128) * n_split
+    int n_split;            // dK/dV: parts of each group's query heads (1: write dk, dv)
+    float* ws;              // n_split > 1: fp32 partials [n_split][dV, dK][B * Hkv * N][D]
     float c;                // scale * log2(e)
     float scale;
 };
@@ -140,6 +143,18 @@ struct TileReads {
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     const bf16x2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void store_row_f32(float* row, const f32x16 (&acc)[4], float mul, int hh) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[db][4 * r4 + i] * mul;
+            *(f32x4*)(row + 32 * db + 8 * r4 + 4 * hh) = v;
+        }
 }
 
 __device__ __forceinline__ void store_row_bf16(uint16_t* row, const f32x16 (&acc)[4], float mul,
@@ -345,9 +360,15 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
 
     // with a causal mask the first key tiles of a head see the most rows, and
     // they come first in this order
+    // with n_split parts, part sp covers query heads [sp*gh, (sp+1)*gh) of the
+    // group; the key tiles of one (batch, K/V head, part) stay consecutive
+    const int ns = p.n_split > 1 ? p.n_split : 1;
     const int logical = xcd_remap(blockIdx.x, p.total_k);
-    const int bk = logical / p.n_ktiles;
+    const int bks = logical / p.n_ktiles;
     const int kt = logical % p.n_ktiles;
+    const int bk = bks / ns;
+    const int sp = bks % ns;
+    const int gh = p.group / ns;
     const int b = bk / p.Hkv;
     const int kvh = bk % p.Hkv;
     const int N = p.N;
@@ -356,11 +377,11 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
     const int myk = wk0 + l32;
     const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
 
-    // query tiles of 64 rows: t0..n_qt-1 for each query head of the group
+    // query tiles of 64 rows: t0..n_qt-1 for each query head of the part
     const int n_qt = (N + KV_QROWS - 1) / KV_QROWS;
     const int t0 = CAUSAL ? k0 / KV_QROWS : 0;
     const int n_t = n_qt - t0;
-    const int n_it = p.group * n_t;
+    const int n_it = gh * n_t;
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
     uint32_t dma_off[2];
@@ -372,7 +393,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
     // stage it % 3 <- Q, dO, LSE, delta of iteration it
     auto issue = [&](int it) {
         if (it >= n_it) return;
-        const int hq = kvh * p.group + it / n_t;
+        const int hq = kvh * p.group + sp * gh + it / n_t;
         const int t = t0 + it % n_t;
         const size_t r0 = ((size_t)b * p.Hq + hq) * (size_t)N + (size_t)t * KV_QROWS;
         const uint32_t left = (uint32_t)(N - t * KV_QROWS);
@@ -559,8 +580,39 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
     }
 
     if (myk < N) {
-        if (is_a) store_row_bf16(p.dv + kv_panel + (size_t)myk * HD, acc, 1.0f, hh);
-        else store_row_bf16(p.dk + kv_panel + (size_t)myk * HD, acc, p.scale, hh);
+        if (ns == 1) {
+            if (is_a) store_row_bf16(p.dv + kv_panel + (size_t)myk * HD, acc, 1.0f, hh);
+            else store_row_bf16(p.dk + kv_panel + (size_t)myk * HD, acc, p.scale, hh);
+        } else {
+            // this part's fp32 sums; attn_bwd_reduce_kernel adds the parts
+            const size_t rows = (size_t)p.B * p.Hkv * N;
+            const size_t part = (size_t)(2 * sp + (is_a ? 0 : 1)) * rows;
+            store_row_f32(p.ws + (part + ((size_t)b * p.Hkv + kvh) * N + myk) * HD, acc,
+                          is_a ? 1.0f : p.scale, hh);
+        }
+    }
+}
+
+// dV and dK from n_split fp32 partials: summed in part order (so the result is
+// reproducible), rounded once to bf16.  One thread per 4 elements.
+__global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(const float* ws, uint16_t* dk,
+                                                              uint16_t* dv, size_t rows, int ns) {
+    const size_t n4 = rows * HD / 4;   // 4-element groups of one tensor
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n4; i += (size_t)gridDim.x * 256) {
+        const size_t t = i >= n4 ? 1 : 0;   // 0: dV, 1: dK
+        const size_t j = i - t * n4;
+        f32x4 acc = ((const f32x4*)(ws + t * rows * HD))[j];
+        for (int sp = 1; sp < ns; ++sp) {
+            const f32x4 x = ((const f32x4*)(ws + (2 * (size_t)sp + t) * rows * HD))[j];
+            acc[0] += x[0];
+            acc[1] += x[1];
+            acc[2] += x[2];
+            acc[3] += x[3];
+        }
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[e];
+        ((bf16x4*)(t ? dk : dv))[j] = o;
     }
 }
 
@@ -577,7 +629,7 @@ struct Buf {
 // inputs and from each other) and the device, then fills the kernel
 // parameters.  Nothing is launched unless the result is ATTN_OK.
 attn_status prepare(const Buf* ins, int n_in, const Buf* outs, int n_out, int B, int H_q,
-                    int H_kv, int N, int D, float scale, BwdParams& p) {
+                    int H_kv, int N, int D, float scale, BwdParams& p, bool ws_short = false) {
     for (int i = 0; i < n_in; ++i)
         if (!ins[i].ptr) return ATTN_ERR_NULL;
     for (int i = 0; i < n_out; ++i)
@@ -606,6 +658,7 @@ attn_status prepare(const Buf* ins, int n_in, const Buf* outs, int n_out, int B,
             if (ranges_overlap(outs[i].ptr, outs[i].bytes, outs[j].ptr, outs[j].bytes))
                 return ATTN_ERR_ALIAS;
     }
+    if (ws_short) return ATTN_ERR_WORKSPACE;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
 
@@ -639,6 +692,40 @@ void launch_dkdv(const BwdParams& p, bool causal, hipStream_t s) {
         hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)p.total_k), dim3(KV_THREADS), 0, s, p);
     else
         hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)p.total_k), dim3(KV_THREADS), 0, s, p);
+}
+void launch_reduce(const BwdParams& p, hipStream_t s) {
+    const size_t rows = (size_t)p.B * p.Hkv * p.N;
+    const size_t groups = 2 * rows * HD / 4;
+    const unsigned grid = (unsigned)std::min<size_t>((groups + 255) / 256, 8192);
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3(grid), dim3(256), 0, s, (const float*)p.ws, p.dk,
+                       p.dv, rows, p.n_split);
+}
+
+// Parts of each group's query heads for the dK/dV step of attn_bwd_ws: a
+// divisor of the group size.  n_splits <= 0: the smallest divisor that gives
+// at least one dK/dV workgroup per compute unit of an MI355X (256; one
+// workgroup fits per CU), or the largest divisor up to 16 when none does.
+// n_splits > 0: the largest divisor of the group size not above n_splits.
+int bwd_splits(int B, int H_q, int H_kv, int N, int n_splits) {
+    const int group = H_q / H_kv;
+    const int64_t base = (int64_t)B * H_kv * (((int64_t)N + KV_KEYS - 1) / KV_KEYS);
+    int best = 1;
+    for (int s = 1; s <= std::min(group, 16); ++s) {
+        if (group % s != 0) continue;
+        if (n_splits > 0) {
+            if (s <= n_splits) best = s;
+            continue;
+        }
+        best = s;
+        if (base * s >= 256) break;
+    }
+    return best;
+}
+size_t bwd_ws_bytes(int B, int H_kv, int N, int ns) {
+    return ns > 1 ? (size_t)ns * 2 * B * H_kv * (size_t)N * HD * sizeof(float) : 0;
+}
+bool bwd_shape_ok(int B, int H_q, int H_kv, int N, int D) {
+    return B > 0 && H_q > 0 && H_kv > 0 && N > 0 && D == HD && H_q % H_kv == 0;
 }
 
 }  // namespace
@@ -717,6 +804,59 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
     launch_dq(p, causal != 0, s);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
     launch_dkdv(p, causal != 0, s);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int attn_bwd_splits(int B, int H_q, int H_kv, int N, int D, int n_splits) {
+    return bwd_shape_ok(B, H_q, H_kv, N, D) ? bwd_splits(B, H_q, H_kv, N, n_splits) : 0;
+}
+
+extern "C" size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int n_splits) {
+    if (!bwd_shape_ok(B, H_q, H_kv, N, D)) return 0;
+    return bwd_ws_bytes(B, H_kv, N, bwd_splits(B, H_q, H_kv, N, n_splits));
+}
+
+extern "C" attn_status attn_bwd_ws(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
+                                   float scale, int n_splits, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    const int ns = bwd_shape_ok(B, H_q, H_kv, N, D) ? bwd_splits(B, H_q, H_kv, N, n_splits) : 1;
+    if (ns == 1)
+        return attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H_q, H_kv, N, D, causal, scale,
+                        stream);
+    const size_t need = bwd_ws_bytes(B, H_kv, N, ns);
+    const Buf ins[6] = {{q, q_bytes(B, H_q, N), 16}, {k, kv_bytes(B, H_kv, N), 16},
+                        {v, kv_bytes(B, H_kv, N), 16}, {o, q_bytes(B, H_q, N), 16},
+                        {dout, q_bytes(B, H_q, N), 16}, {lse, row_bytes(B, H_q, N), 4}};
+    const Buf outs[5] = {{dq, q_bytes(B, H_q, N), 16}, {dk, kv_bytes(B, H_kv, N), 16},
+                         {dv, kv_bytes(B, H_kv, N), 16}, {delta, row_bytes(B, H_q, N), 4},
+                         {workspace, std::min(need, workspace_bytes), 16}};
+    BwdParams p;
+    const attn_status st = prepare(ins, 6, outs, 5, B, H_q, H_kv, N, D, scale, p, workspace_bytes < need);
+    if (st != ATTN_OK) return st;
+    if ((int64_t)p.total_k * ns > INT32_MAX) return ATTN_ERR_SHAPE;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o;
+    p.dout = (const uint16_t*)dout;
+    p.lse = lse;
+    p.dq = (uint16_t*)dq;
+    p.dk = (uint16_t*)dk;
+    p.dv = (uint16_t*)dv;
+    p.delta = delta;
+    p.n_split = ns;
+    p.ws = (float*)workspace;
+    p.total_k *= ns;
+    // dQ (writes delta), dK/dV parts (read delta, write the workspace), then
+    // the sum of the parts: one stream, in this order
+    const hipStream_t s = (hipStream_t)stream;
+    launch_dq(p, causal != 0, s);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+    launch_dkdv(p, causal != 0, s);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+    launch_reduce(p, s);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -204,6 +204,62 @@ def test_bwd_split_calls_without_gpu_report_device(lib):
     assert call_dq() == 9 and call_dkdv() == 9
 
 
+def test_bwd_splits_and_workspace_bytes(lib):
+    # MQA, B = 8, N = 2048: 128 dK/dV workgroups -> 2 parts reach 256
+    assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 128) == 2
+    assert sdpa.attn_bwd_workspace_bytes(8, 16, 1, 2048, 128) == 2 * 2 * 8 * 2048 * 128 * 4
+    # the grid already has 256 workgroups: no split, no workspace
+    assert sdpa.attn_bwd_splits(8, 16, 2, 2048, 128) == 1
+    assert sdpa.attn_bwd_workspace_bytes(8, 16, 2, 2048, 128) == 0
+    assert sdpa.attn_bwd_splits(2, 16, 16, 16384, 128) == 1
+    # tiny grid: the largest divisor of the group up to 16
+    assert sdpa.attn_bwd_splits(1, 16, 1, 512, 128) == 16
+    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128) == 12
+    assert sdpa.attn_bwd_splits(1, 4, 2, 256, 128) == 2
+    # requested: the largest divisor of the group not above the request
+    assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 128, 3) == 2
+    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, 5) == 4
+    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, 1) == 1
+    assert sdpa.attn_bwd_workspace_bytes(1, 12, 1, 512, 128, 5) == 4 * 2 * 512 * 128 * 4
+    # invalid arguments -> 0
+    assert sdpa.attn_bwd_splits(8, 15, 2, 2048, 128) == 0
+    assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 64) == 0
+    assert sdpa.attn_bwd_splits(0, 16, 1, 2048, 128) == 0
+    assert sdpa.attn_bwd_workspace_bytes(8, 16, 1, 0, 128) == 0
+
+
+# attn_bwd_ws on a shape that splits (MQA, 4 query heads, 2 parts requested)
+BWS = dict(BW, H_q=4, H_kv=1, n_splits=2, ws=0x1400000000, ws_bytes=1 << 30)
+
+
+def call_bwd_ws(**kw):
+    a = dict(BWS)
+    a.update(kw)
+    return sdpa.attn_bwd_ws(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                            a["dv"], a["delta"], a["B"], a["H_q"], a["H_kv"], a["N"], a["D"],
+                            a["causal"], a["scale"], a["n_splits"], a["ws"], a["ws_bytes"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), 1), (dict(q=None), 1), (dict(N=0), 2), (dict(H_q=5, H_kv=2), 3), (dict(D=64), 4),
+    (dict(scale=float("nan")), 5), (dict(ws=0x1400000008), 6),
+    (dict(ws=0x100000), 7), (dict(ws=0x1200000000), 7), (dict(dk=0x1400000000 + 4096), 7),
+    (dict(ws_bytes=2 * 2 * 64 * 128 * 4 - 16), 10), (dict(ws_bytes=0), 10),
+])
+def test_bwd_ws_argument_errors(lib, kw, code):
+    assert call_bwd_ws(**kw) == code
+
+
+def test_bwd_ws_valid_arguments_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake pointers")
+    assert call_bwd_ws() == 9
+    assert call_bwd_ws(ws_bytes=2 * 2 * 64 * 128 * 4) == 9      # exactly enough
+    assert call_bwd_ws(n_splits=1, ws=None, ws_bytes=0) == 9     # one part: attn_bwd, no workspace
+
+
 # attn_decode / attn_lse_merge (fake, far-apart addresses; validation only)
 DC = dict(q=0x100000, k=0x200000000, v=0x400000000, o=0x600000000, lse=0x800000000, B=8,
           H_q=16, H_kv=2, M=1, L=32768, D=128, causal=0, scale=1 / math.sqrt(128), n_splits=0,

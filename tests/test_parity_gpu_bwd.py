@@ -49,8 +49,9 @@ def inputs(B, Hq, Hkv, N, seed):
     return q, k, v, do
 
 
-def run_bwd(q, k, v, do, causal, scale, o=None, lse=None):
-    """HIP forward (unless o, lse are given) then HIP backward; numpy results."""
+def run_bwd(q, k, v, do, causal, scale, o=None, lse=None, n_splits=0, workspace=None):
+    """HIP forward (unless o, lse are given) then HIP backward (n_splits: parts of
+    the dK/dV step, <= 0 the library's choice); numpy results."""
     import torch
     import scaled_dot_product_17_amd as sdpa
     qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
@@ -58,7 +59,8 @@ def run_bwd(q, k, v, do, causal, scale, o=None, lse=None):
         og, lg = sdpa.fwd(qg, kg, vg, causal=causal, scale=scale)
     else:
         og, lg = to_gpu(o), torch.from_numpy(np.ascontiguousarray(lse, np.float32)).cuda()
-    dq, dk, dv, delta = sdpa.bwd(qg, kg, vg, og, lg, dog, causal=causal, scale=scale)
+    dq, dk, dv, delta = sdpa.bwd(qg, kg, vg, og, lg, dog, causal=causal, scale=scale,
+                                 n_splits=n_splits, workspace=workspace)
     torch.cuda.synchronize()
     return {"dq": bf16_to_np(dq), "dk": bf16_to_np(dk), "dv": bf16_to_np(dv),
             "delta": delta.cpu().numpy()}
@@ -77,15 +79,45 @@ SMALL = [(1, 2, 2, 256), (2, 4, 2, 1), (1, 2, 1, 17), (1, 3, 3, 64), (1, 2, 2, 6
          (1, 4, 4, 1536)]
 
 
+@pytest.mark.parametrize("splits", [0, 1], ids=["auto_parts", "one_part"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "b%d_hq%d_hkv%d_n%d" % s)
-def test_bwd_small_full(shape, causal):
+def test_bwd_small_full(shape, causal, splits):
+    """Both dK/dV forms: the library's choice (these small grids split every
+    group of more than one query head) and one part (attn_bwd)."""
     B, Hq, Hkv, N = shape
-    say(f"[bwd small] {shape} causal={causal}")
+    say(f"[bwd small] {shape} causal={causal} n_splits={splits}")
     q, k, v, do = inputs(B, Hq, Hkv, N, seed=11000 + N)
-    res = run_bwd(q, k, v, do, causal, SCALE)
+    res = run_bwd(q, k, v, do, causal, SCALE, n_splits=splits)
     ref = oracle.attn_bwd_ref(q, k, v, do, causal, SCALE, mags=True)
-    check_all(res, ref, f"{shape} causal={causal}")
+    check_all(res, ref, f"{shape} causal={causal} n_splits={splits}")
+
+
+def test_bwd_split_parts():
+    """attn_bwd_ws with 2, 4 and 8 parts of a 16-head group (GQA 16:2, ragged
+    N): every part count meets the bound, dQ and delta equal the one-part
+    result bitwise (the dQ kernel does not change), each part count is
+    reproducible bitwise, and the workspace's old contents do not matter."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = 1, 16, 2, 1000
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=13100)
+    for causal in (False, True):
+        ref = oracle.attn_bwd_ref(q, k, v, do, causal, SCALE, mags=True)
+        one = run_bwd(q, k, v, do, causal, SCALE, n_splits=1)
+        for ns in (2, 4, 8):
+            assert sdpa.attn_bwd_splits(B, Hq, Hkv, N, 128, ns) == ns
+            need = sdpa.attn_bwd_workspace_bytes(B, Hq, Hkv, N, 128, ns)
+            assert need == ns * 2 * B * Hkv * N * 128 * 4
+            ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
+            say(f"[bwd parts] causal={causal} n_splits={ns}")
+            a = run_bwd(q, k, v, do, causal, SCALE, n_splits=ns, workspace=ws)
+            b = run_bwd(q, k, v, do, causal, SCALE, n_splits=ns)
+            check_all(a, ref, f"causal={causal} n_splits={ns}")
+            for name in a:
+                assert np.array_equal(a[name], b[name]), f"{name} differs between runs"
+            for name in ("dq", "delta"):
+                assert np.array_equal(a[name], one[name]), f"{name} depends on the dK/dV parts"
 
 
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.5])
@@ -210,7 +242,8 @@ def test_bwd_split_calls_match():
     qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
     for causal in (False, True):
         o, lse = sdpa.fwd(qg, kg, vg, causal=causal, scale=SCALE)
-        dq, dk, dv, delta = sdpa.bwd(qg, kg, vg, o, lse, dog, causal=causal, scale=SCALE)
+        dq, dk, dv, delta = sdpa.bwd(qg, kg, vg, o, lse, dog, causal=causal, scale=SCALE,
+                                     n_splits=1)
         dq2, dk2, dv2 = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
         delta2 = torch.empty_like(lse)
         sp = torch.cuda.current_stream().cuda_stream
@@ -242,3 +275,8 @@ def test_bwd_errors_reported():
     with pytest.raises(sdpa.AttnError) as e:
         sdpa.bwd(bad, kg[..., :64].contiguous(), vg[..., :64].contiguous(), bad, lse, bad)
     assert e.value.status == 4
+    # a split call with too small a workspace (2 parts of the 4:2 group)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sdpa.AttnError) as e:
+        sdpa.bwd(qg, kg, vg, o, lse, dog, n_splits=2, workspace=small)
+    assert e.value.status == 10
