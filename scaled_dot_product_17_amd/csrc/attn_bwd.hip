@@ -33,6 +33,10 @@
 //     one tile later wave B computes dP = dO V^T, dS = P (dP - delta) and
 //     dK^T += Q^T dS.  dO^T and Q^T are read with the transposing LDS read.
 //     The two waves of a pair share a SIMD, so A's softmax overlaps B's MFMAs.
+//   * attn_bwd_ws may split each group's query heads into parts in the dK/dV
+//     step, so that few K/V heads still give one workgroup per CU: each part
+//     writes fp32 dV and dK sums to a workspace and attn_bwd_reduce_kernel adds
+//     the parts in part order (still reproducible bitwise) and rounds to bf16.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -359,9 +363,9 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
     const int hh = lane >> 5;
 
     // with a causal mask the first key tiles of a head see the most rows, and
-    // they come first in this order
-    // with n_split parts, part sp covers query heads [sp*gh, (sp+1)*gh) of the
-    // group; the key tiles of one (batch, K/V head, part) stay consecutive
+    // they come first in this order.  With n_split parts, part sp covers query
+    // heads [sp*gh, (sp+1)*gh) of the group, and the key tiles of one (batch,
+    // K/V head, part) stay consecutive.
     const int ns = p.n_split > 1 ? p.n_split : 1;
     const int logical = xcd_remap(blockIdx.x, p.total_k);
     const int bks = logical / p.n_ktiles;

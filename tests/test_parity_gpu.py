@@ -81,6 +81,22 @@ def test_workload_sampled(name):
     parity.check(m, name)
 
 
+@pytest.mark.parametrize("shape", [(1, 5, 5, 3000), (3, 5, 1, 1000)],
+                         ids=lambda s: "b%d_hq%d_hkv%d_n%d" % s)
+def test_causal_head_groups_full(shape):
+    """Causal grids interleave the tiles of groups of heads (enough tiles to fill
+    one XCD's workgroup slots: 3 heads of 24 tiles, 8 heads of 8 tiles here),
+    and the last group is short (2 and 7 heads).  Every row of every head must
+    still be computed once and match the oracle."""
+    B, Hq, Hkv, N = shape
+    say(f"[causal groups] {shape}")
+    q, k, v = inputs(B, Hq, Hkv, N, seed=7500 + N)
+    o, lse = run(q, k, v, True, SCALE)
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, True, SCALE)
+    m = parity.compare(o, lse, o_ref, lse_ref)
+    parity.check(m, f"{shape} causal")
+
+
 def test_deterministic():
     q, k, v = inputs(2, 8, 2, 2048, seed=9100)
     for causal in (False, True):

@@ -96,6 +96,20 @@ def test_fp8_small_full(shape, causal):
     check_rows(o, lse, q8, k8, v8, d, d, d, causal, SCALE, what=f"{shape} causal={causal}")
 
 
+def test_fp8_causal_head_groups_full():
+    """Causal FP8 grids interleave the tiles of groups of heads (8 heads of 8
+    tiles here) and the last group is short (7 heads): every row of every head
+    must still be computed once and meet the bound."""
+    B, Hq, Hkv, N = 3, 5, 1, 1000
+    say(f"[fp8 causal groups] {(B, Hq, Hkv, N)}")
+    q8 = codes(15500, (B, Hq, N, 128))
+    k8 = codes(15501, (B, Hkv, N, 128))
+    v8 = codes(15502, (B, Hkv, N, 128))
+    d = synth.FP8_DESCALE
+    o, lse = run_fp8(q8, k8, v8, d, d, d, True, SCALE)
+    check_rows(o, lse, q8, k8, v8, d, d, d, True, SCALE, what="causal head groups")
+
+
 @pytest.mark.parametrize("scale,dq,dk,dv", [
     (SCALE, 0.0137, 0.0291, 0.77), (-0.0625, 0.02, 0.02, 1.0), (0.0, 0.02, 0.02, 0.5),
     (SCALE, 0.013, 0.014, -2.5), (0.5, 0.013, 0.013, 0.013)])
