@@ -360,7 +360,7 @@ def main_bwd(args, w):
             f"{'dkdv(1) ms':>10s}")
         for name, x in synth.WORKLOADS.items():
             tt = time_bwd(x, max(5, args.steps // 5), 3)
-            parts = sdpa.attn_bwd_splits(x.B, x.H_q, x.H_kv, x.N, x.D, 0)
+            parts = sdpa.attn_bwd_splits(x.B, x.H_q, x.H_kv, x.N, x.D, x.causal)
             tf = 10 * x.D * bwd_pairs(x) / (tt["ms_step"] * 1e-3) / 1e12
             log(f"{name:36s} {tt['ms_step']:9.3f} {tf:9.1f} {100 * tf / PEAK_TFLOPS:7.1f} "
                 f"{parts:5d} {tt['dq']:8.3f} {tt['dkdv']:10.3f}")

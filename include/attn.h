@@ -258,14 +258,14 @@ attn_status attn_bwd_ws(const void* q, const void* k, const void* v, const void*
 
 /* attn_bwd_splits: the parts attn_bwd_ws uses for these arguments (n_splits <=
  * 0: the library's choice, the smallest divisor of H_q / H_kv that gives at
- * least 256 dK/dV workgroups, at most 16), or 0 if they are invalid.
- * Host-only arithmetic. */
-int attn_bwd_splits(int B, int H_q, int H_kv, int N, int D, int n_splits);
+ * least 256 dK/dV workgroups, causal: 1024, or 2048 from N = 8192, at most
+ * 16), or 0 if they are invalid.  Host-only arithmetic. */
+int attn_bwd_splits(int B, int H_q, int H_kv, int N, int D, int causal, int n_splits);
 
 /* attn_bwd_workspace_bytes: bytes of workspace attn_bwd_ws needs for these
  * arguments: 2 * parts * B * H_kv * N * D * 4 when it splits, else 0 (also 0 if
  * they are invalid).  Host-only arithmetic. */
-size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int n_splits);
+size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int causal, int n_splits);
 
 /*
  * attn_decode: enqueue split-KV decode attention on `stream`.

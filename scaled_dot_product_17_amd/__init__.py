@@ -66,9 +66,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_bwd_ws.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
             lib.attn_bwd_splits.restype = ctypes.c_int
-            lib.attn_bwd_splits.argtypes = [ctypes.c_int] * 6
+            lib.attn_bwd_splits.argtypes = [ctypes.c_int] * 7
             lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
-            lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 6
+            lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 7
             lib.attn_fwd_varlen.restype = ctypes.c_int
             lib.attn_fwd_varlen.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 9 + [
                 ctypes.c_float, ctypes.c_void_p]
@@ -213,12 +213,14 @@ def attn_bwd_ws(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H_q, H_kv, N, D, ca
                               workspace, int(workspace_bytes), stream)
 
 
-def attn_bwd_splits(B, H_q, H_kv, N, D, n_splits=0) -> int:
-    return load().attn_bwd_splits(int(B), int(H_q), int(H_kv), int(N), int(D), int(n_splits))
+def attn_bwd_splits(B, H_q, H_kv, N, D, causal=False, n_splits=0) -> int:
+    return load().attn_bwd_splits(int(B), int(H_q), int(H_kv), int(N), int(D), int(bool(causal)),
+                                  int(n_splits))
 
 
-def attn_bwd_workspace_bytes(B, H_q, H_kv, N, D, n_splits=0) -> int:
-    return load().attn_bwd_workspace_bytes(int(B), int(H_q), int(H_kv), int(N), int(D), int(n_splits))
+def attn_bwd_workspace_bytes(B, H_q, H_kv, N, D, causal=False, n_splits=0) -> int:
+    return load().attn_bwd_workspace_bytes(int(B), int(H_q), int(H_kv), int(N), int(D),
+                                           int(bool(causal)), int(n_splits))
 
 
 def attn_bwd_flops(B, H_q, N, D, causal) -> float:
@@ -372,14 +374,14 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     elif delta.dtype != torch.float32 or tuple(delta.shape) != (B, Hq, N) or \
             not delta.is_contiguous() or delta.device != q.device:
         raise ValueError("delta must be a contiguous fp32 [B, H_q, N] tensor on q's device")
-    ns = attn_bwd_splits(B, Hq, Hkv, N, D, n_splits)
+    ns = attn_bwd_splits(B, Hq, Hkv, N, D, causal, n_splits)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                 B, Hq, Hkv, N, D, causal, scale)
         if ns > 1:
-            need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, D, ns)
+            need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, D, causal, ns)
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             elif not isinstance(workspace, torch.Tensor) or workspace.device != q.device or \

@@ -708,11 +708,15 @@ void launch_reduce(const BwdParams& p, hipStream_t s) {
 // Parts of each group's query heads for the dK/dV step of attn_bwd_ws: a
 // divisor of the group size.  n_splits <= 0: the smallest divisor that gives
 // at least one dK/dV workgroup per compute unit of an MI355X (256; one
-// workgroup fits per CU), or the largest divisor up to 16 when none does.
-// n_splits > 0: the largest divisor of the group size not above n_splits.
-int bwd_splits(int B, int H_q, int H_kv, int N, int n_splits) {
+// workgroup fits per CU), or four per CU when causal and eight from 8192 keys
+// (a causal key tile's work falls with its index; smaller parts let the
+// heaviest-first order even it out, and long sequences have the heaviest
+// tiles), or the largest divisor up to 16 when none does.  n_splits > 0: the
+// largest divisor of the group size not above n_splits.
+int bwd_splits(int B, int H_q, int H_kv, int N, bool causal, int n_splits) {
     const int group = H_q / H_kv;
     const int64_t base = (int64_t)B * H_kv * (((int64_t)N + KV_KEYS - 1) / KV_KEYS);
+    const int64_t target = causal ? (N >= 8192 ? 8 : 4) * 256 : 256;
     int best = 1;
     for (int s = 1; s <= std::min(group, 16); ++s) {
         if (group % s != 0) continue;
@@ -721,7 +725,7 @@ int bwd_splits(int B, int H_q, int H_kv, int N, int n_splits) {
             continue;
         }
         best = s;
-        if (base * s >= 256) break;
+        if (base * s >= target) break;
     }
     return best;
 }
@@ -811,13 +815,14 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-extern "C" int attn_bwd_splits(int B, int H_q, int H_kv, int N, int D, int n_splits) {
-    return bwd_shape_ok(B, H_q, H_kv, N, D) ? bwd_splits(B, H_q, H_kv, N, n_splits) : 0;
+extern "C" int attn_bwd_splits(int B, int H_q, int H_kv, int N, int D, int causal, int n_splits) {
+    return bwd_shape_ok(B, H_q, H_kv, N, D) ? bwd_splits(B, H_q, H_kv, N, causal != 0, n_splits) : 0;
 }
 
-extern "C" size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int n_splits) {
+extern "C" size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int causal,
+                                           int n_splits) {
     if (!bwd_shape_ok(B, H_q, H_kv, N, D)) return 0;
-    return bwd_ws_bytes(B, H_kv, N, bwd_splits(B, H_q, H_kv, N, n_splits));
+    return bwd_ws_bytes(B, H_kv, N, bwd_splits(B, H_q, H_kv, N, causal != 0, n_splits));
 }
 
 extern "C" attn_status attn_bwd_ws(const void* q, const void* k, const void* v, const void* o,
@@ -825,7 +830,7 @@ extern "C" attn_status attn_bwd_ws(const void* q, const void* k, const void* v, 
                                    float* delta, int B, int H_q, int H_kv, int N, int D, int causal,
                                    float scale, int n_splits, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    const int ns = bwd_shape_ok(B, H_q, H_kv, N, D) ? bwd_splits(B, H_q, H_kv, N, n_splits) : 1;
+    const int ns = bwd_shape_ok(B, H_q, H_kv, N, D) ? bwd_splits(B, H_q, H_kv, N, causal != 0, n_splits) : 1;
     if (ns == 1)
         return attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H_q, H_kv, N, D, causal, scale,
                         stream);

@@ -216,11 +216,21 @@ def test_bwd_splits_and_workspace_bytes(lib):
     assert sdpa.attn_bwd_splits(1, 16, 1, 512, 128) == 16
     assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128) == 12
     assert sdpa.attn_bwd_splits(1, 4, 2, 256, 128) == 2
+    # causal: four workgroups per CU, eight from N = 8192 (a causal key tile's
+    # work falls with its index)
+    assert sdpa.attn_bwd_splits(1, 16, 1, 32768, 128) == 1
+    assert sdpa.attn_bwd_splits(1, 16, 1, 32768, 128, causal=True) == 8
+    assert sdpa.attn_bwd_splits(2, 16, 2, 8192, 128, causal=True) == 8
+    assert sdpa.attn_bwd_splits(8, 16, 2, 2048, 128, causal=True) == 4
+    assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 128, causal=True) == 8
+    assert sdpa.attn_bwd_splits(2, 16, 16, 16384, 128, causal=True) == 1
+    assert sdpa.attn_bwd_workspace_bytes(1, 16, 1, 32768, 128, True) == 8 * 2 * 32768 * 128 * 4
     # requested: the largest divisor of the group not above the request
-    assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 128, 3) == 2
-    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, 5) == 4
-    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, 1) == 1
-    assert sdpa.attn_bwd_workspace_bytes(1, 12, 1, 512, 128, 5) == 4 * 2 * 512 * 128 * 4
+    assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 128, n_splits=3) == 2
+    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, n_splits=5) == 4
+    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, True, 5) == 4
+    assert sdpa.attn_bwd_splits(1, 12, 1, 512, 128, n_splits=1) == 1
+    assert sdpa.attn_bwd_workspace_bytes(1, 12, 1, 512, 128, n_splits=5) == 4 * 2 * 512 * 128 * 4
     # invalid arguments -> 0
     assert sdpa.attn_bwd_splits(8, 15, 2, 2048, 128) == 0
     assert sdpa.attn_bwd_splits(8, 16, 1, 2048, 64) == 0

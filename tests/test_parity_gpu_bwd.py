@@ -106,8 +106,8 @@ def test_bwd_split_parts():
         ref = oracle.attn_bwd_ref(q, k, v, do, causal, SCALE, mags=True)
         one = run_bwd(q, k, v, do, causal, SCALE, n_splits=1)
         for ns in (2, 4, 8):
-            assert sdpa.attn_bwd_splits(B, Hq, Hkv, N, 128, ns) == ns
-            need = sdpa.attn_bwd_workspace_bytes(B, Hq, Hkv, N, 128, ns)
+            assert sdpa.attn_bwd_splits(B, Hq, Hkv, N, 128, causal, ns) == ns
+            need = sdpa.attn_bwd_workspace_bytes(B, Hq, Hkv, N, 128, causal, ns)
             assert need == ns * 2 * B * Hkv * N * 128 * 4
             ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
             say(f"[bwd parts] causal={causal} n_splits={ns}")
