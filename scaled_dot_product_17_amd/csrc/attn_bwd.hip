@@ -92,6 +92,7 @@ struct BwdParams {
     int B, Hq, Hkv, N;
     int group;              // Hq / Hkv
     int n_qtiles, total_q;  // attn_bwd_dq grid: B * Hq * ceil(N / 256)
+    int cgroup;             // attn_bwd_dq, causal: heads whose tiles are interleaved
     int n_ktiles, total_k;  // attn_bwd_dkdv grid: B * Hkv * ceil(N / 128) * n_split
     int n_split;            // dK/dV: parts of each group's query heads (1: write dk, dv)
     float* ws;              // n_split > 1: fp32 partials [n_split][dV, dK][B * Hkv * N][D]
@@ -187,10 +188,24 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p)
     const int l32 = lane & 31;   // query column owned by this lane
     const int hh = lane >> 5;
 
+    // causal: groups of cgroup heads one after another (a group's tiles share K
+    // and V in one XCD's L2), tile-major and heaviest tile first within a group;
+    // a group holds at least an XCD's worth of workgroup slots, so light tiles
+    // of one group, not heavy tiles of the next, end each XCD's share
     const int logical = xcd_remap(blockIdx.x, p.total_q);
-    const int bh = logical / p.n_qtiles;
-    int qt = logical % p.n_qtiles;
-    if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
+    int bh, qt;
+    if (CAUSAL) {
+        const int per = p.B * p.Hq;
+        const int G = p.cgroup > 1 ? p.cgroup : 1;
+        const int grp = logical / (G * p.n_qtiles);
+        const int r = logical - grp * G * p.n_qtiles;
+        const int gh = min(G, per - grp * G);
+        qt = p.n_qtiles - 1 - r / gh;
+        bh = grp * G + r % gh;
+    } else {
+        bh = logical / p.n_qtiles;
+        qt = logical % p.n_qtiles;
+    }
     const int b = bh / p.Hq;
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
@@ -674,6 +689,8 @@ attn_status prepare(const Buf* ins, int n_in, const Buf* outs, int n_out, int B,
     p.group = H_q / H_kv;
     p.n_qtiles = (int)n_qtiles;
     p.total_q = (int)total_q;
+    // one 8-wave dQ workgroup per CU: 32 slots per XCD
+    p.cgroup = (int)std::min<int64_t>((int64_t)B * H_q, (32 + n_qtiles - 1) / n_qtiles);
     p.n_ktiles = (int)n_ktiles;
     p.total_k = (int)total_k;
     p.c = (float)((double)scale * 1.4426950408889634);
