@@ -93,6 +93,7 @@ struct BwdParams {
     int group;              // Hq / Hkv
     int n_qtiles, total_q;  // attn_bwd_dq grid: B * Hq * ceil(N / 256)
     int cgroup;             // attn_bwd_dq, causal: heads whose tiles are interleaved
+    int kgroup;             // attn_bwd_dkdv, causal: (batch, K/V head, part)s interleaved
     int n_ktiles, total_k;  // attn_bwd_dkdv grid: B * Hkv * ceil(N / 128) * n_split
     int n_split;            // dK/dV: parts of each group's query heads (1: write dk, dv)
     float* ws;              // n_split > 1: fp32 partials [n_split][dV, dK][B * Hkv * N][D]
@@ -381,10 +382,24 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
     // they come first in this order.  With n_split parts, part sp covers query
     // heads [sp*gh, (sp+1)*gh) of the group, and the key tiles of one (batch,
     // K/V head, part) stay consecutive.
+    // Causal grids interleave the key tiles of kgroup such units (enough tiles
+    // for one XCD's workgroup slots), tile by tile, so light tiles of one group,
+    // not heavy tiles of the next, end each XCD's share.
     const int ns = p.n_split > 1 ? p.n_split : 1;
     const int logical = xcd_remap(blockIdx.x, p.total_k);
-    const int bks = logical / p.n_ktiles;
-    const int kt = logical % p.n_ktiles;
+    int bks, kt;
+    if (CAUSAL) {
+        const int per = p.B * p.Hkv * ns;
+        const int G = p.kgroup > 1 ? p.kgroup : 1;
+        const int grp = logical / (G * p.n_ktiles);
+        const int r = logical - grp * G * p.n_ktiles;
+        const int gu = min(G, per - grp * G);
+        kt = r / gu;
+        bks = grp * G + r % gu;
+    } else {
+        bks = logical / p.n_ktiles;
+        kt = logical % p.n_ktiles;
+    }
     const int bk = bks / ns;
     const int sp = bks % ns;
     const int gh = p.group / ns;
@@ -689,8 +704,9 @@ attn_status prepare(const Buf* ins, int n_in, const Buf* outs, int n_out, int B,
     p.group = H_q / H_kv;
     p.n_qtiles = (int)n_qtiles;
     p.total_q = (int)total_q;
-    // one 8-wave dQ workgroup per CU: 32 slots per XCD
+    // one 8-wave dQ or dK/dV workgroup per CU: 32 slots per XCD
     p.cgroup = (int)std::min<int64_t>((int64_t)B * H_q, (32 + n_qtiles - 1) / n_qtiles);
+    p.kgroup = (int)std::min<int64_t>((int64_t)B * H_kv, (32 + n_ktiles - 1) / n_ktiles);
     p.n_ktiles = (int)n_ktiles;
     p.total_k = (int)total_k;
     p.c = (float)((double)scale * 1.4426950408889634);
@@ -875,6 +891,7 @@ extern "C" attn_status attn_bwd_ws(const void* q, const void* k, const void* v, 
     p.n_split = ns;
     p.ws = (float*)workspace;
     p.total_k *= ns;
+    p.kgroup = (int)std::min<int64_t>((int64_t)B * H_kv * ns, (32 + p.n_ktiles - 1) / p.n_ktiles);
     // dQ (writes delta), dK/dV parts (read delta, write the workspace), then
     // the sum of the parts: one stream, in this order
     const hipStream_t s = (hipStream_t)stream;
