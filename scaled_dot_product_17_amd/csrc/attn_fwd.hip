@@ -94,6 +94,7 @@ struct Params {
     // packed variable-length batch (VARLEN kernels only): B = 1 and N = tokens
     const int* cu;    // n_seq + 1 token offsets
     int n_seq;
+    int lpt;          // several sequences of unequal lengths: tile-major order
     int left, right;  // window: row i sees keys i-left .. i+right (< 0: unbounded)
     // block-sparse mask (SPARSE kernels only): lists of SP_BLOCK-key blocks per
     // (mask head, SP_BLOCK-row query block), block-compressed-row form
@@ -197,11 +198,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     // batch index is the sequence of a packed batch (B = 1, N = all tokens).
     const int logical = xcd_remap(blockIdx.x, p.total);
     int bh, qt;
-    if (VARLEN && p.n_seq > 1) {
-        // several sequences: tile-major, largest tile index first.  Tiles far
-        // into a sequence exist only for long sequences and carry the most keys
-        // (causal, windowed or not), so the heaviest work starts first and short
-        // tiles fill the tail (longest-processing-time-first order).
+    if (VARLEN && p.n_seq > 1 && p.lpt) {
+        // several sequences of unequal lengths: tile-major, largest tile index
+        // first.  Tiles far into a sequence exist only for long sequences and
+        // carry the most keys (causal, windowed or not), so the heaviest work
+        // starts first and short tiles fill the tail (longest-processing-time-
+        // first order).
         const int per = p.B * p.Hq;
         qt = p.n_qtiles - 1 - logical / per;
         bh = logical % per;
@@ -799,6 +801,12 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.total = (int)grid;
     p.cu = cu_seqlens;
     p.n_seq = n_seq;
+    // Sequences of nearly equal length (the longest within 1.25x the mean)
+    // take the dense order: a few heads at a time, whose K/V stays in one
+    // XCD's L2 (grouped as for dense causal grids).  Unequal lengths take the
+    // tile-major longest-first order, which balances them.
+    p.lpt = n_seq > 1 && (int64_t)max_seqlen * n_seq * 4 > (int64_t)total * 5;
+    p.cgroup = (int)std::min<int64_t>((int64_t)n_seq * H_q, (64 + n_qtiles - 1) / n_qtiles);
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;
     set_scale(p, scale);

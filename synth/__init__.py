@@ -520,4 +520,7 @@ VARLEN_WORKLOADS = {w.name: w for w in [
     # one 32768-token sequence, 16 heads, a symmetric local window of 1024 tokens
     VarlenWorkload("local1024_h16_t32768", 16, 16, 32768, 32768, 32768, causal=False, left=1024,
                    right=1024, seed_base=7020),
+    # eight sequences of exactly 4096 tokens, 16 heads, causal: the packed form of
+    # dense causal B = 8, N = 4096
+    VarlenWorkload("varlen_causal_equal_h16_8x4096", 16, 16, 32768, 4096, 4096, seed_base=7030),
 ]}

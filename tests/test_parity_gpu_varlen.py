@@ -157,6 +157,37 @@ def test_varlen_workload_sequences(name):
         parity.check(m, f"{name} sequence {s}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_lengths_match_dense(causal):
+    """A packed batch of sequences of one length (the longest within 1.25x the
+    mean: the dense grid order, a few heads at a time) equals the dense kernel
+    on the same batch bitwise, every row of every head: each row's arithmetic
+    is the same, and a tile the order skipped or repeated would show."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    S, L, Hq, Hkv = 6, 640, 4, 2
+    q, k, v, cu = packed(14600, Hq, Hkv, [L] * S)
+    o, lse = run_varlen(q, k, v, cu, causal, SCALE, (-1, -1))
+    dense = lambda a, h: to_gpu(a).view(h, S, L, 128).transpose(0, 1).contiguous()
+    od, ld = sdpa.fwd(dense(q, Hq), dense(k, Hkv), dense(v, Hkv), causal=causal, scale=SCALE)
+    torch.cuda.synchronize()
+    od = bf16_to_np(od).transpose(1, 0, 2, 3).reshape(Hq, S * L, 128)
+    ld = ld.cpu().numpy().transpose(1, 0, 2).reshape(Hq, S * L)
+    assert np.array_equal(o, od) and np.array_equal(lse, ld), "packed != dense"
+
+
+def test_nearly_equal_lengths_full():
+    """Lengths within 1.25x of the mean (dense grid order) with ragged tails and
+    GQA, both masks: every row against the oracle."""
+    q, k, v, cu = packed(14700, 8, 2, [500, 512, 480, 512, 431])
+    for causal in (False, True):
+        o, lse = run_varlen(q, k, v, cu, causal, SCALE, (-1, -1))
+        o_ref, lse_ref = oracle.attn_varlen_ref(q, k, v, cu, causal, SCALE, -1, -1)
+        m = parity.compare(o, lse, o_ref, lse_ref)
+        say(f"  nearly equal lengths causal={causal}: {m}")
+        parity.check(m, f"nearly equal lengths causal={causal}")
+
+
 @pytest.mark.parametrize("causal,n", [(False, 8192), (True, 9000), (False, 5000)])
 def test_four_and_eight_wave_workgroups_agree(causal, n):
     """A single sequence through the packed entry point (4-wave workgroups) equals
