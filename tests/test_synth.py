@@ -60,6 +60,22 @@ def test_workload_catalogue():
     assert len(set(seeds)) == len(seeds)
 
 
+def test_varlen_catalogue():
+    """Packed workloads: lengths in range and summing to the token count, distinct
+    seeds; the equal-length batch has dense causal B = 8, N = 4096's pair count."""
+    seeds = []
+    for w in synth.VARLEN_WORKLOADS.values():
+        L = w.lengths()
+        assert int(L.sum()) == w.total and L.min() >= 1 and L.max() <= w.max_len
+        assert (L[:-1] >= w.min_len).all()      # only the last may be cut short
+        assert w.cu_seqlens()[-1] == w.total and w.H_q % w.H_kv == 0
+        seeds += [w.seed_base, w.seed_base + 3]
+    assert len(set(seeds)) == len(seeds)
+    eq = synth.VARLEN_WORKLOADS["varlen_causal_equal_h16_8x4096"]
+    assert list(eq.lengths()) == [4096] * 8
+    assert eq.pairs == 16 * 8 * 4096 * 4097 // 2
+
+
 def test_e4m3_encoder_matches_torch_and_ties_to_even():
     """f64_to_e4m3 against torch's float8_e4m3fn cast on a dense grid (in range),
     exact midpoints (ties to the even code) and saturation at 448."""
