@@ -398,9 +398,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     }
 
     // ---- prologue: K blocks 0-2 and V block 0 in flight, then Q into VGPRs
-    if (VARLEN || SPARSE || N % KB != 0) {
-        // rows past N of the tail block must read as zeros, not stale LDS (and the
-        // union build's scratch must be gone before the first block arrives)
+    if (VARLEN || (SPARSE && N % SP_BLOCK != 0) || N % KB != 0) {
+        // rows past N of the tail block must read as zeros, not stale LDS.  A
+        // block-sparse part past N is not copied at all, which happens only when
+        // N is not a multiple of SP_BLOCK; the union build's scratch lies in K
+        // slot 0, which block 0's copy overwrites before any read.
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < LDS_BYTES / (16 * NTH); ++i)
