@@ -169,3 +169,49 @@ def test_blocksparse_workload_sampled(name):
     m = parity.compare(o.reshape(-1, 128)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
     say(f"  {name}: {m}")
     parity.check(m, name)
+
+
+def _poison_lds():
+    """Dense forwards over NaN K and V, with enough workgroups to cover every CU
+    at both workgroup sizes, leave NaN bf16 rows in the LDS that the next
+    launch's workgroups inherit (LDS is not cleared between launches)."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    for n in (8192, 4096):          # 8-wave and 4-wave workgroups, 512 of each
+        q = torch.randn(1, 16, n, 128, device="cuda").to(torch.bfloat16)
+        kv = torch.full((1, 16, n, 128), float("nan"), device="cuda", dtype=torch.bfloat16)
+        sdpa.fwd(q, kv, kv)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_stale_lds_is_never_read(causal):
+    """Launches whose LDS rings are not cleared first (block-sparse with N a
+    multiple of 128, dense with N a multiple of 32) read only ring slots their
+    own copies filled: after the LDS has been filled with NaN rows by other
+    launches, they reproduce their results bitwise."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = 2, 8, 2, 1024
+    nb = N // BLK
+    q, k, v = inputs(17800, B, Hq, Hkv, N)
+    lists = random_lists(17803, nb, nb)
+    lists[1] = []                                   # a query block with no key
+    lists[2] = [nb - 1]                              # only the last block (causal: nothing)
+    ptr, idx = synth.lists_to_csr(lists)
+    qg, kg, vg = to_gpu(q), to_gpu(k), to_gpu(v)
+
+    def both():
+        o1, l1 = sdpa.fwd_blocksparse(qg, kg, vg, i32_gpu(ptr), i32_gpu(idx), causal=causal, scale=SCALE)
+        o2, l2 = sdpa.fwd(qg, kg, vg, causal=causal, scale=SCALE)
+        torch.cuda.synchronize()
+        return [bf16_to_np(o1), l1.cpu().numpy(), bf16_to_np(o2), l2.cpu().numpy()]
+
+    first = both()
+    _poison_lds()
+    after = both()
+    for a, b in zip(first, after):
+        assert np.array_equal(a, b, equal_nan=True)
+    assert np.all(np.isfinite(after[0])) and np.all(np.isfinite(after[2]))
+    o_ref, lse_ref = oracle.attn_blocksparse_ref(q, k, v, ptr, idx, BLK, causal, SCALE)
+    check(after[0], after[1], o_ref, lse_ref, f"block-sparse after stale LDS, causal={causal}")
