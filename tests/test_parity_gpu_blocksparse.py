@@ -18,7 +18,7 @@ import pytest
 import oracle
 import synth
 from tests import parity
-from tests.gpu_util import bf16_to_np, to_gpu
+from tests.gpu_util import bf16_to_np, poison_lds, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -171,19 +171,6 @@ def test_blocksparse_workload_sampled(name):
     parity.check(m, name)
 
 
-def _poison_lds():
-    """Dense forwards over NaN K and V, with enough workgroups to cover every CU
-    at both workgroup sizes, leave NaN bf16 rows in the LDS that the next
-    launch's workgroups inherit (LDS is not cleared between launches)."""
-    import torch
-    import scaled_dot_product_17_amd as sdpa
-    for n in (8192, 4096):          # 8-wave and 4-wave workgroups, 512 of each
-        q = torch.randn(1, 16, n, 128, device="cuda").to(torch.bfloat16)
-        kv = torch.full((1, 16, n, 128), float("nan"), device="cuda", dtype=torch.bfloat16)
-        sdpa.fwd(q, kv, kv)
-    torch.cuda.synchronize()
-
-
 @pytest.mark.parametrize("causal", [False, True])
 def test_stale_lds_is_never_read(causal):
     """Launches whose LDS rings are not cleared first (block-sparse with N a
@@ -208,7 +195,7 @@ def test_stale_lds_is_never_read(causal):
         return [bf16_to_np(o1), l1.cpu().numpy(), bf16_to_np(o2), l2.cpu().numpy()]
 
     first = both()
-    _poison_lds()
+    poison_lds()
     after = both()
     for a, b in zip(first, after):
         assert np.array_equal(a, b, equal_nan=True)
