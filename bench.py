@@ -519,7 +519,7 @@ def main_varlen(args, w):
                    "window": [w.left, w.right], "D": w.D, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fwd_kernel<varlen>",
+                     "traffic": stored_traffic(w.name, "attn_fwd_varlen"), "kernel": "attn_fwd_kernel<varlen>",
                      "launch_ms_mean": round(mean, 4),
                      "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
                                            round(float(np.percentile(per, 90)), 4)]},
@@ -619,7 +619,8 @@ def main_sparse(args, w):
                                "per_head": w.per_head},
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic(w.name, "attn_fwd_blocksparse"),
                      "kernel": "attn_fwd_kernel<sparse>", "launch_ms_mean": round(mean, 4),
                      "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
                                            round(float(np.percentile(per, 90)), 4)]},

@@ -94,7 +94,7 @@ struct Params {
     // packed variable-length batch (VARLEN kernels only): B = 1 and N = tokens
     const int* cu;    // n_seq + 1 token offsets
     int n_seq;
-    int lpt;          // several sequences of unequal lengths: tile-major order
+    int dealt;        // several sequences of unequal lengths: head groups dealt to the XCDs in turn
     int left, right;  // window: row i sees keys i-left .. i+right (< 0: unbounded)
     // block-sparse mask (SPARSE kernels only): lists of SP_BLOCK-key blocks per
     // (mask head, SP_BLOCK-row query block), block-compressed-row form
@@ -198,15 +198,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     // batch index is the sequence of a packed batch (B = 1, N = all tokens).
     const int logical = xcd_remap(blockIdx.x, p.total);
     int bh, qt;
-    if (VARLEN && p.n_seq > 1 && p.lpt) {
-        // several sequences of unequal lengths: tile-major, largest tile index
-        // first.  Tiles far into a sequence exist only for long sequences and
-        // carry the most keys (causal, windowed or not), so the heaviest work
-        // starts first and short tiles fill the tail (longest-processing-time-
-        // first order).
+    if (VARLEN && p.n_seq > 1 && p.dealt) {
+        // several sequences of unequal lengths: groups of cgroup (sequence,
+        // head)s, each group's tiles tile-major with the heaviest first, so a
+        // group's K/V is read from HBM about once and then served by its XCD's
+        // L2.  Whole groups are dealt to the 8 XCDs in turn (workgroup i runs on
+        // XCD i % 8), so every XCD receives an even share of every sequence's
+        // heads and the XCDs finish together.
         const int per = p.B * p.Hq;
-        qt = p.n_qtiles - 1 - logical / per;
-        bh = logical % per;
+        const int G = p.cgroup > 1 ? p.cgroup : 1;
+        const int x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+        const int k = sx / (G * p.n_qtiles);
+        const int r = sx - k * G * p.n_qtiles;
+        const int grp = x + 8 * k;
+        const int gh = min(G, per - grp * G);   // heads in this group (the last may be short)
+        if (gh <= 0 || r >= gh * p.n_qtiles) return;   // padding of the grid: no barrier yet
+        qt = p.n_qtiles - 1 - r / gh;
+        bh = grp * G + r % gh;
     } else if (CAUSAL && !SPARSE) {
         // groups of cgroup (batch, head)s one after another, so the tiles of a
         // group share K/V in the L2 of one XCD; within a group tile-major,
@@ -770,7 +778,15 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     // workgroups balance better (as for short dense sequences)
     const int br = BR / 2;
     const int64_t n_qtiles = ((int64_t)max_seqlen + br - 1) / br;
-    const int64_t grid = (int64_t)n_seq * H_q * n_qtiles;
+    // Sequences of nearly equal length (the longest within 1.25x the mean)
+    // take the dense order: a few heads at a time, whose K/V stays in one
+    // XCD's L2 (grouped as for dense causal grids).  Unequal lengths deal whole
+    // groups of heads to the XCDs in turn, which balances them.
+    const bool unequal = n_seq > 1 && (int64_t)max_seqlen * n_seq * 4 > (int64_t)total * 5;
+    const int64_t pairs = (int64_t)n_seq * H_q;
+    const int64_t cgroup = std::min<int64_t>(pairs, (64 + n_qtiles - 1) / n_qtiles);
+    const int64_t n_groups = (pairs + cgroup - 1) / cgroup;
+    const int64_t grid = unequal ? 8 * ((n_groups + 7) / 8) * cgroup * n_qtiles : pairs * n_qtiles;
     if (grid > INT32_MAX || n_seq == INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
     if (mis != 0 || (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) != 0) return ATTN_ERR_ALIGN;
@@ -803,12 +819,8 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.total = (int)grid;
     p.cu = cu_seqlens;
     p.n_seq = n_seq;
-    // Sequences of nearly equal length (the longest within 1.25x the mean)
-    // take the dense order: a few heads at a time, whose K/V stays in one
-    // XCD's L2 (grouped as for dense causal grids).  Unequal lengths take the
-    // tile-major longest-first order, which balances them.
-    p.lpt = n_seq > 1 && (int64_t)max_seqlen * n_seq * 4 > (int64_t)total * 5;
-    p.cgroup = (int)std::min<int64_t>((int64_t)n_seq * H_q, (64 + n_qtiles - 1) / n_qtiles);
+    p.dealt = unequal;
+    p.cgroup = (int)cgroup;
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;
     set_scale(p, scale);
