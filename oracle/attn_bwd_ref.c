@@ -312,8 +312,10 @@ int attn_bwd_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 /*
  * dK and dV of a subset of key rows: n_keys flat key ids ((b*H_kv + kv)*N + j).
  * dk, dv (and the optional mag_dk, mag_dv) are [n_keys, D] doubles in the order
- * given.  Phase 1 runs, without dQ, over every row of the query heads whose
- * group contains a listed key; phase 2 only for the listed keys.  Same
+ * given.  Phase 1 runs, without dQ, over the rows of the query heads whose
+ * group contains a listed key that phase 2 reads: every row, or with the causal
+ * mask only rows i >= the smallest listed key of that (b, kv) panel (row i sees
+ * key j only when j <= i).  Phase 2 runs only for the listed keys.  Same
  * arithmetic as attn_bwd_ref_f64, so the rows agree with its full result.
  * Returns 0, -1 on bad arguments, -2 on allocation failure.
  */
@@ -332,24 +334,30 @@ int attn_bwd_ref_keys_f64(const uint16_t *q, const uint16_t *k, const uint16_t *
         if (keys[t] < 0 || keys[t] >= nkv * N) return -1;
     if (n_keys == 0) return 0;
 
-    /* the (b, kv) panels that hold a listed key, and every row of their heads */
-    char *used = (char *)calloc((size_t)nkv, 1);
+    /* the (b, kv) panels that hold a listed key, the first row of each that
+     * phase 2 reads (causal: the panel's smallest listed key; else row 0), and
+     * those rows of every query head of the panel's group */
+    int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (size_t)nkv);
     double *stats = bwd_stats_alloc(total);
     int64_t *rows = NULL;
     int rc = -2;
-    if (!used || !stats) goto done;
-    for (int64_t t = 0; t < n_keys; ++t) used[keys[t] / N] = 1;
-    int64_t n_used = 0;
-    for (int64_t u = 0; u < nkv; ++u) n_used += used[u];
+    if (!first || !stats) goto done;
+    for (int64_t u = 0; u < nkv; ++u) first[u] = N;   /* N: panel unused */
+    for (int64_t t = 0; t < n_keys; ++t) {
+        const int64_t u = keys[t] / N, j = keys[t] % N;
+        const int64_t f = causal ? j : 0;
+        if (f < first[u]) first[u] = f;
+    }
     const int64_t group = H_q / H_kv;
-    rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_used * group * N));
+    int64_t n_need = 0;
+    for (int64_t u = 0; u < nkv; ++u) n_need += group * (N - first[u]);
+    rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_need > 0 ? n_need : 1));
     if (!rows) goto done;
     int64_t n_rows = 0;
     for (int64_t u = 0; u < nkv; ++u) {
-        if (!used[u]) continue;
         const int64_t b = u / H_kv, kvh = u % H_kv;
         for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)
-            for (int64_t i = 0; i < N; ++i) rows[n_rows++] = (b * H_q + h) * N + i;
+            for (int64_t i = first[u]; i < N; ++i) rows[n_rows++] = (b * H_q + h) * N + i;
     }
     bctx_t c;
     memset(&c, 0, sizeof c);
@@ -367,7 +375,7 @@ int attn_bwd_ref_keys_f64(const uint16_t *q, const uint16_t *k, const uint16_t *
     rc = bwd_par_for(&c, 1, n_rows, n_threads);
     if (rc == 0) rc = bwd_par_for(&c, 2, n_keys, n_threads);
 done:
-    free(used);
+    free(first);
     free(stats);
     free(rows);
     return rc;

@@ -47,8 +47,12 @@ MUTATIONS = {
                               "const double kjd = bwd_widen(kp[(nkeys - 1 - j) * D + d]);"),
     "mag_dv_signed": ("if (mdv) mdv[d] += p * fabs(dorow[d]);",
                       "if (mdv) mdv[d] += p * dorow[d];"),
-    "keys_mode_skips_group": ("for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)\n            for (int64_t i = 0; i < N; ++i) rows[n_rows++]",
-                              "for (int64_t h = kvh * group; h < kvh * group + 1; ++h)\n            for (int64_t i = 0; i < N; ++i) rows[n_rows++]"),
+    "keys_mode_skips_group": ("for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)\n            for (int64_t i = first[u]; i < N; ++i) rows[n_rows++]",
+                              "for (int64_t h = kvh * group; h < kvh * group + 1; ++h)\n            for (int64_t i = first[u]; i < N; ++i) rows[n_rows++]"),
+    "keys_mode_first_row_past_key": ("const int64_t f = causal ? j : 0;",
+                                     "const int64_t f = causal ? j + 1 : 0;"),
+    "keys_mode_skips_rows_noncausal": ("const int64_t f = causal ? j : 0;",
+                                       "const int64_t f = j;"),
     "mag_dq_drops_k_abs": ("if (mdq_row) mdq_row[d] += w * fabs(kjd);",
                            "if (mdq_row) mdq_row[d] += w * kjd;"),
 }

@@ -121,6 +121,37 @@ def test_bwd_split_parts():
 
 
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.5])
+def _kgroup(B, Hkv, N, ns):
+    """The causal dK/dV grid's interleave of (batch, K/V head, part) units, as
+    attn_bwd_ws sets it: enough 128-key tiles to fill one XCD's 32 workgroup
+    slots, at most all units."""
+    n_ktiles = -(-N // 128)
+    return min(B * Hkv * ns, -(-32 // n_ktiles))
+
+
+def test_bwd_split_mqa_full():
+    """The dK/dV split path of the long-context causal MQA workload (B=1,
+    H_q=16, H_kv=1, N=32768: 8 parts of 2 query heads, one unit per causal
+    interleave group) at N=4096, where the oracle computes every gradient:
+    the same part count, heads per part and interleave, on peaky inputs
+    (Q, K scaled by 3 as in that workload), compared element by element."""
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N_big, N = 1, 16, 1, 32768, 4096
+    ns = sdpa.attn_bwd_splits(B, Hq, Hkv, N_big, 128, True, 0)
+    assert ns == 8
+    assert sdpa.attn_bwd_splits(B, Hq, Hkv, N, 128, True, ns) == ns
+    assert _kgroup(B, Hkv, N_big, ns) == _kgroup(B, Hkv, N, ns) == 1
+    q = synth.normal_bf16(13500, (B, Hq, N, 128), 3.0)
+    k = synth.normal_bf16(13501, (B, Hkv, N, 128), 3.0)
+    v = synth.normal_bf16(13502, (B, Hkv, N, 128))
+    do = synth.normal_bf16(13503, (B, Hq, N, 128))
+    say(f"[bwd mqa split] N={N} n_splits={ns}")
+    res = run_bwd(q, k, v, do, True, SCALE, n_splits=ns)
+    ref = oracle.attn_bwd_ref(q, k, v, do, True, SCALE, mags=True)
+    check_all(res, ref, f"causal MQA N={N} n_splits={ns}")
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.5])
 def test_bwd_other_scales(scale):
     say(f"[bwd scale] {scale}")
     q, k, v, do = inputs(1, 4, 2, 300, seed=12000)
@@ -206,19 +237,32 @@ def test_bwd_workload_sampled(name):
     say(f"  {name} dq rows: {met}")
     parity.bwd_check(met, f"{name} dq")
 
-    # dK, dV on sampled keys of one or two K/V panels (the oracle then needs
-    # every row of those panels' query heads)
+    # dK, dV on sampled keys of one or two K/V panels.  The oracle needs every
+    # row of those panels' query heads that sees a sampled key: all rows, or
+    # with the causal mask the rows from the smallest sampled key on.  Where
+    # all rows of a group would take too long (the 16-head causal MQA panel at
+    # 32768 tokens: 16 * 32768 rows), the keys come from the panel's last
+    # 1024, i.e. its last 8 key tiles (the same dK/dV parts and sum; the
+    # split grid at a smaller size is compared in full by
+    # test_bwd_split_mqa_full).
     group_rows = (w.H_q // w.H_kv) * w.N * w.N
     panels = [(0, 0)] if group_rows > 2 ** 28 or w.B * w.H_kv == 1 else \
         [(0, 0), (w.B - 1, w.H_kv - 1)]
     if group_rows <= 2 ** 30:
         keys = _panel_keys(w.B, w.H_kv, w.N, panels, rng)
-        rk, rv, mk, mv = oracle.attn_bwd_ref(q, k, v, do, w.causal, w.scale, keys=keys, mags=True)
-        kidx = torch.from_numpy(keys).cuda()
-        for nm, g, r, m in (("dk", dk, rk, mk), ("dv", dv, rv, mv)):
-            met = parity.bwd_compare(bf16_to_np(g.view(-1, 128)[kidx]), r, m)
-            say(f"  {name} {nm} keys: {met}")
-            parity.bwd_check(met, f"{name} {nm}")
+    else:
+        assert w.causal, "a non-causal group this large has no cheap key sample"
+        lo = w.N - 1024
+        js = {lo, lo + 1, lo + 127, lo + 128, w.N - 129, w.N - 128, w.N - 2, w.N - 1} | \
+            set(int(x) for x in rng.integers(lo, w.N, 40))
+        keys = np.array(sorted(js), np.int64)   # panel (0, 0)
+    say(f"  {name}: oracle dK/dV for {len(keys)} keys")
+    rk, rv, mk, mv = oracle.attn_bwd_ref(q, k, v, do, w.causal, w.scale, keys=keys, mags=True)
+    kidx = torch.from_numpy(keys).cuda()
+    for nm, g, r, m in (("dk", dk, rk, mk), ("dv", dv, rv, mv)):
+        met = parity.bwd_compare(bf16_to_np(g.view(-1, 128)[kidx]), r, m)
+        say(f"  {name} {nm} keys: {met}")
+        parity.bwd_check(met, f"{name} {nm}")
 
     # every row of P sums to one: sum_j dV_j = sum of dO over the group's rows,
     # within U (sum_j |dV_j| + sum_i |dO_i|) (the rounding of P and of dV)
