@@ -62,9 +62,11 @@ int attn_blocksparse_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_
         if (rows[t] < 0 || rows[t] >= all) return -1;
     double *e = (double *)malloc(sizeof(double) * (size_t)N);
     char *allowed = (char *)malloc((size_t)n_blocks);
-    if (!e || !allowed) {
+    char *sees = (char *)malloc((size_t)N);   /* row i sees key j */
+    if (!e || !allowed || !sees) {
         free(e);
         free(allowed);
+        free(sees);
         return -2;
     }
     const int group = H_q / H_kv;
@@ -87,7 +89,9 @@ int attn_blocksparse_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_
         int seen = 0;
         for (int j = 0; j < N; ++j) {
             e[j] = -INFINITY;
+            sees[j] = 0;
             if (!allowed[j / block] || (causal && j > i)) continue;
+            sees[j] = 1;
             double dot = 0.0;
             for (int d = 0; d < D; ++d) dot += bs_widen(qr[d]) * bs_widen(kp[(size_t)j * D + d]);
             e[j] = scale * dot;
@@ -100,7 +104,7 @@ int attn_blocksparse_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_
         }
         double l = 0.0;
         for (int j = 0; j < N; ++j) {
-            if (e[j] == -INFINITY) continue;
+            if (!sees[j]) continue;
             const double p = exp(e[j] - m);
             l += p;
             for (int d = 0; d < D; ++d) orow[d] += p * bs_widen(vp[(size_t)j * D + d]);
@@ -110,5 +114,6 @@ int attn_blocksparse_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_
     }
     free(e);
     free(allowed);
+    free(sees);
     return 0;
 }

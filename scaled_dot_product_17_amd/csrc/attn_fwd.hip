@@ -76,6 +76,12 @@ constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx
 constexpr int SP_BLOCK = 128;
 constexpr int SP_MAX = 2048;               // key blocks a mask may have (N <= 262144)
 constexpr int SP_BYTES = 2 * SP_MAX + 64;  // union list + per-wave counts
+constexpr int RARE_WAVE_BYTES = 32 * KB * 2;  // a wave's bf16 weights of one block (non-finite V path)
+// Mark the fast kernel leaves in the first output row of a workgroup it hands
+// to the exact kernel: eight signalling-NaN bf16 codes (0x7F81 .. 0x7F88).
+// Arithmetic never produces them (every NaN it makes is quiet), so no output
+// row can hold them.
+__constant__ const uint32_t NF_MARK[4] = {0x7F827F81u, 0x7F847F83u, 0x7F867F85u, 0x7F887F87u};
 
 struct Params {
     const uint16_t* q;
@@ -178,7 +184,9 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
 }
 
-template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW>
+// SAFE = false: the fast kernel.  SAFE = true: the exact kernel, which redoes
+// only the workgroups the fast kernel marked (see NF_MARK).
+template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW, bool SAFE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     static_assert(NW == 8 || NW == 4, "workgroups of 4 or 8 waves");
     constexpr int BRW = 32 * NW;                 // query rows of this workgroup
@@ -186,7 +194,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     constexpr int DMA_PER_WAVE = 32 / (4 * NW);  // 4-row DMA instructions per wave per key block
     constexpr int QB_WG = BRW / SP_BLOCK;        // SPARSE: query blocks per workgroup (1 or 2)
     constexpr int SP_PER_T = SP_MAX / NTH;       // SPARSE: key blocks each thread compacts
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SPARSE ? SP_BYTES : 0)];
+    constexpr int RARE_OFF = LDS_BYTES + (SPARSE ? SP_BYTES : 0);   // SAFE: per-wave weights of a masked block
+    __shared__ __attribute__((aligned(1024))) char lds[RARE_OFF + (SAFE ? NW * RARE_WAVE_BYTES : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -253,6 +262,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     const int pbat = VARLEN ? 0 : b;      // batch index of the panels
     const size_t qo_panel = ((size_t)pbat * p.Hq + h) * (size_t)N * HD;
     const size_t kv_panel = ((size_t)pbat * p.Hkv + kvh) * (size_t)N * HD;
+    uint16_t* const mark = p.o + qo_panel + (size_t)q0 * HD;   // the workgroup's first output row
+    if constexpr (SAFE) {
+        // only the workgroups the fast kernel marked (every thread reads the
+        // same 16 bytes, so the exit is workgroup-uniform)
+        const u32x4 w = *(const u32x4*)mark;
+        if (w[0] != NF_MARK[0] || w[1] != NF_MARK[1] || w[2] != NF_MARK[2] || w[3] != NF_MARK[3]) return;
+    }
 
     // ---- key blocks of 32 from key kb0: n_blk_wg streamed through LDS, n_blk used
     // by this wave.  Dense causal: a wave's 32 rows start on a block boundary, so
@@ -380,9 +396,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     auto dma_block = [&](const uint16_t* panel, const uint32_t* voff, int ring, int g) {
         if (g < n_blk_wg) {
             const int key = SPARSE ? sp_key(g) : kb0 + g * KB;
-            if (SPARSE && key >= N) return;   // a 32-key part past the end of a short last block
-            const u32x4 r = sgpr_rsrc(panel + (size_t)(key - kb0) * HD, (uint32_t)(N - key) * ROW_BYTES);
             const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 4 * DMA_PER_WAVE * wave * ROW_BYTES;
+            // the copy's range ends at the sequence's last key (VARLEN) or the
+            // panel's: rows past it are not fetched.  VARLEN and SPARSE zero
+            // those rows of the slot, so no row of an earlier block stays there
+            // (a key outside some row's window or list; the dense path's
+            // leftovers are earlier keys of the same rows' panel)
+            const int end = VARLEN ? s1 : N;
+            if constexpr (VARLEN || SPARSE) {
+                if (key + KB > end) {
+#pragma unroll
+                    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+                        const int row = 4 * DMA_PER_WAVE * wave + 4 * i + (lane >> 4);
+                        if (key + row >= end)
+                            *(u32x4*)(lds + (dst - lds_base) + 4 * i * ROW_BYTES + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+                if (key >= end) return;   // SPARSE: a 32-key part past the end of a short last block
+            }
+            const u32x4 r = sgpr_rsrc(panel + (size_t)(key - kb0) * HD, (uint32_t)(end - key) * ROW_BYTES);
 #pragma unroll
             for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
         }
@@ -463,22 +495,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         }
         return (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
     };
+    // true when key `key` of a block (listed or not for this wave's query
+    // block: SPARSE) is not visible to this lane's row
+    auto key_bad = [&](int key, bool listed) {
+        if constexpr (VARLEN) return key < lo_i || key > hi_i;
+        else return !listed || (key >= N) || (CAUSAL && key > myq);
+    };
     auto apply_mask = [&](f32x16& s, int g) {
         const int kbase_g = SPARSE ? sp_key(g) : kb0 + g * KB;
         const bool listed = SPARSE ? sp_member(g) : true;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kbase_g + 8 * (r >> 2) + 4 * hh + (r & 3);
-            bool bad;
-            if constexpr (VARLEN) bad = key < lo_i || key > hi_i;
-            else bad = !listed || (key >= N) || (CAUSAL && key > myq);
-            s[r] = bad ? -INFINITY : s[r];
-        }
+        for (int r = 0; r < 16; ++r)
+            s[r] = key_bad(kbase_g + 8 * (r >> 2) + 4 * hh + (r & 3), listed) ? -INFINITY : s[r];
     };
+    bool mask_prev = false;   // the previous step's block was masked
 
     f32x16 o[4];          // O^T: 4 blocks of 32 head dims x 32 query columns
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    const bool live = myq < s1;   // a row that is written (padding rows past the end are not)
     float m = -INFINITY;  // reference max of the raw scores q.k of this lane's row
     float mb = 0.f;       // m * c, or 0 while m is -inf
     float l = 0.f;        // this lane's partial sum of p (fp32): the LSE
@@ -499,6 +534,50 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
                                                                 o[db], 0, 0, 0);
             }
     };
+    // A masked block multiplies the V rows of keys some rows may not see by
+    // zero weights, and 0 * NaN or 0 * inf is NaN in the matrix core.  Before
+    // its main loop each wave scans the V rows of its masked blocks in global
+    // memory; only a wave that finds a non-finite value there runs the loop
+    // variant in which masked blocks take pv_exact instead of pv.
+    // O^T += V^T P^T for masked block gb whose V holds a non-finite value, as
+    // the formula has it: each visible key adds p * v to its rows and no other,
+    // so a NaN or an infinity reaches exactly the rows that see its key.  The
+    // wave writes its rows' bf16 weights to its LDS area, then each lane walks
+    // the block's 32 keys and adds p * v (fp32) for those its row sees to its
+    // 64 output elements; element (db, r) of a lane is head dim
+    // 32 db + 8 (r / 4) + 4 hh + r % 4.  Slow, and only taken for such blocks.
+    auto pv_exact = [&](const u32x4 (&pw)[2], uint32_t vslot, int gb) {
+        char* wp = lds + RARE_OFF + wave * RARE_WAVE_BYTES + l32 * (KB * 2);   // this row's 32 weights
+        // keys 8a + 4hh + (0..3) of the row are accumulator registers 4a .. 4a+3
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const u32x4& w = pw[a >> 1];
+            *(uint2*)(wp + 2 * (8 * a + 4 * hh)) = uint2{w[2 * (a & 1)], w[2 * (a & 1) + 1]};
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+        __builtin_amdgcn_wave_barrier();
+        const int kbase_g = SPARSE ? sp_key(gb) : kb0 + gb * KB;
+        const bool listed = SPARSE ? sp_member(gb) : true;
+#pragma unroll 1
+        for (int j = 0; j < KB; ++j) {
+            if (key_bad(kbase_g + j, listed)) continue;
+            const float pj = (float)*(const __bf16*)(wp + 2 * j);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    __builtin_amdgcn_sched_barrier(0);   // one 4-dim read in flight at a time
+                    const uint32_t chunk = (uint32_t)(4 * db + q);
+                    const uint32_t off = vslot + (uint32_t)j * ROW_BYTES +
+                                         ((chunk ^ (((uint32_t)j & 3u) << 2)) << 4) + 8u * (uint32_t)hh;
+                    const bf16x4 v4 = *(const bf16x4*)(lds + off);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) o[db][4 * q + rr] = fmaf(pj, (float)v4[rr], o[db][4 * q + rr]);
+                }
+        }
+        __builtin_amdgcn_wave_barrier();   // the area is rewritten only after every lane's reads
+    };
+
     // P = exp2(s*c - mb) rounded to bf16 in pairs (the B operand of the PV
     // MFMA); ls sums the fp32 p, lbs the bf16 pairs (v_dot2 against (1, 1)).
     auto probs = [&](const f32x16& s, u32x4 (&pw)[2], float& ls, float& lbs) {
@@ -551,20 +630,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         const bool use_n = !SPARSE || (g + 1 < n_blk_wg && sp_member(g + 1));
         const bool use_g = !SPARSE || (valid && sp_member(g));
         const bool use_p = !SPARSE || (g >= 1 && sp_member(g - 1));
-        if (!FIRST && valid && use_g && needs_mask(g)) apply_mask(s, g);
+        const bool mask_g = needs_mask(g);
+        if (!FIRST && valid && use_g && mask_g) apply_mask(s, g);
         if (use_n) scores(sn, KS);
-        if constexpr (!FIRST)
-            if (use_p) pv(pp, VS);
+        if constexpr (!FIRST) {
+            if constexpr (SAFE) {
+                // exact kernel: masked blocks take the exact product
+                if (use_p) {
+                    if (mask_prev) pv_exact(pp, VS, g - 1);
+                    else pv(pp, VS);
+                }
+            } else if (use_p) {
+                pv(pp, VS);
+            }
+        }
+        if constexpr (SAFE) mask_prev = mask_g;
         if (!use_g) return;
         float ls, lbs;
         probs(s, pc, ls, lbs);
         // keep P_g ahead of the branch below (not sunk into its fall-through
         // path), so its VALU work interleaves with the MFMAs issued above
         asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(ls), "+v"(lbs));
-        // VARLEN: a row whose window has not started yet keeps m = -inf; it moves
-        // its reference (through the rare path) at its first allowed key
-        const bool no_ref = (VARLEN || SPARSE) && m == -INFINITY && myq < s1;
-        const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM) || no_ref);
+        // While a row has seen no finite score (m = -inf: a window or block list
+        // that has not started, or -inf scores), mb is -inf, so any score makes
+        // its sum inf or NaN and takes the branch below, which moves m to the
+        // first finite score and weighs the rest of the block against it.
+        const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM));
         if (valid && over != 0) {
             const float m_new = fmaxf(m, row_max(s));
             const bool move = m_new > m;
@@ -578,6 +669,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             probs(s, pc, ls, lbs);
+            if (m == -INFINITY && live) mb = -INFINITY;
         }
         if (valid) {
             l += ls;
@@ -587,16 +679,56 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
 
     f32x16 sa, sb;    // scores of even / odd key blocks
     u32x4 pa[2], pb[2];  // bf16 P of even / odd key blocks
+    // Masked blocks are a prefix and a suffix of the wave's blocks (window
+    // start; causal diagonal, window end, sequence or panel end).  Their V rows
+    // in range are read from global memory and checked for a non-finite value.
+    uint32_t nf_bits = 0u;
+    if (!SAFE && n_blk > 0) {
+        const int end = VARLEN ? s1 : N;
+        auto vcheck = [&](int g) {
+            const int key = SPARSE ? sp_key(g) : kb0 + g * KB;
+            if (key >= end) return;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(vbase + (size_t)(key - kb0) * HD,
+                                                       (uint32_t)(end - key) * ROW_BYTES);
+#pragma unroll
+            for (int i = 0; i < BLK_BYTES / 1024; ++i) {
+                const u32x4 x = buf_load16(r, (uint32_t)(16 * lane + 1024 * i));
+                // a bf16 half with an all-ones exponent carries into its top bit
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nf_bits |= (x[e] & 0x7F807F80u) + 0x00800080u;
+            }
+        };
+        int g = 0;
+        for (; g < n_blk && needs_mask(g); ++g) vcheck(g);
+        for (int h = n_blk - 1; h >= g && needs_mask(h); --h) vcheck(h);
+    }
     // vmcnt(0) through the builtin, so the compiler also knows the Q loads are
     // complete and never waits on vmcnt (which counts the DMA) inside the loop
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    // fast kernel: the waves' answers meet in V slot 3 (not refilled before
+    // tile 1); a workgroup with a non-finite V value in a masked block marks its
+    // first output row and leaves the rows to the exact kernel
+    uint32_t* const nf_wave = (uint32_t*)(lds + V_RING + 3 * BLK_BYTES);
+    if constexpr (!SAFE) {
+        const bool nf = __builtin_amdgcn_ballot_w64((nf_bits & 0x80008000u) != 0u) != 0;
+        if (lane == 0) nf_wave[wave] = nf ? 1u : 0u;
+    }
     __syncthreads();
+    if constexpr (!SAFE) {
+        uint32_t any = 0u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any |= nf_wave[w];
+        if (any != 0u) {
+            if (tid == 0) *(u32x4*)mark = u32x4{NF_MARK[0], NF_MARK[1], NF_MARK[2], NF_MARK[3]};
+            return;
+        }
+    }
     if (n_blk > 0) {
         // block 0's scores and the first reference (its row max)
         scores(sa, K_RING);
         if (needs_mask(0)) apply_mask(sa, 0);
         m = row_max(sa);
-        mb = (m == -INFINITY) ? 0.f : m * c;
+        mb = (m == -INFINITY) ? (live ? -INFINITY : 0.f) : m * c;
     }
     __syncthreads();   // K slot 0 is refilled in the first tile
 
@@ -645,8 +777,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     const float l_tot = wave_swap_sum(l);
     const float lb_tot = wave_swap_sum(lb);
     // SPARSE: a row that sees no key (its lists hold none of its keys) gets
-    // O = 0 and LSE = -inf
-    const bool empty = SPARSE && !(lb_tot > 0.f);
+    // O = 0 and LSE = -inf.  A row that sees keys whose scores are all -inf
+    // gets NaN, as the formula gives (m = -inf, exp(-inf - m) = NaN).
+    // The union list is in key order, so a row sees a key exactly when the
+    // list is not empty and, causal, its first key block starts at or before
+    // the row (every listed block holds a key below N).
+    bool empty = false;
+    if constexpr (SPARSE) empty = n_blk_wg == 0 || (CAUSAL && sp_key(0) > myq);
     const float inv = empty ? 0.f : 1.0f / lb_tot;
     if (myq < s1) {
         uint16_t* orow = p.o + qo_panel + (size_t)myq * HD;
@@ -661,7 +798,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
             }
         if (p.lse != nullptr && hh == 0) {
             const size_t li = ((size_t)pbat * p.Hq + h) * (size_t)N + myq;
-            p.lse[li] = empty ? -INFINITY : m * p.lse_scale + logf(l_tot);
+            p.lse[li] = empty ? -INFINITY : m == -INFINITY ? __builtin_nanf("") : m * p.lse_scale + logf(l_tot);
         }
     }
 }
@@ -699,10 +836,17 @@ void set_scale(Params& p, float scale) {
 template <bool VARLEN, bool SPARSE, int NW = NWAVE>
 attn_status launch_fwd(const Params& p, bool causal, void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (causal)
-        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW>), dim3((unsigned)p.total), dim3(NW * 64), 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW>), dim3((unsigned)p.total), dim3(NW * 64), 0, s, p);
+    // the fast kernel, then the exact kernel over the same grid: it redoes the
+    // workgroups the fast kernel marked (a NaN or infinity in the V rows of a
+    // masked block) and every other workgroup of it exits at once
+    const dim3 grid((unsigned)p.total), block(NW * 64);
+    if (causal) {
+        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW, false>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW, true>), grid, block, 0, s, p);
+    } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW, false>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW, true>), grid, block, 0, s, p);
+    }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

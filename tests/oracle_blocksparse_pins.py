@@ -154,5 +154,45 @@ def pin_list_hygiene_and_sharing(bref):
         assert np.array_equal(so, o.reshape(-1, 16)[rows]) and np.array_equal(sl, lse.reshape(-1)[rows])
 
 
+def pin_sparse_nonfinite(bref):
+    """Non-finite inputs under a block list: a NaN in V of a block a query block
+    does not list leaves its rows bitwise unchanged, and reaches every row that
+    lists it; a listed key with a -inf score has weight 0 (torch's fp64 SDPA
+    over the row's other keys); a row whose listed scores are all -inf is NaN,
+    unlike a row with no listed key (O = 0, LSE = -inf)."""
+    B, Hq, Hkv, N, blk = 1, 2, 1, 24, 8
+    q, k, v = _inputs(2700, B, Hq, Hkv, N)
+    lists = [[0], [0, 1], [2], []]
+    ptr, idx = lists_to_csr(lists[:3])
+    o0, l0 = bref(q, k, v, ptr, idx, blk, False, SCALE)
+    v2 = v.copy()
+    v2[0, 0, 10, 4] = 0x7FC0        # key block 1: listed by query block 1 only
+    o2, l2 = bref(q, k, v2, ptr, idx, blk, False, SCALE)
+    assert np.all(np.isnan(o2[0, :, 8:16, 4])), "NaN must reach the rows that list its block"
+    keep = np.ones(o0.shape, bool)
+    keep[0, :, 8:16, 4] = False
+    assert np.array_equal(o2[keep], o0[keep]) and np.array_equal(l2, l0), "NaN spread"
+    # -inf score of listed key 3 for row 2 (query block 0 lists block 0 only)
+    q3, k3 = q.copy(), k.copy()
+    q3[0, 0, 2, 5] = 0x3F80         # +1
+    k3[0, 0, 3, 5] = 0xFF80         # -inf
+    o3, l3 = bref(q3, k3, v, ptr, idx, blk, False, SCALE)
+    keys = [0, 1, 2, 4, 5, 6, 7]
+    qi = torch.from_numpy(bits_to64(q3[0, 0, 2:3]))
+    ko = torch.from_numpy(bits_to64(k3[0, 0, keys]))
+    vo = torch.from_numpy(bits_to64(v[0, 0, keys]))
+    eo = torch.nn.functional.scaled_dot_product_attention(qi, ko, vo, scale=SCALE)
+    el = scipy.special.logsumexp(SCALE * (qi.numpy() @ ko.numpy().T), axis=-1)
+    close(o3[0, 0, 2], eo.numpy()[0], tol=1e-12, what="-inf score drops its key")
+    close(l3[0, 0, 2], el[0], tol=1e-12, what="-inf score drops its key (LSE)")
+    # all listed scores -inf (row 17 lists block 2: keys 16..23)
+    q4, k4 = q.copy(), k.copy()
+    k4[0, 0, 16:24, 6] = 0xBF80     # -1
+    q4[0, 1, 17, 6] = 0x7F80        # +inf
+    for causal in (False, True):
+        o4, l4 = bref(q4, k4, v, ptr, idx, blk, causal, SCALE)
+        assert np.all(np.isnan(o4[0, 1, 17])) and np.isnan(l4[0, 1, 17]), "all -inf listed scores"
+
+
 ALL_PINS = [pin_full_lists_equal_dense, pin_diagonal_blocks_equal_packed, pin_torch_expanded_mask,
-            pin_empty_rows, pin_locality, pin_list_hygiene_and_sharing]
+            pin_empty_rows, pin_locality, pin_list_hygiene_and_sharing, pin_sparse_nonfinite]

@@ -306,7 +306,90 @@ def pin_row_subset(ref):
             np.array_equal(ls, l.reshape(-1)[rows]), "row subset"
 
 
+# ---------------------------------------------------------------- non-finite inputs
+NAN_BITS, PINF_BITS, NINF_BITS = 0x7FC0, 0x7F80, 0xFF80
+
+
+def pin_nonfinite(ref):
+    """Non-finite inputs follow the formula in IEEE arithmetic (limits that hold
+    for any correct evaluation of it):
+      * NaN in q_i -> row i all NaN (O and LSE), every other row unchanged;
+      * NaN or +inf in V_j[d] -> O_i[d] NaN or +inf exactly for the rows that see
+        key j (each has weight > 0), every other element unchanged; +inf at
+        key j1 and -inf at key j2 > j1 of one column -> causal rows in
+        [j1, j2) +inf, rows from j2 on NaN;
+      * a -inf score of key j (q_i . k_j = -inf) gives it weight 0: row i equals
+        attention over the keys without j;
+      * a row whose scores are all -inf is NaN (max -inf, exp(-inf + inf) NaN);
+        a +inf score makes its row NaN (exp(inf - inf))."""
+    B, H, N, D = 1, 2, 24, 16
+    q, k, v = rnd(141, (B, H, N, D)), rnd(142, (B, H, N, D)), rnd(143, (B, H, N, D))
+    for causal in (False, True):
+        o0, l0 = ref(q, k, v, causal, SCALE)
+        sees = (np.arange(N)[:, None] >= np.arange(N)[None, :]) if causal else np.ones((N, N), bool)
+        # NaN in q
+        q1 = q.copy()
+        q1[0, 1, 9, 3] = NAN_BITS
+        o1, l1 = ref(q1, k, v, causal, SCALE)
+        assert np.all(np.isnan(o1[0, 1, 9])) and np.isnan(l1[0, 1, 9]), "NaN query row"
+        keep = np.ones((B, H, N), bool)
+        keep[0, 1, 9] = False
+        assert np.array_equal(o1[keep], o0[keep]) and np.array_equal(l1[keep], l0[keep]), "NaN row spread"
+        # NaN / inf in V
+        for bits, test in ((NAN_BITS, np.isnan), (PINF_BITS, np.isposinf)):
+            v2 = v.copy()
+            v2[0, 0, 13, 5] = bits
+            o2, l2 = ref(q, k, v2, causal, SCALE)
+            hit = np.zeros((B, H, N, D), bool)
+            hit[0, 0, sees[:, 13], 5] = True
+            assert np.all(test(o2[hit])), "non-finite V must reach every row that sees its key"
+            assert np.array_equal(o2[~hit], o0[~hit]) and np.array_equal(l2, l0), "non-finite V spread"
+        # +inf then -inf in one column
+        v3 = v.copy()
+        v3[0, 1, 4, 7] = PINF_BITS
+        v3[0, 1, 15, 7] = NINF_BITS
+        o3, _ = ref(q, k, v3, causal, SCALE)
+        col = o3[0, 1, :, 7]
+        if causal:
+            assert np.all(np.isfinite(col[:4])) and np.all(np.isposinf(col[4:15])) and np.all(np.isnan(col[15:]))
+        else:
+            assert np.all(np.isnan(col)), "+inf and -inf of one column give NaN"
+    # a -inf score drops its key: key j holds -inf in a dimension where row i's
+    # query is +1, so s_ij = -inf; row i then equals torch's fp64 SDPA and
+    # scipy's logsumexp over the other keys
+    q4, k4 = q.copy(), k.copy()
+    j, i = 6, 20
+    q4[0, 0, i, 2] = bf([1.0])[0]
+    k4[0, 0, j, 2] = NINF_BITS
+    o4, l4 = ref(q4, k4, v, False, SCALE)
+    others = [x for x in range(N) if x != j]
+    qi = torch.from_numpy(bits_to64(q4[0, 0, i:i + 1]))
+    ko = torch.from_numpy(bits_to64(k4[0, 0, others]))
+    vo = torch.from_numpy(bits_to64(v[0, 0, others]))
+    eo = torch.nn.functional.scaled_dot_product_attention(qi, ko, vo, scale=SCALE)
+    el = scipy.special.logsumexp(SCALE * (qi.numpy() @ ko.numpy().T), axis=-1)
+    close(o4[0, 0, i], eo.numpy()[0], tol=1e-12, what="-inf score drops its key")
+    close(l4[0, 0, i], el[0], tol=1e-12, what="-inf score drops its key (LSE)")
+    # the dropped key still takes part in the sum: 0 * NaN is NaN
+    v4 = v.copy()
+    v4[0, 0, j, 1] = NAN_BITS
+    o4n, _ = ref(q4, k4, v4, False, SCALE)
+    assert np.isnan(o4n[0, 0, i, 1]), "a zero weight times NaN is NaN"
+    assert np.array_equal(np.delete(o4n[0, 0, i], 1), np.delete(o4[0, 0, i], 1)), "zero-weight NaN spread"
+    # all -inf row, and a +inf score
+    q6, k6 = q.copy(), k.copy()
+    k6[0, 0, :, 11] = bf([-1.0])[0]
+    q6[0, 0, 3, 11] = PINF_BITS       # every score of row 3 is -inf
+    k6[0, 1, 8, 0] = PINF_BITS
+    q6[0, 1, 17, 0] = bf([1.0])[0]    # score of key 8 for row 17 is +inf
+    for causal in (False, True):
+        o6, l6 = ref(q6, k6, v, causal, SCALE)
+        assert np.all(np.isnan(o6[0, 0, 3])) and np.isnan(l6[0, 0, 3]), "all -inf row must be NaN"
+        assert np.all(np.isnan(o6[0, 1, 17])) and np.isnan(l6[0, 1, 17]), "+inf score row must be NaN"
+        assert np.all(np.isfinite(o6[0, 0, :3])), "other rows of the all -inf head stay finite"
+
+
 ALL_PINS = [pin_identical_keys, pin_dominant_score, pin_causal_row0, pin_probabilities,
             pin_constant_v, pin_uniform, pin_single_key, pin_hand_example, pin_library,
             pin_gqa_equals_repeated_mha, pin_key_shift, pin_key_permutation,
-            pin_causal_future, pin_causal_prefix, pin_row_subset]
+            pin_causal_future, pin_causal_prefix, pin_row_subset, pin_nonfinite]

@@ -119,5 +119,38 @@ def pin_window_locality(vref):
     assert not np.array_equal(a[1][:, i], c[1][:, i]), "a key inside the window was ignored"
 
 
-ALL_PINS = [pin_varlen_sequences_are_independent, pin_window_library, pin_window_closed_forms,
+def pin_varlen_nonfinite(vref):
+    """Non-finite values stay in their sequence and window: a NaN in V at the
+    first token of sequence 1 makes that element NaN in exactly the rows of
+    sequence 1 that see it (window and causal rule), and leaves every other
+    element bitwise unchanged; a row of sequence 2 whose scores are all -inf is
+    NaN (O and LSE)."""
+    Hq, Hkv, lens = 2, 1, [5, 7, 6]
+    q, k, v, cu = _packed(4100, Hq, Hkv, lens)
+    s1 = int(cu[1])
+    v2 = v.copy()
+    v2[0, s1, 3] = 0x7FC0
+    q3, k3 = q.copy(), k.copy()
+    s2 = int(cu[2])
+    k3[0, s2:, 9] = 0xBF80          # -1 in dim 9 for every key of sequence 2
+    q3[1, s2 + 2, 9] = 0x7F80       # +inf: every score of that row is -inf
+    for causal in (False, True):
+        for left, right in ((-1, -1), (2, 0), (1, 3)):
+            o0, l0 = vref(q, k, v, cu, causal, SCALE, left, right)
+            o2, l2 = vref(q, k, v2, cu, causal, SCALE, left, right)
+            hit = np.zeros(o0.shape, bool)
+            for i in range(s1, s2):
+                lo = max(s1, i - left) if left >= 0 else s1
+                hi = min(s2 - 1, i + right) if right >= 0 else s2 - 1
+                if causal:
+                    hi = min(hi, i)
+                if lo <= s1 <= hi:
+                    hit[:, i, 3] = True
+            assert np.all(np.isnan(o2[hit])), "NaN must reach the rows that see its key"
+            assert np.array_equal(o2[~hit], o0[~hit]) and np.array_equal(l2, l0), "NaN spread"
+            o3, l3 = vref(q3, k3, v, cu, causal, SCALE, left, right)
+            assert np.all(np.isnan(o3[1, s2 + 2])) and np.isnan(l3[1, s2 + 2]), "all -inf row"
+
+
+ALL_PINS = [pin_varlen_nonfinite, pin_varlen_sequences_are_independent, pin_window_library, pin_window_closed_forms,
             pin_window_locality]

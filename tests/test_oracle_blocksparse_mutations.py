@@ -25,6 +25,7 @@ MUTATIONS = {
     "lse_without_max": ("lse[t] = m + log(l);", "lse[t] = log(l);"),
     "empty_rows_nan": ("        if (!seen) {\n            lse[t] = -INFINITY;\n            continue;\n        }\n", ""),
     "drop_scale": ("e[j] = scale * dot;", "e[j] = dot;"),
+    "neg_inf_scores_skipped": ("if (!sees[j]) continue;", "if (!sees[j] || e[j] == -INFINITY) continue;"),
 }
 
 

@@ -17,6 +17,9 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_ref.c")
 
 MUTATIONS = {
     "drop_scale": ("s[j] = jb->scale * dot;", "s[j] = dot;"),
+    # non-finite inputs
+    "max_guarded_at_minus_inf": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j] - (m == -INFINITY ? 0.0 : m));"),
+    "zero_weights_skipped": ("const double p = s[j];", "const double p = s[j];\n        if (p == 0.0) continue;"),
     "causal_off_by_one": ("jb->causal ? i + 1 : N", "jb->causal ? (i + 2 < N ? i + 2 : N) : N"),
     "causal_excludes_diagonal": ("jb->causal ? i + 1 : N", "jb->causal ? (i > 0 ? i : 1) : N"),
     "gqa_modulo_map": ("const int64_t kvh = h / group;", "const int64_t kvh = h % jb->Hkv;"),

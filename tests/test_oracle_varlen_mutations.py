@@ -26,6 +26,8 @@ MUTATIONS = {
     "drop_scale": ("e[j - lo] = scale * dot;", "e[j - lo] = dot;"),
     "lse_without_max": ("lse[(size_t)h * total + i] = m + log(l);",
                         "lse[(size_t)h * total + i] = log(l);"),
+    "max_guarded_at_minus_inf": ("e[j - lo] = exp(e[j - lo] - m);",
+                                 "e[j - lo] = exp(e[j - lo] - (m == -INFINITY ? 0.0 : m));"),
 }
 
 

@@ -1,0 +1,155 @@
+"""GPU parity with non-finite inputs: NaN and infinities planted in Q, K and V
+propagate as the formula does (the fp64 oracles apply it in IEEE arithmetic):
+
+  * a NaN score, or a +inf score (m = +inf, exp(inf - inf) = NaN), makes the
+    whole row NaN: every O element and the LSE;
+  * a -inf score gives its key weight exp(-inf - m) = 0; a row whose scores are
+    all -inf is NaN (m = -inf, exp(-inf + inf) = NaN);
+  * a NaN or infinity in V_j[d] reaches O_i[d] of exactly the rows i that see
+    key j (p * inf = inf, inf - inf = NaN), and no row that does not: not the
+    earlier rows of a causal diagonal block, not rows outside a window, not the
+    rows of another packed sequence.
+
+The NaN / +inf / -inf pattern of O and LSE must equal the oracle's exactly;
+finite elements meet the forward's bar (tests/parity.py).  The planted scores
+stay within a few nats of each row's maximum, so no visible weight underflows.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+from tests.gpu_util import bf16_to_np, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1 / math.sqrt(128)))
+NAN, PINF, NINF, MINUS_ONE = 0x7FC0, 0x7F80, 0xFF80, 0xBF80   # bf16 bit patterns
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_dot_product_17_amd as sdpa
+    sdpa.load()
+
+
+def check_nonfinite(o, lse, o_ref, lse_ref, what):
+    """Exact NaN / +inf / -inf pattern, forward bar on the finite elements."""
+    for name, g, r in (("O", o, o_ref), ("LSE", lse, lse_ref)):
+        g = np.asarray(g, np.float64)
+        for kind, f in (("NaN", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+            diff = np.argwhere(f(g) != f(r))
+            assert diff.size == 0, f"{what}: {name} {kind} pattern differs at {diff[:6].tolist()}"
+    fin = np.isfinite(o_ref)
+    err = np.abs(np.asarray(o, np.float64)[fin] - o_ref[fin])
+    over = (err > parity.MAX_ABS) & ~parity.faithful(np.asarray(o, np.float64)[fin], o_ref[fin])
+    assert not over.any(), f"{what}: {int(over.sum())} finite O elements beyond the bar (max {err.max()})"
+    assert err.mean() <= parity.MEAN_ABS, f"{what}: mean-abs {err.mean()}"
+    lf = np.isfinite(lse_ref)
+    le = np.abs(np.asarray(lse, np.float64)[lf] - lse_ref[lf])
+    assert le.size == 0 or le.max() <= parity.LSE_ABS, f"{what}: LSE max-abs {le.max()}"
+    n_bad = int((~fin).sum())
+    say(f"  {what}: {n_bad} non-finite O elements, {int((~lf).sum())} non-finite LSE, "
+        f"finite max-abs {err.max():.2e}")
+    return n_bad
+
+
+def dense_case(B, Hq, Hkv, N, seed):
+    """Seeded inputs with NaN and infinities planted at rows chosen relative to
+    the 32-key blocks (mid diagonal block, tail)."""
+    q = synth.normal_bf16(seed, (B, Hq, N, 128))
+    k = synth.normal_bf16(seed + 1, (B, Hkv, N, 128))
+    v = synth.normal_bf16(seed + 2, (B, Hkv, N, 128))
+    g = Hq // Hkv
+    q[0, min(1, Hq - 1), 37 % N, 5] = NAN              # a NaN row
+    q[0, Hq - 1, 5 % N, 0] = PINF                      # +inf and -inf scores (signs of K[:, 0])
+    k[0, 0, 70 % N, 3] = PINF                          # key 70: +inf or -inf score by sign of q[3]
+    j = min(32 * 3 + 17, N - 1)
+    v[0, Hkv - 1, j, 9] = NAN                          # mid diagonal block: rows < j unaffected
+    v[0, 0, 50 % N, 7] = PINF                          # +inf then -inf in one column
+    v[0, 0, 150 % N, 7] = NINF
+    v[0, 0, N - 1, 0] = NINF                           # last key (a ragged tail block when N % 32)
+    # an all -inf row: K[:, 11] = -1 for the first K/V head, Q = +inf there
+    k[0, 0, :, 11] = MINUS_ONE
+    q[0, 0, 20 % N, 11] = PINF
+    assert g >= 1
+    return q, k, v
+
+
+DENSE = [(1, 4, 2, 200), (1, 4, 2, 256), (1, 2, 1, 4200), (2, 4, 4, 1000)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", DENSE, ids=lambda s: "b%d_hq%d_hkv%d_n%d" % s)
+def test_nonfinite_dense(shape, causal):
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = shape
+    say(f"[nonfinite dense] {shape} causal={causal}")
+    q, k, v = dense_case(B, Hq, Hkv, N, seed=21000 + N)
+    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=causal, scale=SCALE)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, causal, SCALE)
+    n = check_nonfinite(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref, f"{shape} causal={causal}")
+    assert n > 0
+
+
+def test_nonfinite_causal_8wave():
+    """A causal length that takes the 8-wave kernel (N > 8192)."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = 1, 2, 1, 8300
+    say(f"[nonfinite dense] causal N={N}")
+    q, k, v = dense_case(B, Hq, Hkv, N, seed=21900)
+    v[0, 0, 8192 + 40, 100] = PINF
+    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, True, SCALE)
+    check_nonfinite(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref, f"causal N={N}")
+
+
+VARLEN = [([100, 130, 70], (-1, -1)), ([100, 130, 70], (16, 0)), ([33, 64, 300], (40, 40)),
+          ([1, 96, 5], (-1, -1))]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "n%s_w%d_%d" % ("-".join(map(str, c[0])), *c[1]))
+def test_nonfinite_varlen(case, causal):
+    """NaN and infinities at sequence boundaries of a packed batch reach only
+    their own sequence's rows (and, with a window, only rows in it)."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    lens, window = case
+    Hq, Hkv = 4, 2
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    seed = 22000 + total + window[0]
+    q = synth.normal_bf16(seed, (Hq, total, 128))
+    k = synth.normal_bf16(seed + 1, (Hkv, total, 128))
+    v = synth.normal_bf16(seed + 2, (Hkv, total, 128))
+    s1 = int(cu[1])
+    v[0, s1 - 1, 4] = PINF          # last key of sequence 0
+    v[0, s1, 4] = NAN               # first key of sequence 1
+    v[1, min(s1 + 40, total - 1), 60] = NINF
+    k[1, min(s1 + 10, total - 1), 2] = PINF
+    q[2, total - 1, 8] = NAN
+    say(f"[nonfinite varlen] {lens} window={window} causal={causal}")
+    cu_t = torch.from_numpy(cu).cuda()
+    o, lse = sdpa.fwd_varlen(to_gpu(q), to_gpu(k), to_gpu(v), cu_t, int(max(lens)), causal=causal,
+                             scale=SCALE, window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_varlen_ref(q, k, v, cu, causal, SCALE, *window)
+    n = check_nonfinite(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref,
+                        f"{lens} window={window} causal={causal}")
+    assert n > 0
