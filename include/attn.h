@@ -71,6 +71,14 @@ typedef enum attn_status {
  * q, k, v or each other.  Results are bitwise reproducible for identical
  * inputs.  Thread-safe.
  *
+ * Non-finite inputs propagate as the formula does in IEEE arithmetic, over the
+ * keys each row sees: a NaN or +inf score makes its row NaN (O and LSE), a -inf
+ * score gives its key weight 0, a row whose scores are all -inf is NaN, and a
+ * NaN or infinity in V row j reaches O of exactly the rows that see key j.
+ * The call enqueues two kernels: the fast one, and an exact one that redoes
+ * only the query tiles whose masked key blocks (causal diagonal, ragged end)
+ * hold a NaN or infinity in V; its other workgroups exit at once.
+ *
  * Errors: returns a status code (see above).  A fault inside the kernel (for
  * example a pointer to too little memory) is reported by the HIP runtime at
  * the caller's next synchronisation, not by this call.
@@ -152,8 +160,13 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
  * fp32 softmax and accumulation; page "GPU注意力算子性能优化" (QiMeng-Attention),
  * section 3.1.1; FP8 storage with wider accumulation: page "从硬件视角看注意力
  * 机制优化", section 2.3).  The softmax weights are rounded to e4m3 for the
- * second product and O is normalised by the sum of the rounded weights; the
- * LSE uses the fp32 weights.
+ * second product: each row's weights of a block of 64 keys are first
+ * multiplied by the power of two that puts their largest one in (224, 448],
+ * the top binade of e4m3 (so none overflows and none is rounded more coarsely
+ * than 2^-10 / 224 of the largest), and the matrix core's E8M0 operand scale
+ * takes the power of two back exactly.  O is normalised by the sum of the
+ * rounded weights; the LSE uses the fp32 weights.  NaN codes propagate as in
+ * attn_fwd (e4m3 has no infinity).
  *
  * q8       device pointer, uint8 [B, H_q, N, D] codes, contiguous row-major.
  * k8, v8   device pointers, uint8 [B, H_kv, N, D] codes.

@@ -76,7 +76,12 @@ constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx
 constexpr int SP_BLOCK = 128;
 constexpr int SP_MAX = 2048;               // key blocks a mask may have (N <= 262144)
 constexpr int SP_BYTES = 2 * SP_MAX + 64;  // union list + per-wave counts
-constexpr int RARE_WAVE_BYTES = 32 * KB * 2;  // a wave's bf16 weights of one block (non-finite V path)
+// Exact kernel (non-finite V in a masked block): a zero block, and per wave up
+// to MAX_SAVED masked blocks' bf16 weights (32 rows x 32 keys), the factor each
+// block's weights have been rescaled by since (one per lane) and its index.
+constexpr int MAX_SAVED = 4;
+constexpr int SAVE_P = 32 * KB * 2;
+constexpr int SAVE_WAVE_BYTES = MAX_SAVED * (SAVE_P + 64 * 4) + 16;
 // Mark the fast kernel leaves in the first output row of a workgroup it hands
 // to the exact kernel: eight signalling-NaN bf16 codes (0x7F81 .. 0x7F88).
 // Arithmetic never produces them (every NaN it makes is quiet), so no output
@@ -194,8 +199,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     constexpr int DMA_PER_WAVE = 32 / (4 * NW);  // 4-row DMA instructions per wave per key block
     constexpr int QB_WG = BRW / SP_BLOCK;        // SPARSE: query blocks per workgroup (1 or 2)
     constexpr int SP_PER_T = SP_MAX / NTH;       // SPARSE: key blocks each thread compacts
-    constexpr int RARE_OFF = LDS_BYTES + (SPARSE ? SP_BYTES : 0);   // SAFE: per-wave weights of a masked block
-    __shared__ __attribute__((aligned(1024))) char lds[RARE_OFF + (SAFE ? NW * RARE_WAVE_BYTES : 0)];
+    constexpr int ZERO_OFF = LDS_BYTES + (SPARSE ? SP_BYTES : 0);   // exact kernel: a block of zeros
+    constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;                     // exact kernel: per-wave saved blocks
+    __shared__ __attribute__((aligned(1024))) char lds[ZERO_OFF + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -449,6 +455,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
             *(u32x4*)(lds + 16 * (tid + NTH * i)) = z;
         __syncthreads();
     }
+    if constexpr (SAFE) {
+        // the zero block masked products run against (first read after the
+        // barrier below)
+#pragma unroll
+        for (int i = 0; i < BLK_BYTES / (16 * NTH); ++i)
+            *(u32x4*)(lds + ZERO_OFF + 16 * (tid + NTH * i)) = u32x4{0u, 0u, 0u, 0u};
+    }
     dma_block(kbase, k_dma, K_RING, 0);
     dma_block(vbase, v_dma, V_RING, 0);
     dma_block(kbase, k_dma, K_RING, 1);
@@ -501,14 +514,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         if constexpr (VARLEN) return key < lo_i || key > hi_i;
         else return !listed || (key >= N) || (CAUSAL && key > myq);
     };
+    bool seen_g = false;      // exact kernel: some key of the masked block is visible to this lane's row
     auto apply_mask = [&](f32x16& s, int g) {
         const int kbase_g = SPARSE ? sp_key(g) : kb0 + g * KB;
         const bool listed = SPARSE ? sp_member(g) : true;
+        bool any = false;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            s[r] = key_bad(kbase_g + 8 * (r >> 2) + 4 * hh + (r & 3), listed) ? -INFINITY : s[r];
+        for (int r = 0; r < 16; ++r) {
+            const bool bad = key_bad(kbase_g + 8 * (r >> 2) + 4 * hh + (r & 3), listed);
+            if constexpr (SAFE) any = any || !bad;
+            s[r] = bad ? -INFINITY : s[r];
+        }
+        if constexpr (SAFE) seen_g = any;
     };
-    bool mask_prev = false;   // the previous step's block was masked
+    bool mask_prev = false;   // exact kernel: the previous step's block was masked
+    bool keep_prev = false;   // ... and some row of the wave sees one of its keys
+    int n_saved = 0;          // exact kernel: masked blocks saved for the exact phase
 
     f32x16 o[4];          // O^T: 4 blocks of 32 head dims x 32 query columns
 #pragma unroll
@@ -536,46 +557,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     };
     // A masked block multiplies the V rows of keys some rows may not see by
     // zero weights, and 0 * NaN or 0 * inf is NaN in the matrix core.  Before
-    // its main loop each wave scans the V rows of its masked blocks in global
-    // memory; only a wave that finds a non-finite value there runs the loop
-    // variant in which masked blocks take pv_exact instead of pv.
-    // O^T += V^T P^T for masked block gb whose V holds a non-finite value, as
-    // the formula has it: each visible key adds p * v to its rows and no other,
-    // so a NaN or an infinity reaches exactly the rows that see its key.  The
-    // wave writes its rows' bf16 weights to its LDS area, then each lane walks
-    // the block's 32 keys and adds p * v (fp32) for those its row sees to its
-    // 64 output elements; element (db, r) of a lane is head dim
-    // 32 db + 8 (r / 4) + 4 hh + r % 4.  Slow, and only taken for such blocks.
-    auto pv_exact = [&](const u32x4 (&pw)[2], uint32_t vslot, int gb) {
-        char* wp = lds + RARE_OFF + wave * RARE_WAVE_BYTES + l32 * (KB * 2);   // this row's 32 weights
+    // its main loop each wave of the fast kernel scans the V rows of its
+    // masked blocks in global memory; a workgroup that finds a non-finite value
+    // there is redone by the exact kernel.  The exact kernel runs a masked
+    // block's product against a block of zeros instead of its V (same code
+    // path, so the loop keeps its registers) and saves the block's weights;
+    // after the loop it adds each saved block's terms p * v for the keys each
+    // row sees (V read from global memory), times the factor its weights have
+    // been rescaled by since.  So a NaN or an infinity reaches exactly the rows
+    // that see its key.
+    auto save_block = [&](const u32x4 (&pw)[2], int gb) {
+        char* base = lds + SAVE_OFF + wave * SAVE_WAVE_BYTES;
+        char* wp = base + n_saved * SAVE_P + l32 * (KB * 2);   // this row's 32 weights
         // keys 8a + 4hh + (0..3) of the row are accumulator registers 4a .. 4a+3
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const u32x4& w = pw[a >> 1];
             *(uint2*)(wp + 2 * (8 * a + 4 * hh)) = uint2{w[2 * (a & 1)], w[2 * (a & 1) + 1]};
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
-        __builtin_amdgcn_wave_barrier();
-        const int kbase_g = SPARSE ? sp_key(gb) : kb0 + gb * KB;
-        const bool listed = SPARSE ? sp_member(gb) : true;
-#pragma unroll 1
-        for (int j = 0; j < KB; ++j) {
-            if (key_bad(kbase_g + j, listed)) continue;
-            const float pj = (float)*(const __bf16*)(wp + 2 * j);
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    __builtin_amdgcn_sched_barrier(0);   // one 4-dim read in flight at a time
-                    const uint32_t chunk = (uint32_t)(4 * db + q);
-                    const uint32_t off = vslot + (uint32_t)j * ROW_BYTES +
-                                         ((chunk ^ (((uint32_t)j & 3u) << 2)) << 4) + 8u * (uint32_t)hh;
-                    const bf16x4 v4 = *(const bf16x4*)(lds + off);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) o[db][4 * q + rr] = fmaf(pj, (float)v4[rr], o[db][4 * q + rr]);
-                }
-        }
-        __builtin_amdgcn_wave_barrier();   // the area is rewritten only after every lane's reads
+        ((float*)(base + MAX_SAVED * SAVE_P))[n_saved * 64 + lane] = 1.0f;
+        if (lane == 0) ((int*)(base + MAX_SAVED * (SAVE_P + 256)))[n_saved] = gb;
+        ++n_saved;
     };
 
     // P = exp2(s*c - mb) rounded to bf16 in pairs (the B operand of the PV
@@ -632,19 +634,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         const bool use_p = !SPARSE || (g >= 1 && sp_member(g - 1));
         const bool mask_g = needs_mask(g);
         if (!FIRST && valid && use_g && mask_g) apply_mask(s, g);
-        if (use_n) scores(sn, KS);
-        if constexpr (!FIRST) {
-            if constexpr (SAFE) {
-                // exact kernel: masked blocks take the exact product
+        if constexpr (SAFE) {
+            // exact kernel: a masked block's product runs against the zero
+            // block, and its weights are saved when some row sees one of its keys
+            if constexpr (!FIRST)
                 if (use_p) {
-                    if (mask_prev) pv_exact(pp, VS, g - 1);
-                    else pv(pp, VS);
+                    pv(pp, mask_prev ? (uint32_t)ZERO_OFF : VS);
+                    if (mask_prev && keep_prev && n_saved < MAX_SAVED) save_block(pp, g - 1);
                 }
-            } else if (use_p) {
-                pv(pp, VS);
-            }
+            mask_prev = valid && use_g && mask_g;
+            keep_prev = mask_prev && __builtin_amdgcn_ballot_w64(seen_g) != 0;
+            if (use_n) scores(sn, KS);
+        } else {
+            if (use_n) scores(sn, KS);
+            if constexpr (!FIRST)
+                if (use_p) pv(pp, VS);
         }
-        if constexpr (SAFE) mask_prev = mask_g;
         if (!use_g) return;
         float ls, lbs;
         probs(s, pc, ls, lbs);
@@ -668,6 +673,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            if constexpr (SAFE) {
+                float* fac = (float*)(lds + SAVE_OFF + wave * SAVE_WAVE_BYTES + MAX_SAVED * SAVE_P);
+                for (int i = 0; i < n_saved; ++i) fac[i * 64 + lane] *= alpha;
+            }
             probs(s, pc, ls, lbs);
             if (m == -INFINITY && live) mb = -INFINITY;
         }
@@ -769,6 +778,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb, sa, pa, pb);
         wait_dma();
         __syncthreads();
+    }
+
+    // ---- exact kernel: the saved masked blocks' terms p * v, for the keys each
+    // row sees, in fp32 (V from global memory; the wave's own LDS area holds
+    // the weights and the factors they have been rescaled by since).  Output
+    // element (db, r) of a lane is head dim 32 db + 8 (r / 4) + 4 hh + r % 4.
+    if constexpr (SAFE) {
+        const char* base = lds + SAVE_OFF + wave * SAVE_WAVE_BYTES;
+        const int end = VARLEN ? s1 : N;
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)(end - kb0) * ROW_BYTES);
+        for (int i = 0; i < n_saved; ++i) {
+            const int gb = __builtin_amdgcn_readfirstlane(((const int*)(base + MAX_SAVED * (SAVE_P + 256)))[i]);
+            const float fac = ((const float*)(base + MAX_SAVED * SAVE_P))[i * 64 + lane];
+            const char* wp = base + i * SAVE_P + l32 * (KB * 2);
+            const int kbase_g = SPARSE ? sp_key(gb) : kb0 + gb * KB;
+            const bool listed = SPARSE ? sp_member(gb) : true;
+#pragma unroll 1
+            for (int j = 0; j < KB; ++j) {
+                const int key = kbase_g + j;
+                if (key_bad(key, listed)) continue;
+                const float pj = (float)*(const __bf16*)(wp + 2 * j) * fac;
+                const uint32_t row_off = (uint32_t)(key - kb0) * ROW_BYTES;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t off = row_off + 2u * (uint32_t)(32 * db + 8 * q + 4 * hh);
+                        const bf16x4 v4 = __builtin_bit_cast(
+                            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0));
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            o[db][4 * q + rr] = fmaf(pj, (float)v4[rr], o[db][4 * q + rr]);
+                    }
+            }
+        }
     }
 
     // ---- epilogue: O = O^T / sum bf16(p) (bf16, round to nearest even),

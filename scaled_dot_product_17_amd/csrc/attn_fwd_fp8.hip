@@ -33,11 +33,18 @@
 //     taken by one more MFMA against a tile of ones (exact fp32 sums of
 //     products), so the rounding of a dominant weight cancels in O; the LSE
 //     uses the fp32 weights;
-//   * softmax in base 2 against a lagging reference m: e = 2^(s*c - m*c + PS),
-//     c = |scale*dq*dk|*log2(e).  The weights are kept at most 2^8.75 < 448 (the
-//     largest e4m3 value): a lane whose 32 weights of a block sum above 448 checks
-//     its largest one, and only when some weight could pass 2^8.75 does the wave
-//     move every row to its running max (rare, wave-uniform branch).
+//   * softmax in base 2 against a lagging reference m: e = 2^(s*c - m*c),
+//     c = |scale*dq*dk|*log2(e).  A row's weights of a block are multiplied by
+//     the power of two 2^k that puts their largest one in (224, 448], the top
+//     binade of e4m3 below its largest value, then rounded to e4m3; the matrix
+//     core's E8M0 scale of the P operand applies 2^-k back, exactly.  In the
+//     32x32x64 operand layout bytes 0-15 of both lanes of a column form the
+//     first 32-value k block and bytes 16-31 the second (checked on the GPU),
+//     and the scale of block b comes from lane column + 32b; both lanes of a
+//     row hold the same k.  No weight can overflow e4m3 and none is rounded
+//     more coarsely than the row's largest weight of the block allows.  The
+//     reference only moves (rare, wave-uniform branch) when a lane's fp32
+//     block sum passes 2^64 or is not finite.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,11 +71,22 @@ constexpr int BLK_BYTES = KB * ROW8;         // 8 KiB per K or V block
 constexpr int K_RING = 0;                    // LDS: a ring of 4 K blocks, then 4 V blocks
 constexpr int V_RING = 4 * BLK_BYTES;
 constexpr int LDS_BYTES = 8 * BLK_BYTES;     // 64 KiB
-constexpr float PS = 4.0f;                   // weights carry a factor 2^PS (room below 448)
-constexpr float SUM_CHECK = 448.0f;          // a lane's block sum above this checks its max
-constexpr float MAX_EXP = 8.75f;             // log2 of the largest weight allowed
+constexpr float LOG2_448 = 8.80735492205760410f;   // log2 of the largest e4m3 value
+constexpr float K_CLAMP = 100.0f;            // |k| of a lane's weight scale 2^k (E8M0: 127 - k)
+constexpr float MOVE_SUM = 18446744073709551616.0f;   // 2^64: a lane's block sum above this moves the reference
+// Exact kernel (a NaN code in a masked block's V): a zero block, and per wave up
+// to MAX_SAVED masked blocks' weights (32 rows x 64 keys, e4m3 times 2^-k,
+// exact in bf16), the factor each block's weights have been rescaled by since
+// (one per lane) and its index.  A wave has at most two masked blocks with a
+// visible key (its causal diagonal block, the ragged last block).
+constexpr int MAX_SAVED = 2;
+constexpr int SAVE_P = 32 * KB * 2;
+constexpr int SAVE_WAVE_BYTES = MAX_SAVED * (SAVE_P + 64 * 4) + 16;
+// Mark the fast kernel leaves in the first output row of a workgroup it hands
+// to the exact kernel: eight signalling-NaN bf16 codes (0x7F81 .. 0x7F88),
+// which arithmetic never produces (every NaN it makes is quiet).
+__constant__ const uint32_t NF_MARK[4] = {0x7F827F81u, 0x7F847F83u, 0x7F867F85u, 0x7F887F87u};
 constexpr int ONE4 = 0x38383838;             // four e4m3 ones
-constexpr float LN2 = 0.693147180559945309f;
 
 struct Params {
     const uint8_t* q;
@@ -113,15 +131,25 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
     // format 0 (e4m3) for both operands, block scales 127 = 2^0
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// The same with an E8M0 scale byte for B.  B's k extent of 64 is two blocks
+// of 32: block b is bytes 16b .. 16b+15 of lanes L and L+32 (column L % 32),
+// and lane L + 32b supplies its scale (byte 0 of sb).
+__device__ __forceinline__ f32x16 mfma8_sb(const i32x8& a, const i32x8& b, const f32x16& c, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
 
 // NW waves per workgroup (8, or 4 for short sequences: twice the workgroups,
-// two per CU, not tied by one barrier)
-template <bool CAUSAL, int NW>
+// two per CU, not tied by one barrier).  SAFE = false: the fast kernel;
+// SAFE = true: the exact kernel, which redoes only the workgroups the fast
+// kernel marked (a NaN code in the V rows of a masked block; see NF_MARK).
+template <bool CAUSAL, int NW, bool SAFE>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p) {
     constexpr int BRW = 32 * NW;      // query rows of this workgroup
     constexpr int NTH = NW * 64;
     constexpr int DPW = 8 / NW;       // 8-row DMA instructions per wave per key block
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    constexpr int ZERO_OFF = LDS_BYTES;                 // exact kernel: a block of zeros
+    constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;      // exact kernel: per-wave saved blocks
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -157,6 +185,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
 
     const size_t q_panel = ((size_t)b * p.Hq + h) * (size_t)N * HD;     // elements (bytes for Q8)
     const size_t kv_panel = ((size_t)b * p.Hkv + kvh) * (size_t)N * HD;
+    uint16_t* const mark = p.o + q_panel + (size_t)q0 * HD;   // the workgroup's first output row
+    if constexpr (SAFE) {
+        // only the workgroups the fast kernel marked (every thread reads the
+        // same 16 bytes, so the exit is workgroup-uniform)
+        const u32x4 w = *(const u32x4*)mark;
+        if (w[0] != NF_MARK[0] || w[1] != NF_MARK[1] || w[2] != NF_MARK[2] || w[3] != NF_MARK[3]) return;
+    }
 
     // key blocks: n_blk_wg streamed through LDS, n_blk used by this wave (a
     // causal wave stops at the block holding its last row's diagonal)
@@ -224,6 +259,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
             *(u32x4*)(lds + 16 * (tid + NTH * i)) = z;
         __syncthreads();
     }
+    if constexpr (SAFE) {
+        // the zero block masked products run against (first read after a barrier)
+#pragma unroll
+        for (int i = 0; i < BLK_BYTES / (16 * NTH); ++i)
+            *(u32x4*)(lds + ZERO_OFF + 16 * (tid + NTH * i)) = u32x4{0u, 0u, 0u, 0u};
+    }
     dma_block(kbase, k_dma, K_RING, 0);
     dma_block(vbase, v_dma, V_RING, 0);
     dma_block(kbase, k_dma, K_RING, 1);
@@ -273,27 +314,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
     auto needs_mask = [&](int g) {
         return (CAUSAL && g * KB + KB - 1 > wq0) || (g * KB + KB > N);
     };
+    bool seen_g = false;   // exact kernel: some key of the masked block is visible to this lane's row
     auto apply_mask = [&](f32x16 (&s)[2], int g) {
+        bool any = false;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = g * KB + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
                 const bool bad = (key >= N) || (CAUSAL && key > myq);
+                if constexpr (SAFE) any = any || !bad;
                 s[sb][r] = bad ? -INFINITY : s[sb][r];
             }
+        if constexpr (SAFE) seen_g = any;
     };
 
     f32x16 o[4];          // O^T: 4 blocks of 32 head dims x 32 query columns
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     f32x16 ol = {};       // every row: sum of the e4m3 weights applied (O's divisor)
+    const bool live = myq < N;   // a row that is written (padding rows past N are not)
     float m = -INFINITY;  // reference: raw score q8.k8 of this lane's row
-    float mb = 0.f;       // m * c - PS
+    float mb = 0.f;       // m * c (-inf while the row has seen no finite score)
     float l = 0.f;        // this lane's partial sum of the fp32 weights (the LSE)
 
-    // O^T += V^T P^T for one block: A = V^T bytes in the key order of P's bytes
-    auto pv = [&](const i32x8& pw, uint32_t vslot) {
+    // O^T += V^T P^T for one block: A = V^T bytes in the key order of P's
+    // bytes; sb is the E8M0 byte of the row's weight scale 2^-k
+    auto pv = [&](const i32x8& pw, int sb, uint32_t vslot) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
             const i32x2 r0 = lds_read_tr8(lds, vslot + v_rd[db]);
@@ -301,29 +348,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
             const i32x2 r2 = lds_read_tr8(lds, vslot + v_rd[db] + 32 * ROW8);
             const i32x2 r3 = lds_read_tr8(lds, vslot + v_rd[db] + 48 * ROW8);
             const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-            o[db] = mfma8(a, pw, o[db]);
+            o[db] = mfma8_sb(a, pw, o[db], sb);
         }
-        ol = mfma8(ones, pw, ol);
-    };
-    // weights e = 2^(s*c - mb) as e4m3, byte 16*sb + r = key 32sb + 8(r/4) + 4hh + r%4
-    auto probs = [&](const f32x16 (&s)[2], i32x8& pw, float& ls) {
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 0], c, -mb));
-                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 1], c, -mb));
-                const float e2 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 2], c, -mb));
-                const float e3 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 3], c, -mb));
-                a0 += e0 + e2;
-                a1 += e1 + e3;
-                // both halves of the dword are written: the old value needs no clearing
-                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pw[4 * sb + w], false);
-                pk = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, pk, true);
-                pw[4 * sb + w] = pk;
-            }
-        ls = a0 + a1;
+        ol = mfma8_sb(ones, pw, ol, sb);
     };
     auto lane_max = [&](const f32x16 (&s)[2]) {
         float mx = fmaxf(s[0][0], s[1][0]);
@@ -331,50 +358,166 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
         return mx;
     };
-
-    // Key block g (valid while g < n_blk; g == n_blk only drains the last PV).
+    // weights e = 2^(s*c - mb) times 2^k, as e4m3: byte 16*sb + r = key
+    // 32sb + 8(r/4) + 4hh + r%4, and k = floor(log2(448) - the row's largest
+    // exponent in the block) puts the row's largest weight of the block in
+    // (224, 448] (k clamped to +-100 for blocks far below the reference, and
+    // for -inf or NaN scores).  ls = the fp32 weights' sum without the 2^k;
+    // sk = the E8M0 byte 127 - k (both halves of the block, both lanes);
+    // mx = the row's largest score in the block.
+    auto probs = [&](const f32x16 (&s)[2], i32x8& pw, float& ls, int& sk, float& mx) {
+        mx = wave_swap_max(lane_max(s));   // both lanes of the row
+        const float kf = fminf(fmaxf(__builtin_floorf(LOG2_448 - fmaf(mx, c, -mb)), -K_CLAMP), K_CLAMP);
+        const float mbk = mb - kf;
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 0], c, -mbk));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 1], c, -mbk));
+                const float e2 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 2], c, -mbk));
+                const float e3 = __builtin_amdgcn_exp2f(fmaf(s[sb][4 * w + 3], c, -mbk));
+                a0 += e0 + e2;
+                a1 += e1 + e3;
+                // both halves of the dword are written: the old value needs no clearing
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pw[4 * sb + w], false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, pk, true);
+                pw[4 * sb + w] = pk;
+            }
+        const int k = (int)kf;
+        ls = ldexpf(a0 + a1, -k);
+        sk = 127 - k;
+    };
+    // A masked block multiplies the V rows of keys some rows may not see by
+    // zero weights, and 0 * NaN is NaN in the matrix core.  Before its main
+    // loop each wave of the fast kernel scans the V rows of its masked blocks
+    // in global memory; a workgroup that finds a NaN code there is redone by
+    // the exact kernel.  The exact kernel runs a masked block's product
+    // against a block of zeros instead of its V (O's divisor still counts its
+    // weights) and saves the weights (e4m3 times 2^-k, exact in bf16); after
+    // the loop it adds each saved block's terms p * v for the keys each row
+    // sees (V from global memory), times the factor its weights have been
+    // rescaled by since.
+    int n_saved = 0;
+    auto save_block = [&](const i32x8& pw, int sk, int gb) {
+        char* base = lds + SAVE_OFF + wave * SAVE_WAVE_BYTES;
+        char* wp = base + n_saved * SAVE_P + l32 * (KB * 2);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float unscale = ldexpf(1.0f, sk - 127);
+                const int d = pw[4 * sb + w];   // keys 32sb + 8w + 4hh + 0..3
+                const bf16x2 lo = {(__bf16)(__builtin_amdgcn_cvt_f32_fp8(d, 0) * unscale),
+                                   (__bf16)(__builtin_amdgcn_cvt_f32_fp8(d, 1) * unscale)};
+                const bf16x2 hi = {(__bf16)(__builtin_amdgcn_cvt_f32_fp8(d, 2) * unscale),
+                                   (__bf16)(__builtin_amdgcn_cvt_f32_fp8(d, 3) * unscale)};
+                *(uint2*)(wp + 2 * (32 * sb + 8 * w + 4 * hh)) =
+                    uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            }
+        ((float*)(base + MAX_SAVED * SAVE_P))[n_saved * 64 + lane] = 1.0f;
+        if (lane == 0) ((int*)(base + MAX_SAVED * (SAVE_P + 256)))[n_saved] = gb;
+        ++n_saved;
+    };
+    bool mask_prev = false;   // exact kernel: the previous step's block was masked
+    bool keep_prev = false;   // ... and some row of the wave sees one of its keys
     auto step = [&](auto first_t, auto ks_t, auto vs_t, int g, f32x16 (&s)[2], f32x16 (&sn)[2],
-                    const i32x8& pp, i32x8& pc) {
+                    const i32x8& pp, int sp, i32x8& pc, int& sc) {
         constexpr bool FIRST = decltype(first_t)::value;
         constexpr uint32_t KS = K_RING + decltype(ks_t)::value * BLK_BYTES;
         constexpr uint32_t VS = V_RING + decltype(vs_t)::value * BLK_BYTES;
         const bool valid = g < n_blk;
-        if (!FIRST && valid && needs_mask(g)) apply_mask(s, g);
-        scores(sn, KS);
-        if constexpr (!FIRST) pv(pp, VS);
-        float ls;
-        probs(s, pc, ls);
-        asm volatile("" : "+v"(pc), "+v"(ls));
-        if (valid && __builtin_amdgcn_ballot_w64(!(ls <= SUM_CHECK)) != 0) {
-            // some lane's weights sum past 448: check the largest weights
-            const float mx = lane_max(s);
-            if (__builtin_amdgcn_ballot_w64(!(fmaf(mx, c, -mb) <= MAX_EXP)) != 0) {
-                const float m_new = fmaxf(m, wave_swap_max(mx));
-                const float alpha = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
-                m = m_new;
-                mb = (m == -INFINITY) ? -PS : m * c - PS;
-                l *= alpha;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) ol[r] *= alpha;
-                probs(s, pc, ls);
+        const bool mask_g = needs_mask(g);
+        if (!FIRST && valid && mask_g) apply_mask(s, g);
+        if constexpr (SAFE) {
+            // exact kernel: a masked block's product runs against the zero
+            // block, and its weights are saved when some row sees one of its keys
+            if constexpr (!FIRST) {
+                pv(pp, sp, mask_prev ? (uint32_t)ZERO_OFF : VS);
+                if (mask_prev && keep_prev && n_saved < MAX_SAVED) save_block(pp, sp, g - 1);
             }
+            mask_prev = valid && mask_g;
+            keep_prev = mask_prev && __builtin_amdgcn_ballot_w64(seen_g) != 0;
+            scores(sn, KS);
+        } else {
+            scores(sn, KS);
+            if constexpr (!FIRST) pv(pp, sp, VS);
+        }
+        float ls, mx;
+        probs(s, pc, ls, sc, mx);
+        asm volatile("" : "+v"(pc), "+v"(ls), "+v"(sc), "+v"(mx));
+        // While a row has seen no finite score, mb is -inf, so any score makes
+        // its sum inf or NaN and takes this branch, which moves m to the first
+        // finite score and weighs the rest of the block against it.
+        if (valid && __builtin_amdgcn_ballot_w64(!(ls <= MOVE_SUM)) != 0) {
+            const float m_new = fmaxf(m, wave_swap_max(mx));
+            const float alpha = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
+            m = m_new;
+            mb = (m == -INFINITY) ? 0.f : m * c;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ol[r] *= alpha;
+            if constexpr (SAFE) {
+                float* fac = (float*)(lds + SAVE_OFF + wave * SAVE_WAVE_BYTES + MAX_SAVED * SAVE_P);
+                for (int i = 0; i < n_saved; ++i) fac[i * 64 + lane] *= alpha;
+            }
+            probs(s, pc, ls, sc, mx);
+            if (m == -INFINITY && live) mb = -INFINITY;
         }
         if (valid) l += ls;
     };
 
     f32x16 sa[2], sb2[2];   // scores of even / odd key blocks
     i32x8 pa = {}, pb = {};  // e4m3 weights of even / odd key blocks
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q loads and the first DMA done
+    int ka = 127, kb = 127;  // their rows' E8M0 scale bytes (2^0 until set)
+    // fast kernel: the V rows of the wave's masked blocks (a prefix and a
+    // suffix of its blocks: causal diagonal, panel end), in range, checked in
+    // global memory for a NaN code (e4m3 has no infinity)
+    uint32_t nf_bits = 0u;
+    if (!SAFE && n_blk > 0) {
+        auto vcheck = [&](int g) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(vbase + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW8);
+#pragma unroll
+            for (int i = 0; i < BLK_BYTES / 1024; ++i) {
+                const u32x4 x = buf_load16(r, (uint32_t)(16 * lane + 1024 * i));
+                // a byte with all seven low bits set (0x7F, 0xFF) carries into its top bit
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nf_bits |= (x[e] & 0x7F7F7F7Fu) + 0x01010101u;
+            }
+        };
+        int g = 0;
+        for (; g < n_blk && needs_mask(g); ++g) vcheck(g);
+        for (int h2 = n_blk - 1; h2 >= g && needs_mask(h2); --h2) vcheck(h2);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q loads, the first DMA and the check done
+    // the waves' answers meet in V slot 3 (not refilled before tile 1); a
+    // workgroup with a NaN code in a masked block's V marks its first output
+    // row and leaves the rows to the exact kernel
+    uint32_t* const nf_wave = (uint32_t*)(lds + V_RING + 3 * BLK_BYTES);
+    if constexpr (!SAFE) {
+        const bool nf = __builtin_amdgcn_ballot_w64((nf_bits & 0x80808080u) != 0u) != 0;
+        if (lane == 0) nf_wave[wave] = nf ? 1u : 0u;
+    }
     __syncthreads();
+    if constexpr (!SAFE) {
+        uint32_t any = 0u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any |= nf_wave[w];
+        if (any != 0u) {
+            if (tid == 0) *(u32x4*)mark = u32x4{NF_MARK[0], NF_MARK[1], NF_MARK[2], NF_MARK[3]};
+            return;
+        }
+    }
     if (n_blk > 0) {
         scores(sa, K_RING);
         if (needs_mask(0)) apply_mask(sa, 0);
         m = wave_swap_max(lane_max(sa));
-        mb = (m == -INFINITY) ? -PS : m * c - PS;
+        mb = (m == -INFINITY) ? (live ? -INFINITY : 0.f) : m * c;
     }
     __syncthreads();   // K slot 0 is refilled in the first tile
 
@@ -395,26 +538,57 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
         dma_block(vbase, v_dma, V_RING, 2 * j + 2);
     };
     refill(0);
-    if (0 <= n_blk) step(std::true_type{}, I1{}, I3{}, 0, sa, sb2, pb, pa);
-    if (1 <= n_blk) step(F{}, I2{}, I0{}, 1, sb2, sa, pa, pb);
+    if (0 <= n_blk) step(std::true_type{}, I1{}, I3{}, 0, sa, sb2, pb, kb, pa, ka);
+    if (1 <= n_blk) step(F{}, I2{}, I0{}, 1, sb2, sa, pa, ka, pb, kb);
     wait_dma();
     __syncthreads();
     for (int j = 1; j < n_tiles; j += 2) {
         refill(j);
-        if (2 * j <= n_blk) step(F{}, I3{}, I1{}, 2 * j, sa, sb2, pb, pa);
-        if (2 * j + 1 <= n_blk) step(F{}, I0{}, I2{}, 2 * j + 1, sb2, sa, pa, pb);
+        if (2 * j <= n_blk) step(F{}, I3{}, I1{}, 2 * j, sa, sb2, pb, kb, pa, ka);
+        if (2 * j + 1 <= n_blk) step(F{}, I0{}, I2{}, 2 * j + 1, sb2, sa, pa, ka, pb, kb);
         wait_dma();
         __syncthreads();
         if (j + 1 >= n_tiles) break;
         refill(j + 1);
-        if (2 * j + 2 <= n_blk) step(F{}, I1{}, I3{}, 2 * j + 2, sa, sb2, pb, pa);
-        if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb2, sa, pa, pb);
+        if (2 * j + 2 <= n_blk) step(F{}, I1{}, I3{}, 2 * j + 2, sa, sb2, pb, kb, pa, ka);
+        if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb2, sa, pa, ka, pb, kb);
         wait_dma();
         __syncthreads();
     }
 
+    // ---- exact kernel: the saved masked blocks' terms p * v, for the keys each
+    // row sees, in fp32.  Output element (db, r) of a lane is head dim
+    // 32 db + 8 (r / 4) + 4 hh + r % 4.
+    if constexpr (SAFE) {
+        const char* base = lds + SAVE_OFF + wave * SAVE_WAVE_BYTES;
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)N * ROW8);
+        for (int i = 0; i < n_saved; ++i) {
+            const int gb = __builtin_amdgcn_readfirstlane(((const int*)(base + MAX_SAVED * (SAVE_P + 256)))[i]);
+            const float fac = ((const float*)(base + MAX_SAVED * SAVE_P))[i * 64 + lane];
+            const char* wp = base + i * SAVE_P + l32 * (KB * 2);
+#pragma unroll 1
+            for (int j = 0; j < KB; ++j) {
+                const int key = gb * KB + j;
+                if ((key >= N) || (CAUSAL && key > myq)) continue;
+                const float pj = (float)*(const __bf16*)(wp + 2 * j) * fac;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int v4 = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                            vr, (uint32_t)key * ROW8 + (uint32_t)(32 * db + 8 * q + 4 * hh), 0, 0);
+                        o[db][4 * q + 0] = fmaf(pj, __builtin_amdgcn_cvt_f32_fp8(v4, 0), o[db][4 * q + 0]);
+                        o[db][4 * q + 1] = fmaf(pj, __builtin_amdgcn_cvt_f32_fp8(v4, 1), o[db][4 * q + 1]);
+                        o[db][4 * q + 2] = fmaf(pj, __builtin_amdgcn_cvt_f32_fp8(v4, 2), o[db][4 * q + 2]);
+                        o[db][4 * q + 3] = fmaf(pj, __builtin_amdgcn_cvt_f32_fp8(v4, 3), o[db][4 * q + 3]);
+                    }
+            }
+        }
+    }
+
     // ---- epilogue: O = dv * O^T / sum(e4m3 weights) in bf16;
-    // LSE = m*|scale dq dk| + ln(sum of fp32 weights) - PS*ln 2
+    // LSE = m*|scale dq dk| + ln(sum of fp32 weights); a row whose scores are
+    // all -inf (or NaN) gets NaN, as the formula gives
     const float l_tot = wave_swap_sum(l);
     const float inv = p.dv / ol[0];
     if (myq < N) {
@@ -430,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
             }
         if (p.lse != nullptr && hh == 0) {
             const size_t li = ((size_t)b * p.Hq + h) * (size_t)N + myq;
-            p.lse[li] = m * p.lse_scale + (logf(l_tot) - PS * LN2);
+            p.lse[li] = m == -INFINITY ? __builtin_nanf("") : m * p.lse_scale + logf(l_tot);
         }
     }
 }
@@ -497,12 +671,24 @@ extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* 
     p.dv = descale_v;
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid((unsigned)total);
+    // the fast kernel, then the exact kernel over the same grid: it redoes the
+    // workgroups the fast kernel marked and every other workgroup exits at once
     if (short_n) {
-        if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4>), grid, dim3(256), 0, s, p);
+        if (causal) {
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4, false>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4, true>), grid, dim3(256), 0, s, p);
+        } else {
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4, false>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4, true>), grid, dim3(256), 0, s, p);
+        }
     } else {
-        if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8>), grid, dim3(512), 0, s, p);
-        else hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8>), grid, dim3(512), 0, s, p);
+        if (causal) {
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8, false>), grid, dim3(512), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8, true>), grid, dim3(512), 0, s, p);
+        } else {
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8, false>), grid, dim3(512), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8, true>), grid, dim3(512), 0, s, p);
+        }
     }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -125,13 +125,22 @@ def bwd_check(m, what=""):
 
 
 # ---------------------------------------------------------------------------
-# FP8 (e4m3) forward bar, derived from the arithmetic of the path:
-#   * each softmax weight is rounded to e4m3 after scaling so that the row's
-#     reference weight is 2^4: relative rounding 2^-4 in the normal range and
-#     an absolute rounding of at most 2^-10 * 2^-4 = 2^-14 (in units of the
-#     row's largest weight) below it -> the oracle's error-scale sum with
-#     (w_rel, w_floor) = (2^-4 + score_err, 2^-14); O is normalised by the
-#     sum of the rounded weights, which is what that sum bounds to first order;
+# FP8 (e4m3) forward accuracy contract.  It follows from the e4m3 format and
+# one stated scaling rule, not from any kernel's choices:
+#   * scaling rule: the softmax weights of a row are rounded to e4m3 in groups
+#     of consecutive keys, each group multiplied first by the power of two that
+#     puts its largest weight in (224, 448]: the top binade of e4m3 below its largest
+#     finite value 448, i.e. the largest placement a power-of-two scale can
+#     guarantee without overflow.  Power-of-two scales are exact, and the
+#     matrix core takes them back exactly (per-lane E8M0 operand scales);
+#   * e4m3 keeps 3 mantissa bits in its normal range (down to 2^-6), so a
+#     rounded weight is within 2^-4 of itself, relatively; below 2^-6 the
+#     spacing is 2^-9, so within 2^-10 absolutely, in scaled units, i.e.
+#     within 2^-10 / 224 of its group's largest weight, and so of the row's
+#     largest weight -> the oracle's error-scale sum with
+#     (w_rel, w_floor) = (2^-4 + score_err, 2^-10 / 224); O is normalised by
+#     the sum of the rounded weights, which is what that sum bounds to first
+#     order;
 #   * the FP8 matrix core accumulates the 64-term products with an error
 #     below 2^-14 of sum |q_d k_d| <= 2^-14 ||q|| ||k|| (measured on gfx950 at
 #     about 2^-18.6); times |scale dq dk| this is score_err (natural-log units),
@@ -150,7 +159,7 @@ def bwd_check(m, what=""):
 # |err| / (rms + 2^-9 |O| + 2^-40) must stay below FP8_MEAN_Z = 1 (zero-mean
 # roundings give about 0.5 or less; a misplaced weight or key gives >> 1).
 FP8_W_REL = 2.0 ** -4
-FP8_W_FLOOR = 2.0 ** -14
+FP8_W_FLOOR = 2.0 ** -10 / 224.0
 FP8_KAPPA = 1.3
 FP8_MFMA_REL = 2.0 ** -14
 FP8_MEAN_Z = 1.0

@@ -153,3 +153,57 @@ def test_nonfinite_varlen(case, causal):
     n = check_nonfinite(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref,
                         f"{lens} window={window} causal={causal}")
     assert n > 0
+
+
+FP8_SHAPES = [(1, 4, 2, 200), (1, 2, 1, 4200), (2, 4, 4, 1000)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "b%d_hq%d_hkv%d_n%d" % s)
+def test_nonfinite_fp8(shape, causal):
+    """e4m3 NaN codes (0x7F, 0xFF; the format has no infinity) planted in Q, K
+    and V, one inside a causal diagonal 64-key block: the NaN pattern equals
+    the FP8 oracle's; finite rows meet the FP8 contract (tests/parity.py)."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, Hq, Hkv, N = shape
+    say(f"[nonfinite fp8] {shape} causal={causal}")
+    d = synth.FP8_DESCALE
+    q8 = synth.normal_e4m3(23000 + N, (B, Hq, N, 128), d)
+    k8 = synth.normal_e4m3(23001 + N, (B, Hkv, N, 128), d)
+    v8 = synth.normal_e4m3(23002 + N, (B, Hkv, N, 128), d)
+    q8[0, min(1, Hq - 1), 37 % N, 5] = 0x7F
+    k8[0, 0, 70 % N, 3] = 0xFF
+    v8[0, Hkv - 1, min(64 + 40, N - 1), 9] = 0x7F      # keys 64..103 of that block are masked for rows < 104
+    v8[0, 0, N - 1, 0] = 0xFF
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).cuda()
+
+    o, lse = sdpa.fwd_fp8(up(q8), up(k8), up(v8), d, d, d, causal=causal, scale=SCALE)
+    torch.cuda.synchronize()
+    o = bf16_to_np(o)
+    lse = lse.cpu().numpy()
+    # the score error bound over the rows with no NaN code (a NaN row's bound is moot)
+    qv = oracle.e4m3_decode(q8.reshape(-1, 128))
+    kv = oracle.e4m3_decode(k8.reshape(-1, 128))
+    serr = parity.fp8_score_err(qv[np.isfinite(qv).all(-1)], kv[np.isfinite(kv).all(-1)], SCALE, d, d)
+    assert np.isfinite(serr)
+    o_ref, lse_ref, mag, rms = oracle.attn_fp8_ref(q8, k8, v8, d, d, d, causal, SCALE,
+                                                   mags=parity.fp8_mags(serr))
+    for name, g, r in (("O", o, o_ref), ("LSE", lse, lse_ref)):
+        diff = np.argwhere(np.isnan(np.asarray(g, np.float64)) != np.isnan(r))
+        assert diff.size == 0, f"FP8 {name} NaN pattern differs at {diff[:6].tolist()}"
+        assert not np.isinf(np.asarray(g, np.float64)).any() and not np.isinf(r).any()
+    ok = np.isfinite(o_ref).all(-1) & np.isfinite(lse_ref)
+    assert (~ok).any(), "the planted codes must reach some rows"
+    m = parity.fp8_compare(o[ok], lse[ok], o_ref[ok], lse_ref[ok], mag[ok], rms[ok], serr, N)
+    say(f"  fp8 {shape} causal={causal}: {int((~ok).sum())} NaN rows; finite rows {m}")
+    parity.fp8_check(m, f"fp8 nonfinite {shape} causal={causal}")
+    # elements of rows that meet a V NaN only in some columns: the other columns finite
+    part = ~ok & np.isfinite(lse_ref)
+    if part.any():
+        fin = np.isfinite(o_ref[part])
+        err = np.abs(np.asarray(o[part], np.float64)[fin] - o_ref[part][fin])
+        tol = 2.0 ** -8 * np.abs(o_ref[part][fin]) + parity.FP8_KAPPA * mag[part][fin]
+        assert np.all(err <= tol), "finite elements of rows with a NaN column"
