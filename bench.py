@@ -82,6 +82,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baselines."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    import oracle
+    return oracle.default_threads()
+
+
+def pmap(fn, items, threads):
+    """fn over items on `threads` host threads (the oracle's C calls release the
+    GIL, so disjoint pieces of a sample run on all cores)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        return list(ex.map(fn, items))
+
+
 def kernel_hash(src: str = KERNEL_SRC) -> str:
     with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -105,6 +130,35 @@ def stored_traffic(workload: str, kernel: str = "attn_fwd", src: str = KERNEL_SR
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def profile_record(workload: str, tag: str, src: str, work: float, peak: float,
+                   unit_scale: float = 1e12):
+    """The committed rocprofv3 kernel-trace summary of a workload, if it was taken
+    on the current kernel source: its file, dominant kernel, that kernel's mean
+    duration, and the rate and fraction of peak that duration gives for `work`
+    (flops or bytes per launch; rate = work / s / unit_scale); else None."""
+    path = os.path.join(PROFILES, f"kernel_trace_{tag}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#")):
+                key, val = ln.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash(src):
+        return None
+    try:
+        ms = float(kv["dominant_kernel_avg_ns"]) * 1e-6
+        step_ms = float(kv.get("step_kernels_avg_ns", kv["dominant_kernel_avg_ns"])) * 1e-6
+    except (KeyError, ValueError):
+        return None
+    rate = work / (ms * 1e-3) / unit_scale
+    return {"file": os.path.relpath(path, ROOT), "kernel": kv.get("dominant_kernel"),
+            "kernel_ms_mean": round(ms, 5), "step_kernels_ms_mean": round(step_ms, 5),
+            "achieved": round(rate, 2), "frac": round(rate / peak, 4),
+            "bench_in_same_session": kv.get("bench_in_same_session")}
 
 
 def upload(a):
@@ -163,7 +217,8 @@ def cpu_baseline(w, target_s: float = 12.0):
     dt, fl = run(n0)
     n = int(min(total_rows, max(n0, n0 * target_s / max(dt, 1e-3))))
     dt, fl = run(n)
-    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{n} random query rows of {w.name} (all {w.N} keys each, fp64), "
                       f"{dt:.1f} s"}
 
@@ -313,7 +368,7 @@ def cpu_baseline_bwd(w):
     dt = time.perf_counter() - t0
     pairs = g * (w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N)
     return {"value": pairs * 10 * w.D / dt / 1e12, "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": f"full fp64 backward of batch 0, K/V head 0 ({g} query head(s), all "
                       f"{w.N} rows and keys) of {w.name}, {dt:.1f} s"}
 
@@ -347,7 +402,9 @@ def main_bwd(args, w):
                      "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": f"attn_bwd_{dom}_kernel",
                      "launch_ms_mean": round(t[dom], 4),
-                     "launch_ms_p10_p90": [round(x, 4) for x in t[f"{dom}_p10_p90"]]},
+                     "launch_ms_p10_p90": [round(x, 4) for x in t[f"{dom}_p10_p90"]],
+                     "profile": profile_record(w.name, "attn_bwd", BWD_SRC, kflops["dkdv"],
+                                               PEAK_TFLOPS)},
         "kernels_ms": {"attn_bwd_dq_kernel": round(t["dq"], 4),
                        "attn_bwd_dkdv_kernel": round(t["dkdv"], 4)},
         "cpu_baseline": None,
@@ -418,20 +475,39 @@ def time_decode(w, steps, warmup):
 
 
 def cpu_baseline_decode(w, target_s: float = 10.0):
-    """The decode oracle as it stands (one thread): rate in the metric's unit
+    """The decode oracle as it stands, on all host cores (one call per
+    (batch entry, K/V head) slice at a time per core): rate in the metric's unit
     (algorithmic bytes of the workload per second)."""
     import oracle
     oracle.build(force=False)
     q, k, v = w.generate()
+    threads = host_threads()
+    g = w.H_q // w.H_kv
+    slices = [(b, kv) for b in range(w.B) for kv in range(w.H_kv)]
+
+    def one(bk):
+        b, kv = bk
+        oracle.attn_decode_ref(q[b:b + 1, kv * g:(kv + 1) * g], k[b:b + 1, kv:kv + 1],
+                               v[b:b + 1, kv:kv + 1], w.causal, w.scale)
     reps, t0 = 0, time.perf_counter()
     while True:   # the whole workload, repeated to about 10 s of CPU work
-        oracle.attn_decode_ref(q, k, v, w.causal, w.scale)
+        pmap(one, slices, threads)
         reps += 1
         dt = time.perf_counter() - t0
         if dt > target_s:
             break
-    return {"value": reps * w.bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 decode of the whole {w.name} workload, {reps} time(s), {dt:.1f} s"}
+    return {"value": reps * w.bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
+            "sample": f"fp64 decode of the whole {w.name} workload ({len(slices)} (batch, K/V head) "
+                      f"slices over {threads} threads), {reps} time(s), {dt:.1f} s"}
+
+
+def decode_split_bytes(w, n_splits: int):
+    """(read, write) algorithmic bytes of one split-kernel launch: K, V and Q read
+    once; each split's partial O and LSE written once."""
+    rows = w.B * w.H_q * w.M
+    return (2 * w.B * w.H_kv * w.L * w.D * 2 + w.B * w.H_q * w.M * w.D * 2,
+            rows * n_splits * (w.D + 1) * 4)
 
 
 def main_decode(args, w):
@@ -440,10 +516,7 @@ def main_decode(args, w):
         f"causal={w.causal}")
     t = time_decode(w, args.steps, args.warmup)
     gbs = w.bytes / (t["ms_step"] * 1e-3) / 1e9
-    rows = w.B * w.H_q * w.M
-    # the split kernel reads K, V and Q once and writes each split's partial O and LSE
-    split_bytes = (2 * w.B * w.H_kv * w.L * w.D * 2 + w.B * w.H_q * w.M * w.D * 2
-                   + rows * t["n_splits"] * (w.D + 1) * 4)
+    split_bytes = sum(decode_split_bytes(w, t["n_splits"]))
     achieved = split_bytes / (t["split"] * 1e-3) / 1e9
     log(f"[bench decode] {t['ms_step'] * 1e3:.1f} us/step ({t['n_splits']} splits): "
         f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of HBM; split kernel "
@@ -463,7 +536,9 @@ def main_decode(args, w):
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "attn_decode_split_kernel",
                      "launch_ms_mean": round(t["split"], 5),
-                     "launch_ms_p10_p90": [round(x, 5) for x in t["split_p10_p90"]]},
+                     "launch_ms_p10_p90": [round(x, 5) for x in t["split_p10_p90"]],
+                     "profile": profile_record(w.name, "attn_decode", DECODE_SRC, split_bytes,
+                                               PEAK_HBM_GBS, 1e9)},
         "cpu_baseline": None,
     }
     if args.sweep:
@@ -522,7 +597,9 @@ def main_varlen(args, w):
                      "traffic": stored_traffic(w.name, "attn_fwd_varlen"), "kernel": "attn_fwd_kernel<varlen>",
                      "launch_ms_mean": round(mean, 4),
                      "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
-                                           round(float(np.percentile(per, 90)), 4)]},
+                                           round(float(np.percentile(per, 90)), 4)],
+                     "profile": profile_record(w.name, "attn_fwd_varlen", KERNEL_SRC, w.flops,
+                                               PEAK_TFLOPS)},
         "cpu_baseline": None,
     }
     if args.sweep:
@@ -549,31 +626,35 @@ def main_varlen(args, w):
 
 
 def cpu_baseline_varlen(w, target_s: float = 10.0):
-    """The varlen oracle as it stands (one thread): sequences of the workload
-    from the shortest up, on the first query head, until about 10 s of CPU work;
-    rate in the metric's unit (4*D flops per allowed pair)."""
+    """The varlen oracle as it stands, on all host cores: sequences of the
+    workload from the shortest up, each query head of K/V head 0's group on its
+    own thread, until about 10 s of CPU work; rate in the metric's unit (4*D
+    flops per allowed pair)."""
     import oracle
     oracle.build(force=False)
     q, k, v = w.generate()
     cu = w.cu_seqlens()
     lens = np.diff(cu)
     g = w.H_q // w.H_kv
+    threads = host_threads()
     done_pairs, t0 = 0, time.perf_counter()
     used = []
     for s in np.argsort(lens, kind="stable"):
         a, b = int(cu[s]), int(cu[s + 1])
-        oracle.attn_varlen_ref(q[:g, a:b], k[:1, a:b], v[:1, a:b], np.array([0, b - a], np.int32),
-                               w.causal, w.scale, w.left, w.right)
+        cu1 = np.array([0, b - a], np.int32)
+        pmap(lambda h: oracle.attn_varlen_ref(q[h:h + 1, a:b], k[:1, a:b], v[:1, a:b], cu1,
+                                              w.causal, w.scale, w.left, w.right),
+             range(g), threads)
         sub = synth.VarlenWorkload("s", g, 1, b - a, b - a, b - a, w.causal, w.left, w.right)
         done_pairs += sub.pairs
         used.append(b - a)
         if time.perf_counter() - t0 > target_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": done_pairs * 4 * w.D / dt / 1e12, "unit": "TFLOPS", "cores": 1,
-            "kind": "oracle",
+    return {"value": done_pairs * 4 * w.D / dt / 1e12, "unit": "TFLOPS", "cores": min(threads, g),
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": f"fp64 oracle on {len(used)} sequence(s) of {w.name} (lengths {used}), "
-                      f"{g} query head(s) of K/V head 0, {dt:.1f} s"}
+                      f"{g} query head(s) of K/V head 0 on {min(threads, g)} threads, {dt:.1f} s"}
 
 
 def main_sparse(args, w):
@@ -623,7 +704,9 @@ def main_sparse(args, w):
                      "traffic": stored_traffic(w.name, "attn_fwd_blocksparse"),
                      "kernel": "attn_fwd_kernel<sparse>", "launch_ms_mean": round(mean, 4),
                      "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
-                                           round(float(np.percentile(per, 90)), 4)]},
+                                           round(float(np.percentile(per, 90)), 4)],
+                     "profile": profile_record(w.name, "attn_fwd_blocksparse", KERNEL_SRC,
+                                               w.flops, PEAK_TFLOPS)},
         "cpu_baseline": None,
     }
     if args.sweep:
@@ -652,8 +735,9 @@ def main_sparse(args, w):
 
 
 def cpu_baseline_sparse(w, target_s: float = 10.0):
-    """The block-sparse oracle as it stands (one thread) over a bounded sample of
-    query rows; rate in the metric's unit (4*D flops per allowed pair)."""
+    """The block-sparse oracle as it stands, on all host cores (disjoint row
+    chunks), over a bounded sample of query rows; rate in the metric's unit
+    (4*D flops per allowed pair)."""
     import oracle
     oracle.build(force=False)
     q, k, v = w.generate()
@@ -672,17 +756,22 @@ def cpu_baseline_sparse(w, target_s: float = 10.0):
                 n += max(0, min(k1, i + 1) - k0) if w.causal else k1 - k0
         return n
 
+    threads = host_threads()
+
     def run(n):
         rows = np.sort(rng.choice(total_rows, n, replace=False)).astype(np.int64)
+        parts = [p for p in np.array_split(rows, threads) if p.size]
         t0 = time.perf_counter()
-        oracle.attn_blocksparse_ref(q, k, v, ptr, idx, w.block, w.causal, w.scale, rows=rows)
+        pmap(lambda r: oracle.attn_blocksparse_ref(q, k, v, ptr, idx, w.block, w.causal, w.scale,
+                                                   rows=r), parts, threads)
         return time.perf_counter() - t0, pairs_of(rows) * 4.0 * w.D
-    dt, fl = run(16)
-    n = int(min(total_rows, max(16, 16 * target_s / max(dt, 1e-3))))
+    dt, fl = run(16 * threads)
+    n = int(min(total_rows, max(16 * threads, 16 * threads * target_s / max(dt, 1e-3))))
     dt, fl = run(n)
-    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": 1, "kind": "oracle",
-            "sample": f"{n} random query rows of {w.name} (their listed keys, fp64, one thread), "
-                      f"{dt:.1f} s"}
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
+            "sample": f"{n} random query rows of {w.name} (their listed keys, fp64, {threads} "
+                      f"threads), {dt:.1f} s"}
 
 
 def main_fp8(args, w):
@@ -727,7 +816,9 @@ def main_fp8(args, w):
                      "traffic": stored_traffic(w.name, "attn_fwd_fp8", FP8_SRC),
                      "kernel": "attn_fwd_fp8_kernel", "launch_ms_mean": round(mean, 4),
                      "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
-                                           round(float(np.percentile(per, 90)), 4)]},
+                                           round(float(np.percentile(per, 90)), 4)],
+                     "profile": profile_record(w.name, "attn_fwd_fp8", FP8_SRC, w.flops,
+                                               PEAK_FP8_TFLOPS)},
         "cpu_baseline": None,
     }
     if args.sweep:
@@ -752,29 +843,356 @@ def main_fp8(args, w):
 
 
 def cpu_baseline_fp8(w, target_s: float = 10.0):
-    """The FP8 oracle as it stands (one thread) over a bounded sample of query
-    rows of the same workload; rate in the metric's unit (4*D flops per pair)."""
+    """The FP8 oracle as it stands, on all host cores (disjoint row chunks), over
+    a bounded sample of query rows of the same workload; rate in the metric's
+    unit (4*D flops per pair)."""
     import oracle
     oracle.build(force=False)
     q8, k8, v8 = w.generate()
     rng = np.random.default_rng(2)
     total_rows = w.B * w.H_q * w.N
 
+    threads = host_threads()
+
     def run(n):
         rows = np.sort(rng.choice(total_rows, n, replace=False)).astype(np.int64)
+        parts = [p for p in np.array_split(rows, threads) if p.size]
         t0 = time.perf_counter()
-        oracle.attn_fp8_ref(q8, k8, v8, w.descale_q, w.descale_k, w.descale_v, w.causal,
-                            w.scale, rows=rows)
+        pmap(lambda r: oracle.attn_fp8_ref(q8, k8, v8, w.descale_q, w.descale_k, w.descale_v,
+                                           w.causal, w.scale, rows=r), parts, threads)
         dt = time.perf_counter() - t0
         i = rows % w.N
         keys = (i + 1) if w.causal else np.full(n, w.N)
         return dt, float(keys.sum()) * 4 * w.D
-    dt, fl = run(4)
-    n = int(min(total_rows, max(4, 4 * target_s / max(dt, 1e-3))))
+    dt, fl = run(4 * threads)
+    n = int(min(total_rows, max(4 * threads, 4 * threads * target_s / max(dt, 1e-3))))
     dt, fl = run(n)
-    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": 1, "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{n} random query rows of {w.name} (all allowed keys each, fp64, "
-                      f"one thread), {dt:.1f} s"}
+                      f"{threads} threads), {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ profiles
+# Summaries under profiles/ are written from rocprofv3 csv output by
+# ``bench.py --summarize-profile DIR --op OP [--workload W]``.  DIR holds the
+# output of these runs, all of the same op and workload, taken one after the
+# other in one session on the GPU (commands from the repository root):
+#   bench.json       python3 bench.py --op OP --workload W > DIR/bench.json
+#   kt/              rocprofv3 --kernel-trace --stats --output-format csv -d DIR/kt -o run
+#                      -- python3 bench.py --op OP --workload W --no-cpu-baseline --no-configs
+#   FETCH_SIZE/ WRITE_SIZE/ sqA/ sqB/ sqC/  (optional)
+#                    rocprofv3 --pmc <counters> --kernel-include-regex RX --output-format csv
+#                      -d DIR/<name> -o run -- python3 bench.py --op OP --workload W --steps 3
+#                      --warmup 1 --no-cpu-baseline --no-configs
+#   copy_FETCH_SIZE/ copy_WRITE_SIZE/  (with FETCH_SIZE/WRITE_SIZE)
+#                    rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d DIR/copy_<c>
+#                      -o run -- python3 bench.py --calibrate-copy 1024
+SQ_SETS = {
+    "sqA": "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT "
+           "SQ_ACTIVE_INST_LDS SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "sqB": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 SQ_WAVE_CYCLES "
+           "SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    "sqC": "SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_ANY "
+           "SQ_INSTS_SALU SQ_ACTIVE_INST_MISC GRBM_GUI_ACTIVE",
+}
+
+
+def kernel_key(name: str) -> str:
+    """'void (anonymous namespace)::k<a, b>((anonymous namespace)::P)' -> 'k<a, b>'."""
+    s = name.replace("(anonymous namespace)::", "")
+    if s.startswith("void "):
+        s = s[5:]
+    i = s.find("(")
+    return s[:i] if i > 0 else s
+
+
+def template_args(key: str):
+    i, j = key.find("<"), key.rfind(">")
+    return [a.strip() for a in key[i + 1:j].split(",")] if 0 <= i < j else []
+
+
+def profile_spec(op: str, w):
+    """What the summaries of one op measure: the kernel source, the include
+    regex of the counter runs, the step's kernels (predicates on kernel keys),
+    the dominant kernel's algorithmic work per launch, and the algorithmic bytes
+    of each kernel whose HBM traffic is summarised."""
+    def fwd_kind(varlen, sparse):
+        def pred(safe):
+            return lambda k: (k.startswith("attn_fwd_kernel<")
+                              and template_args(k)[1:3] == [str(varlen).lower(), str(sparse).lower()]
+                              and template_args(k)[4] == str(safe).lower())
+        return pred(False), pred(True)
+    if op in ("fwd", "varlen", "sparse"):
+        fast, exact = fwd_kind(op == "varlen", op == "sparse")
+        step = [("fast", fast), ("exact (non-finite V check)", exact)]
+    if op == "fwd":
+        qkv = w.B * (w.H_q + 2 * w.H_kv) * w.N * w.D * 2
+        wr = w.B * w.H_q * w.N * (w.D * 2 + 4)
+        return dict(tag="attn_fwd", src=KERNEL_SRC, rx="attn_fwd_kernel", step=step,
+                    desc=f"{'causal' if w.causal else 'non-causal'} B={w.B}, H_q={w.H_q}, "
+                         f"H_kv={w.H_kv}, N={w.N}, D={w.D}, bf16",
+                    work=w.flops, unit="TFLOP/s", scale=1e12, peak=PEAK_TFLOPS,
+                    traffic=[("", fast, qkv, wr, "(Q, K, V read once; O, LSE written once)")],
+                    sq=(fast, w.flops / (4 * w.D) / (32 * 32), "wave x 32-key-block"))
+    if op == "fp8":
+        fast = lambda k: k.startswith("attn_fwd_fp8_kernel<") and template_args(k)[2] == "false"
+        exact = lambda k: k.startswith("attn_fwd_fp8_kernel<") and template_args(k)[2] == "true"
+        qkv = w.B * (w.H_q + 2 * w.H_kv) * w.N * w.D
+        wr = w.B * w.H_q * w.N * (w.D * 2 + 4)
+        return dict(tag="attn_fwd_fp8", src=FP8_SRC, rx="attn_fwd_fp8", desc=(
+                    f"{'causal' if w.causal else 'non-causal'} B={w.B}, H_q={w.H_q}, H_kv={w.H_kv}, "
+                    f"N={w.N}, D={w.D}, e4m3 Q/K/V, bf16 O"),
+                    step=[("fast", fast), ("exact (non-finite V check)", exact)],
+                    work=w.flops, unit="TFLOP/s", scale=1e12, peak=PEAK_FP8_TFLOPS,
+                    traffic=[("", fast, qkv, wr, "(e4m3 Q, K, V read once; bf16 O and fp32 LSE "
+                                                 "written once)")],
+                    sq=(fast, w.flops / (4 * w.D) / (32 * 64), "wave x 64-key-block"))
+    if op == "varlen":
+        lens = w.lengths()
+        rd = (w.H_q + 2 * w.H_kv) * w.total * w.D * 2 + (len(lens) + 1) * 4
+        wr = w.H_q * w.total * (w.D * 2 + 4)
+        return dict(tag="attn_fwd_varlen", src=KERNEL_SRC, rx="attn_fwd_kernel", step=step,
+                    desc=f"packed {'causal ' if w.causal else ''}varlen, H_q={w.H_q}, H_kv={w.H_kv}, "
+                         f"{w.total} tokens in {len(lens)} sequences, window ({w.left}, {w.right}), "
+                         f"D={w.D}, bf16",
+                    work=4 * w.D * w.pairs, unit="TFLOP/s", scale=1e12, peak=PEAK_TFLOPS,
+                    traffic=[("", fast, rd, wr, "(Q, K, V and cu_seqlens read once; O and LSE "
+                                                "written once)")], sq=None)
+    if op == "sparse":
+        ptr, idx = w.csr()
+        rd = w.B * (w.H_q + 2 * w.H_kv) * w.N * w.D * 2 + 4 * (len(ptr) + len(idx))
+        wr = w.B * w.H_q * w.N * (w.D * 2 + 4)
+        return dict(tag="attn_fwd_blocksparse", src=KERNEL_SRC, rx="attn_fwd_kernel", step=step,
+                    desc=f"block-sparse B={w.B}, H_q={w.H_q}, H_kv={w.H_kv}, N={w.N}, D={w.D}, "
+                         f"{w.block}x{w.block} blocks ({w.local} local, {w.n_global} global, "
+                         f"{w.n_random} random per query block), bf16",
+                    work=4 * w.D * w.pairs(), unit="TFLOP/s", scale=1e12, peak=PEAK_TFLOPS,
+                    traffic=[("", fast, rd, wr, "(Q read once; every K and V block is listed by "
+                                                "some query block, so K and V once; the block "
+                                                "lists once; O and LSE written once)")], sq=None)
+    if op == "decode":
+        split = lambda k: k.startswith("attn_decode_split_kernel")
+        merge = lambda k: k.startswith("attn_lse_merge_kernel")
+        return dict(tag="attn_decode", src=DECODE_SRC, rx="attn_decode_split",
+                    desc=f"decode B={w.B}, H_q={w.H_q}, H_kv={w.H_kv}, M={w.M}, L={w.L}, D={w.D}, "
+                         f"bf16",
+                    step=[("split", split), ("merge", merge)], work=None, unit="GB/s", scale=1e9,
+                    peak=PEAK_HBM_GBS, traffic=None, sq=None)
+    if op == "bwd":
+        dq = lambda k: k.startswith("attn_bwd_dq_kernel")
+        dkdv = lambda k: k.startswith("attn_bwd_dkdv_kernel")
+        tq = w.B * w.H_q * w.N * w.D * 2
+        tkv = w.B * w.H_kv * w.N * w.D * 2
+        r4 = w.B * w.H_q * w.N * 4
+        return dict(tag="attn_bwd", src=BWD_SRC, rx="attn_bwd",
+                    desc=f"{'causal' if w.causal else 'non-causal'} B={w.B}, H_q={w.H_q}, "
+                         f"H_kv={w.H_kv}, N={w.N}, D={w.D}, bf16",
+                    step=[("dkdv", dkdv), ("dq", dq)], work=8 * w.D * bwd_pairs(w),
+                    unit="TFLOP/s", scale=1e12, peak=PEAK_TFLOPS,
+                    traffic=[("_dq", dq, 3 * tq + 2 * tkv + r4, tq + r4,
+                              "(reads Q, K, V, O, dO, LSE once; writes dQ, delta once)"),
+                             ("_dkdv", dkdv, 2 * tq + 2 * tkv + 2 * r4, 2 * tkv,
+                              "(reads Q, dO, K, V, LSE, delta once; writes dK, dV once)")],
+                    sq=(dkdv, bwd_pairs(w) / (32 * 32), "wave-pair x 32x32-sub-block"))
+    raise ValueError(op)
+
+
+def _csv_one(d, pattern):
+    import glob
+    f = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if not f:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return f[0]
+
+
+def _per_dispatch(d, pred):
+    """{counter: [value per dispatch]} over the dispatches whose kernel key satisfies pred."""
+    import csv
+    acc = {}
+    with open(_csv_one(d, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if not pred(kernel_key(r["Kernel_Name"])):
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (_, c), v in acc.items():
+        out.setdefault(c, []).append(v)
+    return out
+
+
+def summarize_profile(d: str, op: str, w) -> list:
+    """Writes the profiles/ summaries of one profiling session (see above);
+    returns the files written."""
+    import csv
+    import statistics
+    sp = profile_spec(op, w)
+    h = kernel_hash(sp["src"])
+    tag, name = sp["tag"], w.name
+    wl = f"--op {op} --workload {name}"
+    pmc_cmd = f"bench.py {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-configs"
+    with open(os.path.join(d, "bench.json")) as f:
+        bench = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    written = []
+    if op == "decode":
+        rd_alg, wr_alg = decode_split_bytes(w, int(bench["config"]["n_splits"]))
+        sp["work"] = rd_alg + wr_alg
+        sp["traffic"] = [("_split", sp["step"][0][1], rd_alg, wr_alg,
+                          f"(K, V, Q read once; partial O and LSE of {bench['config']['n_splits']} "
+                          f"splits written once)")]
+
+    # kernel trace
+    rows = []
+    with open(_csv_one(os.path.join(d, "kt"), "run_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((kernel_key(r["Name"]), r))
+    step_avg = {}
+    for label, pred in sp["step"]:
+        hit = [r for k, r in rows if pred(k)]
+        if hit:
+            calls = sum(int(r["Calls"]) for r in hit)
+            step_avg[label] = (sum(float(r["AverageNs"]) * int(r["Calls"]) for r in hit) / calls,
+                               [k for k, r in rows if pred(k)], calls)
+    dom_label = sp["step"][0][0]
+    if dom_label not in step_avg:
+        raise RuntimeError(f"the dominant kernel of {op} is not in the kernel trace")
+    dom_ns, dom_keys, dom_calls = step_avg[dom_label]
+    step_ns = sum(v[0] for v in step_avg.values())
+    rf = bench.get("roofline", {})
+    L = [f"# rocprofv3 kernel-trace summary of bench.py {wl}: {sp['desc']}.",
+         "# Commands, from the repository root on the GPU, one after the other in one session:",
+         f"#   python3 bench.py {wl} > <dir>/bench.json",
+         f"#   cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt "
+         f"-o run -- python3 <repo>/bench.py {wl} --no-cpu-baseline --no-configs",
+         f"#   python3 bench.py --summarize-profile <dir> {wl}",
+         f"kernel_source_sha256_16: {h}",
+         f"dominant_kernel: {' | '.join(dom_keys)}",
+         f"dominant_kernel_avg_ns: {dom_ns:.0f}",
+         f"dominant_kernel_calls: {dom_calls}"]
+    for label, (ns, keys, calls) in step_avg.items():
+        if label != dom_label:
+            L.append(f"other_step_kernel: {label}: {' | '.join(keys)}: avg_ns {ns:.0f}, calls {calls}")
+    L.append(f"step_kernels_avg_ns: {step_ns:.0f}")
+    if sp["work"]:
+        rate = sp["work"] / (dom_ns * 1e-9) / sp["scale"]
+        L.append(f"dominant_kernel_rate: {rate:.2f} {sp['unit']} = {rate / sp['peak']:.4f} of "
+                 f"{sp['peak']:.1f} ({sp['work']:.6g} algorithmic units per launch)")
+    L.append(f"bench_in_same_session: value={bench.get('value')} {bench.get('unit')}, "
+             f"ms_per_step={bench.get('ms_per_step')}, launch_ms_mean={rf.get('launch_ms_mean')}, "
+             f"frac={rf.get('frac')}")
+    L.append("kernel stats (all kernels of the rocprofv3 run):")
+    for k, r in rows:
+        L.append(f"  {k if len(k) <= 100 else k[:97] + '...'}")
+        L.append(f"    calls={r['Calls']} avg_ns={float(r['AverageNs']):.0f} min_ns={r['MinNs']} "
+                 f"max_ns={r['MaxNs']} pct={float(r['Percentage']):.2f}")
+    out = os.path.join(PROFILES, f"kernel_trace_{tag}_{name}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(L) + "\n")
+    written.append(out)
+
+    # HBM traffic
+    if sp["traffic"] and os.path.isdir(os.path.join(d, "FETCH_SIZE")):
+        fc = _per_dispatch(os.path.join(d, "copy_FETCH_SIZE"), lambda k: "copyBuffer" in k)["FETCH_SIZE"]
+        wc = _per_dispatch(os.path.join(d, "copy_WRITE_SIZE"), lambda k: "copyBuffer" in k)["WRITE_SIZE"]
+        fs, ws = 1024 * 1024 / statistics.median(fc), 1024 * 1024 / statistics.median(wc)
+        for suffix, pred, rd_alg, wr_alg, note in sp["traffic"]:
+            fa = _per_dispatch(os.path.join(d, "FETCH_SIZE"), pred)["FETCH_SIZE"]
+            wa = _per_dispatch(os.path.join(d, "WRITE_SIZE"), pred)["WRITE_SIZE"]
+            fr, wr = statistics.mean(fa), statistics.mean(wa)
+            rd, wt = fr * 1024 * fs, wr * 1024 * ws
+            alg = rd_alg + wr_alg
+            L = [f"# HBM traffic per launch of the {tag}{suffix} kernel (fast path) of bench.py {wl}: "
+                 f"{sp['desc']}.",
+                 f"# rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one counter per run), each "
+                 f"scaled by what the same counter reads for a plain 1 GiB device-to-device copy.",
+                 "# Commands, from the repository root on the GPU, in one session:",
+                 f"#   cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {sp['rx']} "
+                 f"--output-format csv -d <dir>/FETCH_SIZE -o run -- python3 <repo>/{pmc_cmd}",
+                 f"#   cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {sp['rx']} "
+                 f"--output-format csv -d <dir>/WRITE_SIZE -o run -- python3 <repo>/{pmc_cmd}",
+                 "#   cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv -d "
+                 "<dir>/copy_FETCH_SIZE -o run -- python3 <repo>/bench.py --calibrate-copy 1024",
+                 "#   cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv -d "
+                 "<dir>/copy_WRITE_SIZE -o run -- python3 <repo>/bench.py --calibrate-copy 1024",
+                 f"#   python3 bench.py --summarize-profile <dir> {wl}",
+                 f"kernel_source_sha256_16: {h}",
+                 f"fetch_kib_per_dispatch_raw: {fr:.1f}   (dispatches: {len(fa)}, min {min(fa):.1f}, "
+                 f"max {max(fa):.1f})",
+                 f"write_kib_per_dispatch_raw: {wr:.1f}   (dispatches: {len(wa)})",
+                 f"copy_1GiB_fetch_kib_raw: {statistics.median(fc):.1f}   -> fetch scale {fs:.4f}",
+                 f"copy_1GiB_write_kib_raw: {statistics.median(wc):.1f}   -> write scale {ws:.4f}",
+                 f"hbm_read_bytes_per_launch: {rd:.0f}",
+                 f"hbm_write_bytes_per_launch: {wt:.0f}",
+                 f"hbm_bytes_per_launch: {rd + wt:.0f}",
+                 f"algorithmic_bytes_per_launch: {alg}   {note}",
+                 f"traffic_over_algorithmic: {(rd + wt) / alg:.3f}   (reads {rd / rd_alg:.3f}x, "
+                 f"writes {wt / wr_alg:.3f}x the algorithmic bytes)"]
+            out = os.path.join(PROFILES, f"hbm_traffic_{tag}{suffix}_{name}.txt")
+            with open(out, "w") as f:
+                f.write("\n".join(L) + "\n")
+            written.append(out)
+
+    # SQ counters
+    if sp["sq"] and all(os.path.isdir(os.path.join(d, s)) for s in SQ_SETS):
+        pred, units, unit_desc = sp["sq"]
+        sq = {}
+        for s in SQ_SETS:
+            for k, v in _per_dispatch(os.path.join(d, s), pred).items():
+                if k == "GRBM_GUI_ACTIVE" and k in sq:
+                    continue
+                sq[k] = statistics.mean(v)
+        el = sq["GRBM_GUI_ACTIVE"] / 8
+        tot = el * 1024
+        mf = sq["SQ_INSTS_MFMA"]
+        ms = dom_ns * 1e-6
+        L = [f"# rocprofv3 SQ counters per dispatch of the {tag} kernel (fast path) of bench.py {wl}: "
+             f"{sp['desc']}.",
+             "# Three passes of 7 counters each, from the repository root on the GPU, in one session:",
+             f"#   cd /tmp && TMPDIR=/tmp rocprofv3 --pmc <set> --kernel-include-regex {sp['rx']} "
+             f"--output-format csv -d <dir>/<set> -o run -- python3 <repo>/{pmc_cmd}"]
+        L += [f"#   {k}: {v}" for k, v in SQ_SETS.items()]
+        L += [f"#   python3 bench.py --summarize-profile <dir> {wl}",
+              f"kernel_source_sha256_16: {h}", "raw (summed over the device):"]
+        L += [f"  {k}: {sq[k]:.4g}" for k in sorted(sq)]
+        L += [f"derived (GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs; {units:.0f} "
+              f"{unit_desc} units per launch):",
+              f"  elapsed cycles per XCD: {el:.4g}   (over the {ms:.3f} ms mean of the kernel trace: "
+              f"about {el / (ms * 1e-3) / 1e9:.2f} GHz)",
+              f"  MFMA busy / (elapsed x SIMDs): {100 * sq['SQ_VALU_MFMA_BUSY_CYCLES'] / tot:.1f}%   "
+              f"(MFMA instructions per launch {mf:.4g})",
+              f"  VALU active / (elapsed x SIMDs): {100 * 4 * sq['SQ_ACTIVE_INST_VALU'] / tot:.1f}%   "
+              f"(SQ_ACTIVE_INST_VALU counts 4-cycle units)",
+              f"  MFMA+VALU co-execution / MFMA busy: "
+              f"{100 * sq['SQ_VALU_MFMA_COEXEC_CYCLES'] / sq['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}%",
+              f"  waves waiting (waitcnt or barrier) / wave cycles: "
+              f"{100 * sq['SQ_WAIT_ANY'] / sq['SQ_WAVE_CYCLES']:.1f}%",
+              f"  per {unit_desc} unit: {sq['SQ_INSTS_VALU'] / units:.1f} VALU instructions "
+              f"({mf / units:.1f} of them MFMA), {sq['SQ_INSTS_VALU_TRANS_F32'] / units:.1f} "
+              f"transcendental, {sq['SQ_INSTS_LDS'] / units:.1f} LDS, "
+              f"{sq['SQ_INSTS_SALU'] / units:.1f} SALU",
+              f"  LDS bank conflicts: {sq['SQ_LDS_BANK_CONFLICT']:.0f}; LDS busy "
+              f"{100 * sq['SQ_LDS_IDX_ACTIVE'] / (el * 256):.1f}% of CU cycles"]
+        out = os.path.join(PROFILES, f"sq_counters_{tag}_{name}.txt")
+        with open(out, "w") as f:
+            f.write("\n".join(L) + "\n")
+        written.append(out)
+    return written
+
+
+def workload_of(args):
+    """The workload an op runs: --workload, else the op's headline workload."""
+    table, default = {
+        "fwd": (synth.WORKLOADS, synth.HEADLINE), "bwd": (synth.WORKLOADS, synth.HEADLINE),
+        "decode": (synth.DECODE_WORKLOADS, synth.DECODE_HEADLINE),
+        "varlen": (synth.VARLEN_WORKLOADS, "varlen_causal_h16_t32768"),
+        "fp8": (synth.FP8_WORKLOADS, synth.FP8_HEADLINE),
+        "sparse": (synth.SPARSE_WORKLOADS, next(iter(synth.SPARSE_WORKLOADS))),
+    }[args.op]
+    name = args.workload or default
+    if name not in table:
+        sys.exit(f"{name} is not a workload of --op {args.op}")
+    return table[name]
 
 
 def main():
@@ -791,6 +1209,12 @@ def main():
                     help="default: the headline workload of the op")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="forward: skip the per-config list (every forward workload timed back "
+                         "to back after the headline)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="write the profiles/ summaries of one profiling session held in DIR "
+                         "(for --op and --workload; needs no GPU) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size reference for scaling HBM byte counters) and exit")
@@ -801,6 +1225,10 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
+    if args.summarize_profile:
+        for f in summarize_profile(args.summarize_profile, args.op, workload_of(args)):
+            log(f"[profile] wrote {os.path.relpath(f, ROOT)}")
+        return
 
     import torch
     import scaled_dot_product_17_amd as sdpa
@@ -819,36 +1247,11 @@ def main():
         return
     sdpa.load()
 
-    if args.op == "varlen":
-        name = args.workload or "varlen_causal_h16_t32768"
-        if name not in synth.VARLEN_WORKLOADS:
-            sys.exit(f"{name} is not a varlen workload")
-        main_varlen(args, synth.VARLEN_WORKLOADS[name])
-        return
-    if args.op == "sparse":
-        name = args.workload or next(iter(synth.SPARSE_WORKLOADS))
-        if name not in synth.SPARSE_WORKLOADS:
-            sys.exit(f"{name} is not a block-sparse workload")
-        main_sparse(args, synth.SPARSE_WORKLOADS[name])
-        return
-    if args.op == "fp8":
-        name = args.workload or synth.FP8_HEADLINE
-        if name not in synth.FP8_WORKLOADS:
-            sys.exit(f"{name} is not an FP8 workload")
-        main_fp8(args, synth.FP8_WORKLOADS[name])
-        return
-    if args.op == "decode":
-        name = args.workload or synth.DECODE_HEADLINE
-        if name not in synth.DECODE_WORKLOADS:
-            sys.exit(f"{name} is not a decode workload")
-        main_decode(args, synth.DECODE_WORKLOADS[name])
-        return
-    name = args.workload or synth.HEADLINE
-    if name not in synth.WORKLOADS:
-        sys.exit(f"{name} is not a forward/backward workload")
-    w = synth.WORKLOADS[name]
-    if args.op == "bwd":
-        main_bwd(args, w)
+    w = workload_of(args)
+    mains = {"varlen": main_varlen, "sparse": main_sparse, "fp8": main_fp8,
+             "decode": main_decode, "bwd": main_bwd}
+    if args.op in mains:
+        mains[args.op](args, w)
         return
     log(f"[bench] {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} N={w.N} D={w.D} causal={w.causal}")
     ms_step, ms_launch, per = time_workload(w, args.steps, args.warmup)
@@ -872,15 +1275,24 @@ def main():
                      "traffic": traffic, "kernel": "attn_fwd_kernel",
                      "launch_ms_mean": round(ms_launch, 4),
                      "launch_ms_p10_p90": [round(float(np.percentile(per, 10)), 4),
-                                           round(float(np.percentile(per, 90)), 4)]},
+                                           round(float(np.percentile(per, 90)), 4)],
+                     "profile": profile_record(w.name, "attn_fwd", KERNEL_SRC, w.flops,
+                                               PEAK_TFLOPS)},
+        "configs": None,
         "cpu_baseline": None,
     }
-    if args.sweep:
-        log(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}")
+    if not args.no_configs or args.sweep:
+        # every forward workload, grouped as the five configurations of the
+        # metric, timed back to back in this run after the headline
+        log(f"{'config':6s} {'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}")
+        res["configs"] = []
         for name, x in synth.WORKLOADS.items():
             ms = time_back_to_back(x)
             tf = x.flops / (ms * 1e-3) / 1e12
-            log(f"{name:36s} {ms:9.3f} {tf:9.1f} {100 * tf / PEAK_TFLOPS:7.1f}")
+            cfg = synth.config_of(x)
+            log(f"{cfg:6s} {name:36s} {ms:9.3f} {tf:9.1f} {100 * tf / PEAK_TFLOPS:7.1f}")
+            res["configs"].append({"config": cfg, "workload": name, "ms": round(ms, 4),
+                                   "tflops": round(tf, 2), "frac": round(tf / PEAK_TFLOPS, 4)})
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(w)

@@ -184,6 +184,19 @@ WORKLOADS = {w.name: w for w in [
 HEADLINE = "mha_noncausal_b2_h16_n16384"
 
 
+def config_of(w: Workload) -> str:
+    """Label of the forward configuration a workload belongs to: C1 the tiny
+    MHA case, C2 the mid-shape GQA/MQA pair, C3 and C4 the non-causal and causal
+    MHA sweeps at 32768 tokens, C5 the peaky causal long-context MQA case."""
+    if w.N <= 256:
+        return "C1"
+    if w.qk_mult != 1.0:
+        return "C5"
+    if w.H_kv < w.H_q:
+        return "C2"
+    return "C4" if w.causal else "C3"
+
+
 # --------------------------------------------------------------------------
 # FP8 (e4m3) inputs.  e4m3 (the OCP 8-bit format): sign, 4 exponent bits with
 # bias 7, 3 mantissa bits, subnormals at exponent field 0, no infinities, codes
