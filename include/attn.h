@@ -44,7 +44,8 @@ typedef enum attn_status {
     ATTN_ERR_ALIAS = 7,     /* an output range overlaps an input or the other output   */
     ATTN_ERR_LAUNCH = 8,    /* the HIP runtime rejected the kernel launch              */
     ATTN_ERR_DEVICE = 9,    /* the current device is not a gfx950 (MI350-series) GPU   */
-    ATTN_ERR_WORKSPACE = 10 /* the workspace is smaller than the call needs            */
+    ATTN_ERR_WORKSPACE = 10,/* the workspace is smaller than the call needs            */
+    ATTN_ERR_SCRATCH = 11   /* the call needs more than the library's fixed scratch    */
 } attn_status;
 
 /*
@@ -314,6 +315,31 @@ size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int caus
 attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int H_q, int H_kv, int M, int L, int D, int causal, float scale,
                         int n_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_noalloc: attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops with a fixed memory
+ * plan, harnesses that forbid hipMalloc.  It takes no workspace and calls no
+ * allocator: the partial results live in a fixed array inside the library,
+ * ATTN_DECODE_SCRATCH_BYTES per GPU, which each GPU the library runs on holds
+ * until the process ends.  The array's address on a device is looked up
+ * (hipGetSymbolAddress) on the first call with that device current.
+ *
+ * Every call on one GPU uses that GPU's one array and leaves its partial
+ * results there.  Calls whose work can overlap on one GPU (streams with no
+ * ordering between them) race on it; calls in one stream, or ordered by
+ * events, are safe.  No part of the array needs to start at zero: a call
+ * writes every entry it reads.
+ *
+ * Arguments, precision and errors as for attn_decode, without workspace and
+ * workspace_bytes, plus ATTN_ERR_SCRATCH when attn_decode_workspace_bytes()
+ * for these arguments exceeds ATTN_DECODE_SCRATCH_BYTES (checked before any
+ * HIP call).  o and lse must be 4-byte aligned.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H_q, int H_kv, int M, int L, int D, int causal,
+                                float scale, int n_splits, void* stream);
 
 /*
  * attn_decode_partial: only the local half of attn_decode: the partial result

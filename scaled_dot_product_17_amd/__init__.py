@@ -21,10 +21,10 @@ ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GQA",
                 4: "ATTN_ERR_HEAD_DIM", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIGN",
                 7: "ATTN_ERR_ALIAS", 8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_DEVICE",
-                10: "ATTN_ERR_WORKSPACE"}
+                10: "ATTN_ERR_WORKSPACE", 11: "ATTN_ERR_SCRATCH"}
 EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_fwd_blocksparse", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
             "attn_bwd_ws", "attn_bwd_splits", "attn_bwd_workspace_bytes", "attn_decode",
-            "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
+            "attn_decode_noalloc", "attn_decode_partial", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_lse_merge", "attn_status_string",
             "attn_fwd_flops", "attn_bwd_flops", "attn_decode_flops")
 
 _lock = threading.Lock()
@@ -81,6 +81,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_decode.restype = ctypes.c_int
             lib.attn_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            lib.attn_decode_noalloc.restype = ctypes.c_int
+            lib.attn_decode_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
             lib.attn_decode_partial.restype = ctypes.c_int
             lib.attn_decode_partial.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
@@ -402,6 +405,19 @@ def attn_decode(q, k, v, o, lse, B, H_q, H_kv, M, L, D, causal, scale, n_splits,
     return load().attn_decode(q, k, v, o, lse, int(B), int(H_q), int(H_kv), int(M), int(L),
                               int(D), int(bool(causal)), float(scale), int(n_splits), workspace,
                               int(workspace_bytes), stream)
+
+
+def attn_decode_noalloc(q, k, v, o, lse, B, H_q, H_kv, M, L, D, causal, scale, n_splits,
+                        stream) -> int:
+    """Direct C-ABI call (decode with the library's fixed scratch array, no
+    workspace); returns the status code."""
+    return load().attn_decode_noalloc(q, k, v, o, lse, int(B), int(H_q), int(H_kv), int(M),
+                                      int(L), int(D), int(bool(causal)), float(scale),
+                                      int(n_splits), stream)
+
+
+# bytes of the fixed scratch array attn_decode_noalloc uses (ATTN_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 16 << 20
 
 
 def attn_decode_partial(q, k, v, o_part, lse_part, B, H_q, H_kv, M, L, D, causal, scale,

@@ -434,6 +434,27 @@ attn_status launch_split(const DecParams& p, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// attn_decode_noalloc's partial results: one array per GPU, shared by every
+// call on that GPU.  Host code never uses the name `scratch` as an address (on
+// the host it is only a stand-in for the device symbol): the device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+// Device address of this device's copy of `scratch` (dev must be current), or
+// nullptr if the runtime cannot give it.
+void* scratch_on(int dev) {
+    constexpr int MAX_DEVICES = 64;
+    static std::atomic<void*> cache[MAX_DEVICES];
+    if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    void* ptr = cache[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return nullptr;
+        cache[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int M, int L, int D,
@@ -466,6 +487,33 @@ extern "C" attn_status attn_decode(const void* q, const void* k, const void* v, 
     if (st != ATTN_OK) return st;
     p.o_part = (float*)workspace;
     p.lse_part = (float*)((char*)workspace + align_up(part_o_bytes(pl), 256));
+    const hipStream_t s = (hipStream_t)stream;
+    st = launch_split(p, s);
+    if (st != ATTN_OK) return st;
+    return launch_merge(p.o_part, p.lse_part, (int)pl.rows, pl.n_splits, o, lse, s);
+}
+
+extern "C" attn_status attn_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                           float* lse, int B, int H_q, int H_kv, int M, int L,
+                                           int D, int causal, float scale, int n_splits,
+                                           void* stream) {
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+    attn_status st = check_decode_shape(B, H_q, H_kv, M, L, D, causal, scale);
+    if (st != ATTN_OK) return st;
+    const Plan pl = make_plan(B, H_q, H_kv, M, L, n_splits);
+    if (workspace_bytes(pl) > ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    if (((uintptr_t)o & 3) || ((uintptr_t)lse & 3)) return ATTN_ERR_ALIGN;
+    const void* outs[2] = {o, lse};
+    const size_t out_bytes[2] = {(size_t)pl.rows * HD * 2, lse ? (size_t)pl.rows * 4 : 0};
+    DecParams p;
+    st = prepare_split(q, k, v, outs, out_bytes, 2, B, H_q, H_kv, M, L, D, causal, scale, pl, p);
+    if (st != ATTN_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    char* const ws = (char*)scratch_on(dev);
+    if (ws == nullptr) return ATTN_ERR_LAUNCH;
+    p.o_part = (float*)ws;
+    p.lse_part = (float*)(ws + align_up(part_o_bytes(pl), 256));
     const hipStream_t s = (hipStream_t)stream;
     st = launch_split(p, s);
     if (st != ATTN_OK) return st;

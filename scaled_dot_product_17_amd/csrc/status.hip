@@ -14,6 +14,7 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_LAUNCH: return "kernel launch failed";
         case ATTN_ERR_DEVICE: return "the current device is not a gfx950 GPU";
         case ATTN_ERR_WORKSPACE: return "the workspace is smaller than attn_decode_workspace_bytes()";
+        case ATTN_ERR_SCRATCH: return "the call needs more than the library's fixed scratch array (ATTN_DECODE_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -313,11 +313,44 @@ def test_decode_argument_errors(lib, kw, code):
     assert call_dec(**kw) == code
 
 
+def call_dec_noalloc(**kw):
+    a = dict(DC)
+    a.update(kw)
+    return sdpa.attn_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H_q"],
+                                    a["H_kv"], a["M"], a["L"], a["D"], a["causal"], a["scale"],
+                                    a["n_splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(M=0), 2), (dict(causal=1, M=5, L=4), 2), (dict(H_q=15), 3), (dict(D=64), 4),
+    (dict(scale=float("inf")), 5), (dict(k=0x200000008), 6), (dict(lse=0x800000002), 6),
+    (dict(o=0x100000 + 64), 7), (dict(lse=0x600000000 + 32), 7),
+    # partial results beyond the fixed scratch array: 2048 rows x 32 splits x 516 B
+    (dict(H_kv=16, M=16, n_splits=32), 11),
+])
+def test_decode_noalloc_argument_errors(lib, kw, code):
+    assert call_dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_scratch_size(lib):
+    assert sdpa.DECODE_SCRATCH_BYTES == 16 << 20
+    text = open(HEADER).read()
+    assert "#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    # the largest split count that fits is accepted by the size check (it then
+    # reports the missing device), one more split is refused
+    fits = sdpa.attn_decode_workspace_bytes(8, 16, 16, 16, 32768, 128, 15)
+    over = sdpa.attn_decode_workspace_bytes(8, 16, 16, 16, 32768, 128, 16)
+    assert fits <= sdpa.DECODE_SCRATCH_BYTES < over
+    assert call_dec_noalloc(H_kv=16, M=16, n_splits=16) == 11
+
+
 def test_decode_valid_arguments_without_gpu_report_device(lib):
     import torch
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: this case would launch on fake pointers")
     assert call_dec() == 9 and call_dec(lse=None) == 9
+    assert call_dec_noalloc() == 9 and call_dec_noalloc(lse=None) == 9
 
 
 @pytest.mark.parametrize("args,code", [
