@@ -46,15 +46,19 @@
 
 #include "attn.h"
 #include "cdna4.h"
+#include "tile.h"
 
 namespace {
 
 using namespace cdna4;
-
-constexpr int HD = 128;                    // head dimension handled by these kernels
-constexpr int ROW_BYTES = HD * 2;          // 256 B per bf16 row
-constexpr int KB = 32;                     // rows per MFMA block
-constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB
+// 32-row tiles of 128 head dims (256-byte rows) in the shared swizzled LDS layout
+using tile::BLK_BYTES;
+using tile::HD;
+using tile::KB;
+using tile::ROW_BYTES;
+using tile::pack_bf16;
+using tile::swz;
+using TileReads = tile::Reads;
 constexpr float LOG2E = 1.4426950408889634f;
 
 // attn_bwd_dq: 8 waves, rings of 4 K blocks and 4 V blocks
@@ -99,56 +103,6 @@ struct BwdParams {
     float c;                // scale * log2(e)
     float scale;
 };
-
-// LDS layout of every 256-byte row tile (K, V, Q, dO): 16-byte chunk c of row r
-// sits at chunk position c ^ swz(r).  A row-wise MFMA operand read (16 rows,
-// one chunk) hits 16 distinct positions; a transposing read (4 rows x 4
-// chunks) puts each row in its own 64-byte bank group.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-    return (uint32_t)(row * ROW_BYTES + ((chunk ^ swz(row)) << 4));
-}
-
-// Per-lane LDS offsets of the two operand read patterns of a 32-row block.
-//   rd_row[ks]: A operand with rows = MFMA m, 8 consecutive head dims of k step ks.
-//   tr_lo/tr_hi[db]: A operand with head dims 32db.. = MFMA m and rows = MFMA k in
-//   the order an fp32 accumulator holds them (rows 8(r/4) + 4(lane/32) + r%4 of
-//   register r), so an accumulator turned into bf16 pairs is the matching B
-//   operand.  Rows 16..31 of the block add 16 * ROW_BYTES (the swizzle repeats).
-struct TileReads {
-    uint32_t rd_row[8];
-    uint32_t tr_lo[4], tr_hi[4];
-    __device__ __forceinline__ void init(int lane) {
-        const int l32 = lane & 31, hh = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) rd_row[ks] = tile_off(l32, 2 * ks + hh);
-        const int g = lane >> 4;          // 16-lane group
-        const int rs = (lane & 15) >> 2;  // row within the 4-row group
-        const int cs = lane & 3;          // 4-element column group
-        const int row = 4 * (g >> 1) + rs;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int col = 32 * db + 16 * (g & 1) + 4 * cs;
-            const uint32_t half = (col & 4) ? 8u : 0u;
-            tr_lo[db] = tile_off(row, col >> 3) + half;
-            tr_hi[db] = tile_off(row + 8, col >> 3) + half;
-        }
-    }
-    // A operand of rows 16kk..16kk+15 (accumulator order) x head dims 32db..32db+31
-    __device__ __forceinline__ bf16x8 tr(const char* lds, uint32_t base, int db, int kk) const {
-        const bf16x4 lo = lds_read_tr(lds, base + tr_lo[db] + (uint32_t)(16 * kk * ROW_BYTES));
-        const bf16x4 hi = lds_read_tr(lds, base + tr_hi[db] + (uint32_t)(16 * kk * ROW_BYTES));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    __device__ __forceinline__ bf16x8 row(const char* lds, uint32_t base, int ks) const {
-        return *(const bf16x8*)(lds + base + rd_row[ks]);
-    }
-};
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    const bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 __device__ __forceinline__ void store_row_f32(float* row, const f32x16 (&acc)[4], float mul, int hh) {
 #pragma unroll

@@ -43,16 +43,11 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "cdna4.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace cdna4;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
 // A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for short dense
@@ -69,7 +64,6 @@ constexpr int V_RING = 4 * BLK_BYTES;
 constexpr int LDS_BYTES = 8 * BLK_BYTES;   // 64 KiB
 constexpr float MOVE_SUM = 18446744073709551616.0f;  // 2^64: a lane's block sum of p above
                                                       // this moves the softmax reference
-constexpr uint32_t RSRC_DWORD3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
 // block-sparse masks: blocks of SP_BLOCK query rows x SP_BLOCK keys; a workgroup's
 // 256 rows are two query blocks.  The union of their key-block lists is kept in
 // LDS past the rings, one 16-bit entry per key block (index | 2 membership bits).
@@ -116,16 +110,6 @@ struct Params {
     int n_sblk;         // ceil(N / SP_BLOCK)
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             (int)RSRC_DWORD3);
-}
-
-// 16-byte buffer load into VGPRs; offsets at or beyond the range return zeros.
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // LDS byte offset of the 16-byte chunk (row, chunk) of a K tile.  The chunk
 // index is XOR-swizzled with the low 4 row bits so the 32 rows one MFMA A
 // operand read touches (same logical chunk) fall in distinct banks.
@@ -138,55 +122,6 @@ __device__ __forceinline__ uint32_t k_lds_off(int row, int chunk) {
 // four rows over the four 64-byte bank groups.
 __device__ __forceinline__ uint32_t v_lds_off(int row, int chunk) {
     return (uint32_t)(row * ROW_BYTES + ((chunk ^ ((row & 3) << 2)) << 4));
-}
-
-__device__ __forceinline__ float wave_swap_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                              false, false);
-    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
-}
-__device__ __forceinline__ float wave_swap_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                              false, false);
-    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + off));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
-// Maps the hardware workgroup id to a logical id so that consecutive logical
-// ids land on the same XCD (the dispatcher deals workgroups to the 8 XCDs
-// round-robin).  Tiles of one head then share that XCD's L2 for K/V.
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-    const int nx = 8;
-    const int q = total / nx, r = total % nx;
-    const int x = bid % nx, s = bid / nx;
-    const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-    return start + s;
-}
-
-// LDS DMA of one 16-byte chunk per lane: the buffer unit copies
-// rsrc[voff .. voff+15] to LDS byte lds_addr + 16*lane, without passing
-// through VGPRs.  Out-of-range offsets read as zeros.  Issued as inline
-// assembly so that the compiler does not order later LDS reads behind it; the
-// caller waits for completion (vmcnt) before the workgroup barrier that
-// publishes the data.
-__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Raw buffer descriptor in SGPRs for inline assembly.
-__device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), RSRC_DWORD3};
 }
 
 // SAFE = false: the fast kernel.  SAFE = true: the exact kernel, which redoes
@@ -850,26 +785,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
-constexpr int MAX_DEVICES = 64;
-std::atomic<int> g_arch_ok[MAX_DEVICES];   // 0 unknown, 1 gfx950, 2 other
-
-bool device_is_gfx950(int dev) {
-    if (dev < 0 || dev >= MAX_DEVICES) return false;
-    int s = g_arch_ok[dev].load(std::memory_order_relaxed);
-    if (s == 0) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
-        s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-        g_arch_ok[dev].store(s, std::memory_order_relaxed);
-    }
-    return s == 1;
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return x < y + nb && y < x + na;
-}
-
 void set_scale(Params& p, float scale) {
     const float mag = std::fabs(scale);
     p.q_mode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
@@ -918,11 +833,11 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     const size_t qo_bytes = (size_t)B * H_q * N * HD * 2;
     const size_t kv_bytes = (size_t)B * H_kv * N * HD * 2;
     const size_t lse_bytes = (size_t)B * H_q * N * 4;
-    if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(o, qo_bytes, k, kv_bytes) ||
-        overlaps(o, qo_bytes, v, kv_bytes))
+    if (ranges_overlap(o, qo_bytes, q, qo_bytes) || ranges_overlap(o, qo_bytes, k, kv_bytes) ||
+        ranges_overlap(o, qo_bytes, v, kv_bytes))
         return ATTN_ERR_ALIAS;
-    if (lse && (overlaps(lse, lse_bytes, q, qo_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
-                overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, qo_bytes)))
+    if (lse && (ranges_overlap(lse, lse_bytes, q, qo_bytes) || ranges_overlap(lse, lse_bytes, k, kv_bytes) ||
+                ranges_overlap(lse, lse_bytes, v, kv_bytes) || ranges_overlap(lse, lse_bytes, o, qo_bytes)))
         return ATTN_ERR_ALIAS;
 
     int dev = -1;
@@ -985,9 +900,9 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     const void* ins[4] = {q, k, v, cu_seqlens};
     const size_t in_bytes[4] = {qo_bytes, kv_bytes, kv_bytes, cu_bytes};
     for (int i = 0; i < 4; ++i)
-        if (overlaps(o, qo_bytes, ins[i], in_bytes[i]) || (lse && overlaps(lse, lse_bytes, ins[i], in_bytes[i])))
+        if (ranges_overlap(o, qo_bytes, ins[i], in_bytes[i]) || (lse && ranges_overlap(lse, lse_bytes, ins[i], in_bytes[i])))
             return ATTN_ERR_ALIAS;
-    if (lse && overlaps(lse, lse_bytes, o, qo_bytes)) return ATTN_ERR_ALIAS;
+    if (lse && ranges_overlap(lse, lse_bytes, o, qo_bytes)) return ATTN_ERR_ALIAS;
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
@@ -1046,10 +961,10 @@ extern "C" attn_status attn_fwd_blocksparse(const void* q, const void* k, const 
     const size_t in_bytes[5] = {qo_bytes, kv_bytes, kv_bytes, ptr_bytes, idx_bytes};
     for (int i = 0; i < 5; ++i)
         if (ins[i] && in_bytes[i] &&
-            (overlaps(o, qo_bytes, ins[i], in_bytes[i]) ||
-             (lse && overlaps(lse, lse_bytes, ins[i], in_bytes[i]))))
+            (ranges_overlap(o, qo_bytes, ins[i], in_bytes[i]) ||
+             (lse && ranges_overlap(lse, lse_bytes, ins[i], in_bytes[i]))))
             return ATTN_ERR_ALIAS;
-    if (lse && overlaps(lse, lse_bytes, o, qo_bytes)) return ATTN_ERR_ALIAS;
+    if (lse && ranges_overlap(lse, lse_bytes, o, qo_bytes)) return ATTN_ERR_ALIAS;
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;

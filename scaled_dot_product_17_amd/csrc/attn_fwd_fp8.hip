@@ -116,12 +116,6 @@ __device__ __forceinline__ int v_swz(int r) {
     return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
 }
 
-__device__ __forceinline__ float wave_swap_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                              false, false);
-    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
-}
-
 __device__ __forceinline__ i32x2 lds_read_tr8(const char* lds, uint32_t off) {
     typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds + off));

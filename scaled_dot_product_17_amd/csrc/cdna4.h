@@ -1,4 +1,4 @@
-// Small gfx950 (CDNA4) device and host helpers shared by the backward kernels:
+// Small gfx950 (CDNA4) device and host helpers shared by the kernels:
 // vector types, buffer descriptors, LDS DMA, the transposing LDS read, cross-
 // half wave reductions, the XCD-aware workgroup order and argument checks.
 #pragma once
@@ -66,6 +66,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// Row max and row sum of an S^T accumulator: lane L and lane L ^ 32 hold the
+// two halves of one query column's values; permlane32 swaps the halves.
+__device__ __forceinline__ float wave_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                              false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
 __device__ __forceinline__ float wave_swap_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
                                               false, false);
