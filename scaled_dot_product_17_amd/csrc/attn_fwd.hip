@@ -334,31 +334,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         const int ent = __builtin_amdgcn_readfirstlane((int)sp[g >> 2]);
         return ((ent >> (14 + (wave >> 2))) & 1) != 0;
     };
-    auto dma_block = [&](const uint16_t* panel, const uint32_t* voff, int ring, int g) {
-        if (g < n_blk_wg) {
-            const int key = SPARSE ? sp_key(g) : kb0 + g * KB;
-            const uint32_t dst = lds_base + ring + (g & 3) * BLK_BYTES + 4 * DMA_PER_WAVE * wave * ROW_BYTES;
-            // the copy's range ends at the sequence's last key (VARLEN) or the
-            // panel's: rows past it are not fetched.  VARLEN and SPARSE zero
-            // those rows of the slot, so no row of an earlier block stays there
-            // (a key outside some row's window or list; the dense path's
-            // leftovers are earlier keys of the same rows' panel)
-            const int end = VARLEN ? s1 : N;
-            if constexpr (VARLEN || SPARSE) {
-                if (key + KB > end) {
-#pragma unroll
-                    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-                        const int row = 4 * DMA_PER_WAVE * wave + 4 * i + (lane >> 4);
-                        if (key + row >= end)
-                            *(u32x4*)(lds + (dst - lds_base) + 4 * i * ROW_BYTES + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-                    }
-                }
-                if (key >= end) return;   // SPARSE: a 32-key part past the end of a short last block
-            }
-            const u32x4 r = sgpr_rsrc(panel + (size_t)(key - kb0) * HD, (uint32_t)(end - key) * ROW_BYTES);
-#pragma unroll
-            for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma16(r, dst + 4 * i * ROW_BYTES, voff[i]);
+    // One descriptor per panel serves every copy, with the block's offset in
+    // soffset.  Its range ends at the last key any block of this workgroup
+    // needs (the sequence's or the panel's end, or the end of the workgroup's
+    // last block).  The buffer unit range-checks voffset + soffset, and a lane
+    // past the range reads nothing and writes zeros to LDS: rows past the end
+    // of a ragged last block arrive as zeros (never as a stale row of an
+    // earlier block), and copies of blocks past the workgroup's last one, which
+    // the pipeline issues without a guard, only clear their slot.
+    const int end = VARLEN ? s1 : N;
+    const int lim = SPARSE ? end : min(end, kb0 + n_blk_wg * KB);
+    const uint32_t lds_wave = lds_base + 4 * DMA_PER_WAVE * wave * ROW_BYTES;
+    const u32x4 k_desc = sgpr_rsrc(kbase, (uint32_t)(lim - kb0) * ROW_BYTES);
+    const u32x4 v_desc = sgpr_rsrc(vbase, (uint32_t)(lim - kb0) * ROW_BYTES);
+    auto dma_block = [&](auto ring_t, auto slot_t, const u32x4& desc, const uint32_t* voff, int g) {
+        constexpr uint32_t DST = decltype(ring_t)::value + decltype(slot_t)::value * BLK_BYTES;
+        uint32_t soff = (uint32_t)g * BLK_BYTES;
+        if constexpr (SPARSE) {
+            if (g >= n_blk_wg) return;   // entries past the union list are not keys
+            soff = (uint32_t)sp_key(g) * ROW_BYTES;
         }
+        lds_dma16_at<DST>(desc, lds_wave, voff[0], soff);
+        if constexpr (DMA_PER_WAVE > 1) lds_dma16_at<DST + 4 * ROW_BYTES>(desc, lds_wave, voff[1], soff);
     };
 
     // ---- per-lane LDS read offsets (relative to a block slot)
@@ -379,17 +376,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     }
 
     // ---- prologue: K blocks 0-2 and V block 0 in flight, then Q into VGPRs
-    if (VARLEN || (SPARSE && N % SP_BLOCK != 0) || N % KB != 0) {
-        // rows past N of the tail block must read as zeros, not stale LDS.  A
-        // block-sparse part past N is not copied at all, which happens only when
-        // N is not a multiple of SP_BLOCK; the union build's scratch lies in K
-        // slot 0, which block 0's copy overwrites before any read.
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < LDS_BYTES / (16 * NTH); ++i)
-            *(u32x4*)(lds + 16 * (tid + NTH * i)) = z;
-        __syncthreads();
-    }
     if constexpr (SAFE) {
         // the zero block masked products run against (first read after the
         // barrier below)
@@ -397,10 +383,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         for (int i = 0; i < BLK_BYTES / (16 * NTH); ++i)
             *(u32x4*)(lds + ZERO_OFF + 16 * (tid + NTH * i)) = u32x4{0u, 0u, 0u, 0u};
     }
-    dma_block(kbase, k_dma, K_RING, 0);
-    dma_block(vbase, v_dma, V_RING, 0);
-    dma_block(kbase, k_dma, K_RING, 1);
-    dma_block(kbase, k_dma, K_RING, 2);
+    using R_K = std::integral_constant<uint32_t, K_RING>;
+    using R_V = std::integral_constant<uint32_t, V_RING>;
+    using S0 = std::integral_constant<uint32_t, 0>;
+    using S1 = std::integral_constant<uint32_t, 1>;
+    using S2 = std::integral_constant<uint32_t, 2>;
+    using S3 = std::integral_constant<uint32_t, 3>;
+    dma_block(R_K{}, S0{}, k_desc, k_dma, 0);
+    dma_block(R_V{}, S0{}, v_desc, v_dma, 0);
+    dma_block(R_K{}, S1{}, k_desc, k_dma, 1);
+    dma_block(R_K{}, S2{}, k_desc, k_dma, 2);
 
     bf16x8 qf[8];   // B operand of S^T = K Q^T, k-steps of 16 head dims
     {
@@ -687,28 +679,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     // blocks 2j+3, 2j+4 and V blocks 2j+1, 2j+2 into slots freed by tile j-1.
     // The loop runs one step past the last block so every wave drains its PV.
     const int n_tiles = n_blk_wg / 2 + 1;
-    auto refill = [&](int j) {
-        dma_block(kbase, k_dma, K_RING, 2 * j + 3);
-        dma_block(kbase, k_dma, K_RING, 2 * j + 4);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 1);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 2);
+    // even j: K blocks 2j+3, 2j+4 in slots 3, 0 and V blocks 2j+1, 2j+2 in
+    // slots 1, 2; odd j: K in slots 1, 2 and V in slots 3, 0
+    auto refill_even = [&](int j) {
+        dma_block(R_K{}, S3{}, k_desc, k_dma, 2 * j + 3);
+        dma_block(R_K{}, S0{}, k_desc, k_dma, 2 * j + 4);
+        dma_block(R_V{}, S1{}, v_desc, v_dma, 2 * j + 1);
+        dma_block(R_V{}, S2{}, v_desc, v_dma, 2 * j + 2);
+    };
+    auto refill_odd = [&](int j) {
+        dma_block(R_K{}, S1{}, k_desc, k_dma, 2 * j + 3);
+        dma_block(R_K{}, S2{}, k_desc, k_dma, 2 * j + 4);
+        dma_block(R_V{}, S3{}, v_desc, v_dma, 2 * j + 1);
+        dma_block(R_V{}, S0{}, v_desc, v_dma, 2 * j + 2);
     };
     // tile 0: step 0 has no previous block
-    refill(0);
+    refill_even(0);
     if (0 <= n_blk) step(std::true_type{}, I1{}, I3{}, 0, sa, sb, pb, pa);
     if (1 <= n_blk) step(F{}, I2{}, I0{}, 1, sb, sa, pa, pb);
     wait_dma();
     __syncthreads();
     for (int j = 1; j < n_tiles; j += 2) {
         // odd tile: blocks 2j = 2 (mod 4), 2j+1 = 3 (mod 4)
-        refill(j);
+        refill_odd(j);
         if (2 * j <= n_blk) step(F{}, I3{}, I1{}, 2 * j, sa, sb, pb, pa);
         if (2 * j + 1 <= n_blk) step(F{}, I0{}, I2{}, 2 * j + 1, sb, sa, pa, pb);
         wait_dma();
         __syncthreads();
         if (j + 1 >= n_tiles) break;
         // even tile: blocks 2j+2 = 0 (mod 4), 2j+3 = 1 (mod 4)
-        refill(j + 1);
+        refill_even(j + 1);
         if (2 * j + 2 <= n_blk) step(F{}, I1{}, I3{}, 2 * j + 2, sa, sb, pb, pa);
         if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb, sa, pa, pb);
         wait_dma();

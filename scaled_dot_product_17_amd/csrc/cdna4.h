@@ -55,6 +55,17 @@ __device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_addr, uint32_t
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
 }
+// LDS DMA of 16 bytes per lane from a fixed descriptor: the buffer unit copies
+// rsrc[soff + voff .. +15] of every lane to LDS byte lds_sbase + IMM + 16*lane.
+// soff (an SGPR) carries the block offset, so one descriptor serves every
+// block of a panel; IMM is a compile-time LDS offset, so m0 is one scalar add.
+template <uint32_t IMM>
+__device__ __forceinline__ void lds_dma16_at(u32x4 rsrc, uint32_t lds_sbase, uint32_t voff,
+                                             uint32_t soff) {
+    asm volatile("s_add_u32 m0, %2, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_sbase), "s"(soff), "i"(IMM)
+                 : "memory", "m0", "scc");
+}
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ds_read_b64_tr_b16: each 16-lane group reads a 4 x 16 block of bf16 and
