@@ -167,7 +167,10 @@ def upload(a):
 
 
 def time_workload(w, steps, warmup):
-    """Returns (ms_per_step wall, mean launch ms from HIP events, per-launch list)."""
+    """Returns (ms_per_step wall, mean launch ms from HIP events, per-launch
+    list): the first two from the K launches issued back to back between two
+    synchronizations (an event pair around them on the launch stream), the
+    list from a second loop with an event pair around every launch."""
     import torch
     import scaled_dot_product_17_amd as sdpa
     q, k, v = w.generate()
@@ -178,21 +181,12 @@ def time_workload(w, steps, warmup):
     for _ in range(warmup):
         sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale, out=o, lse=lse)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale, out=o, lse=lse)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in ev]
+    ms_step, per, mean = _event_loop(
+        lambda: sdpa.fwd(qg, kg, vg, causal=w.causal, scale=w.scale, out=o, lse=lse), steps, stream)
     assert bool(torch.isfinite(lse).all()), "non-finite LSE in the benchmark output"
     del qg, kg, vg, o, lse
     torch.cuda.empty_cache()
-    return wall * 1e3 / steps, float(np.mean(per)), per
+    return ms_step, mean, per
 
 
 def cpu_baseline(w, target_s: float = 12.0):
@@ -278,25 +272,28 @@ def b2b(fn, stream, target_ms: float = 150.0) -> float:
 
 def _event_loop(fn, steps, stream):
     """Times `steps` calls of fn: (wall ms per call, per-call HIP event times in
-    ms, mean ms per call from one event pair around all calls back to back).
-    The last is the launch duration the roofline uses: an event pair around
-    every launch adds microseconds that matter for short kernels."""
+    ms, mean ms per call from one event pair on the stream).  The timed region
+    is the K calls issued back to back between two synchronizations, with one
+    event pair around them (the wall time and the event mean both come from
+    it); the per-call times come from a second loop with an event pair around
+    every call, which adds microseconds between short kernels, so they only
+    give the spread."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        fn()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for _ in range(steps):
         fn()
     b1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     return wall * 1e3 / steps, [a.elapsed_time(b) for a, b in ev], b0.elapsed_time(b1) / steps
 
