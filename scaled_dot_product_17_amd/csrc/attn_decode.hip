@@ -32,6 +32,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn.h"
 #include "cdna4.h"
@@ -145,31 +146,44 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // Q loads done: only DMA counts in vmcnt below
 
-    if (L % KB != 0) {
-        // rows past L of the tail block must read as finite values (zeros)
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < DC_WAVE_LDS / (16 * 64); ++t)
-            *(u32x4*)(lds + wlds + 16 * (lane + 64 * t)) = z;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-
     uint32_t dsrc[8];
 #pragma unroll
     for (int r4 = 0; r4 < 8; ++r4) dsrc[r4] = tile::dma_src(4 * r4, lane);
     static_assert(DC_DMA_PER_BLOCK == 16 && DC_RING >= 1 && DC_RING <= 4,
                   "the vmcnt waits below count 16 DMAs per block, at most 3 blocks ahead");
-    // block g (keys lo + 32g ..) -> ring slot g % DC_RING
+    // block g (keys lo + 32g ..) -> ring slot g % DC_RING.  One K and one V
+    // descriptor for the whole panel, the block offset in soffset: the buffer
+    // unit range-checks voffset + soffset against the panel's L rows, and lanes
+    // past them write zeros to LDS, so the rows past L of a ragged last block
+    // arrive as zeros.
+    const u32x4 rk = sgpr_rsrc(kbase, (uint32_t)L * ROW_BYTES);
+    const u32x4 rv = sgpr_rsrc(vbase, (uint32_t)L * ROW_BYTES);
+    const uint32_t ring0 = lds_base + wlds;
+    auto issue_slot = [&](auto slot_t, uint32_t soff) {
+        constexpr uint32_t KS = decltype(slot_t)::value * BLK_BYTES;
+        constexpr uint32_t VS = KS + DC_RING * BLK_BYTES;
+        lds_dma16_at<KS + 0 * 4 * ROW_BYTES>(rk, ring0, dsrc[0], soff);
+        lds_dma16_at<KS + 1 * 4 * ROW_BYTES>(rk, ring0, dsrc[1], soff);
+        lds_dma16_at<KS + 2 * 4 * ROW_BYTES>(rk, ring0, dsrc[2], soff);
+        lds_dma16_at<KS + 3 * 4 * ROW_BYTES>(rk, ring0, dsrc[3], soff);
+        lds_dma16_at<KS + 4 * 4 * ROW_BYTES>(rk, ring0, dsrc[4], soff);
+        lds_dma16_at<KS + 5 * 4 * ROW_BYTES>(rk, ring0, dsrc[5], soff);
+        lds_dma16_at<KS + 6 * 4 * ROW_BYTES>(rk, ring0, dsrc[6], soff);
+        lds_dma16_at<KS + 7 * 4 * ROW_BYTES>(rk, ring0, dsrc[7], soff);
+        lds_dma16_at<VS + 0 * 4 * ROW_BYTES>(rv, ring0, dsrc[0], soff);
+        lds_dma16_at<VS + 1 * 4 * ROW_BYTES>(rv, ring0, dsrc[1], soff);
+        lds_dma16_at<VS + 2 * 4 * ROW_BYTES>(rv, ring0, dsrc[2], soff);
+        lds_dma16_at<VS + 3 * 4 * ROW_BYTES>(rv, ring0, dsrc[3], soff);
+        lds_dma16_at<VS + 4 * 4 * ROW_BYTES>(rv, ring0, dsrc[4], soff);
+        lds_dma16_at<VS + 5 * 4 * ROW_BYTES>(rv, ring0, dsrc[5], soff);
+        lds_dma16_at<VS + 6 * 4 * ROW_BYTES>(rv, ring0, dsrc[6], soff);
+        lds_dma16_at<VS + 7 * 4 * ROW_BYTES>(rv, ring0, dsrc[7], soff);
+    };
+    static_assert(DC_RING == 2, "issue() picks one of two ring slots");
     auto issue = [&](int g) {
-        const int k0 = lo + g * KB;
-        const uint32_t bytes = (uint32_t)(L - k0) * ROW_BYTES;
-        const u32x4 rk = sgpr_rsrc(kbase + (size_t)k0 * HD, bytes);
-        const u32x4 rv = sgpr_rsrc(vbase + (size_t)k0 * HD, bytes);
-        const uint32_t ks = lds_base + wlds + (uint32_t)(g % DC_RING) * BLK_BYTES;
-#pragma unroll
-        for (int r4 = 0; r4 < 8; ++r4) lds_dma16(rk, ks + r4 * 4 * ROW_BYTES, dsrc[r4]);
-#pragma unroll
-        for (int r4 = 0; r4 < 8; ++r4) lds_dma16(rv, ks + DC_RING * BLK_BYTES + r4 * 4 * ROW_BYTES, dsrc[r4]);
+        const uint32_t soff = (uint32_t)(lo + g * KB) * ROW_BYTES;
+        if (g & 1) issue_slot(std::integral_constant<uint32_t, 1>{}, soff);
+        else issue_slot(std::integral_constant<uint32_t, 0>{}, soff);
     };
 
     tile::Reads rd;
