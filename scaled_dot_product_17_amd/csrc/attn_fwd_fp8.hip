@@ -211,15 +211,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
         k_dma[i] = (uint32_t)(row * ROW8 + ((pc ^ k_swz(row)) << 4));
         v_dma[i] = (uint32_t)(row * ROW8 + ((pc ^ v_swz(row)) << 4));
     }
-    auto dma_block = [&](const uint8_t* panel, const uint32_t* voff, int ring, int g) {
-        if (g < n_blk_wg) {
-            const u32x4 r = sgpr_rsrc(panel + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW8);
-#pragma unroll
-            for (int i = 0; i < DPW; ++i)
-                lds_dma16(r, lds_base + ring + (g & 3) * BLK_BYTES + (8 * DPW * wave + 8 * i) * ROW8,
-                          voff[i]);
-        }
+    // One descriptor per panel for every copy, the block's offset in soffset;
+    // its range ends at the workgroup's last needed key.  The buffer unit
+    // range-checks voffset + soffset, and a lane past the range reads nothing
+    // and writes zeros to LDS: rows past N of a ragged last block arrive as
+    // zeros, and copies of blocks past the workgroup's last one, issued
+    // without a guard, only clear their slot.
+    const int lim = min(N, n_blk_wg * KB);
+    const uint32_t lds_wave = lds_base + 8 * DPW * wave * ROW8;
+    const u32x4 k_desc = sgpr_rsrc(kbase, (uint32_t)lim * ROW8);
+    const u32x4 v_desc = sgpr_rsrc(vbase, (uint32_t)lim * ROW8);
+    auto dma_block = [&](auto ring_t, auto slot_t, const u32x4& desc, const uint32_t* voff, int g) {
+        constexpr uint32_t DST = decltype(ring_t)::value + decltype(slot_t)::value * BLK_BYTES;
+        const uint32_t soff = (uint32_t)g * BLK_BYTES;
+        lds_dma16_at<DST>(desc, lds_wave, voff[0], soff);
+        if constexpr (DPW > 1) lds_dma16_at<DST + 8 * ROW8>(desc, lds_wave, voff[1], soff);
     };
+    using R_K = std::integral_constant<uint32_t, K_RING>;
+    using R_V = std::integral_constant<uint32_t, V_RING>;
+    using S0 = std::integral_constant<uint32_t, 0>;
+    using S1 = std::integral_constant<uint32_t, 1>;
+    using S2 = std::integral_constant<uint32_t, 2>;
+    using S3 = std::integral_constant<uint32_t, 3>;
 
     // ---- per-lane LDS read offsets (relative to a block slot)
     // K: rows 32*sb + l32, chunks 4*ks + 2*hh + u (u = 0, 1) -> bytes 64ks+32hh.. of d
@@ -245,24 +258,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
     }
 
     // ---- prologue
-    if (N % KB != 0) {
-        // never-written rows of a tail block must read as zeros, not stale LDS
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < LDS_BYTES / (16 * NTH); ++i)
-            *(u32x4*)(lds + 16 * (tid + NTH * i)) = z;
-        __syncthreads();
-    }
     if constexpr (SAFE) {
         // the zero block masked products run against (first read after a barrier)
 #pragma unroll
         for (int i = 0; i < BLK_BYTES / (16 * NTH); ++i)
             *(u32x4*)(lds + ZERO_OFF + 16 * (tid + NTH * i)) = u32x4{0u, 0u, 0u, 0u};
     }
-    dma_block(kbase, k_dma, K_RING, 0);
-    dma_block(vbase, v_dma, V_RING, 0);
-    dma_block(kbase, k_dma, K_RING, 1);
-    dma_block(kbase, k_dma, K_RING, 2);
+    dma_block(R_K{}, S0{}, k_desc, k_dma, 0);
+    dma_block(R_V{}, S0{}, v_desc, v_dma, 0);
+    dma_block(R_K{}, S1{}, k_desc, k_dma, 1);
+    dma_block(R_K{}, S2{}, k_desc, k_dma, 2);
 
     i32x8 qf[2];   // B operand of S^T: head dims 64ks + 32hh + 0..31 of this lane's row
     {
@@ -525,25 +530,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
     // V block g-1 (slot (g-1)%4), so during tile j the workgroup refills K
     // blocks 2j+3, 2j+4 and V blocks 2j+1, 2j+2 into slots freed by tile j-1.
     const int n_tiles = n_blk_wg / 2 + 1;
-    auto refill = [&](int j) {
-        dma_block(kbase, k_dma, K_RING, 2 * j + 3);
-        dma_block(kbase, k_dma, K_RING, 2 * j + 4);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 1);
-        dma_block(vbase, v_dma, V_RING, 2 * j + 2);
+    // even j: K blocks 2j+3, 2j+4 in slots 3, 0 and V blocks 2j+1, 2j+2 in
+    // slots 1, 2; odd j: K in slots 1, 2 and V in slots 3, 0
+    auto refill_even = [&](int j) {
+        dma_block(R_K{}, S3{}, k_desc, k_dma, 2 * j + 3);
+        dma_block(R_K{}, S0{}, k_desc, k_dma, 2 * j + 4);
+        dma_block(R_V{}, S1{}, v_desc, v_dma, 2 * j + 1);
+        dma_block(R_V{}, S2{}, v_desc, v_dma, 2 * j + 2);
     };
-    refill(0);
+    auto refill_odd = [&](int j) {
+        dma_block(R_K{}, S1{}, k_desc, k_dma, 2 * j + 3);
+        dma_block(R_K{}, S2{}, k_desc, k_dma, 2 * j + 4);
+        dma_block(R_V{}, S3{}, v_desc, v_dma, 2 * j + 1);
+        dma_block(R_V{}, S0{}, v_desc, v_dma, 2 * j + 2);
+    };
+    refill_even(0);
     if (0 <= n_blk) step(std::true_type{}, I1{}, I3{}, 0, sa, sb2, pb, kb, pa, ka);
     if (1 <= n_blk) step(F{}, I2{}, I0{}, 1, sb2, sa, pa, ka, pb, kb);
     wait_dma();
     __syncthreads();
     for (int j = 1; j < n_tiles; j += 2) {
-        refill(j);
+        refill_odd(j);
         if (2 * j <= n_blk) step(F{}, I3{}, I1{}, 2 * j, sa, sb2, pb, kb, pa, ka);
         if (2 * j + 1 <= n_blk) step(F{}, I0{}, I2{}, 2 * j + 1, sb2, sa, pa, ka, pb, kb);
         wait_dma();
         __syncthreads();
         if (j + 1 >= n_tiles) break;
-        refill(j + 1);
+        refill_even(j + 1);
         if (2 * j + 2 <= n_blk) step(F{}, I1{}, I3{}, 2 * j + 2, sa, sb2, pb, kb, pa, ka);
         if (2 * j + 3 <= n_blk) step(F{}, I2{}, I0{}, 2 * j + 3, sb2, sa, pa, ka, pb, kb);
         wait_dma();
