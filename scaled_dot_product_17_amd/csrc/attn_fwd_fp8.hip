@@ -352,10 +352,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
         ol = mfma8_sb(ones, pw, ol, sb);
     };
     auto lane_max = [&](const f32x16 (&s)[2]) {
-        float mx = fmaxf(s[0][0], s[1][0]);
+        // NaN-propagating maximum: three inputs per v_maximum3_f32 and no
+        // canonicalising moves (fmaxf has to quiet each operand first).  A
+        // NaN score yields NaN here; its row's weights, O and LSE are NaN
+        // whatever the block's scale.
+        float m0 = __builtin_elementwise_maximum(s[0][0], s[1][0]);
+        float m1 = __builtin_elementwise_maximum(s[0][1], s[1][1]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-        return mx;
+        for (int r = 2; r < 16; r += 2) {
+            m0 = __builtin_elementwise_maximum(m0, __builtin_elementwise_maximum(s[0][r], s[1][r]));
+            m1 = __builtin_elementwise_maximum(m1, __builtin_elementwise_maximum(s[0][r + 1], s[1][r + 1]));
+        }
+        return __builtin_elementwise_maximum(m0, m1);
     };
     // weights e = 2^(s*c - mb) times 2^k, as e4m3: byte 16*sb + r = key
     // 32sb + 8(r/4) + 4hh + r%4, and k = floor(log2(448) - the row's largest
