@@ -92,7 +92,8 @@ int attn_decode_ref_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 /*
  * o_part: [rows, n_parts, D] doubles; lse_part: [rows, n_parts] doubles (-inf
  * marks an empty part).  o: [rows, D], lse: [rows] doubles.  A row whose parts
- * are all empty gets O = 0 and LSE = -inf.
+ * are all empty gets O = 0 and LSE = -inf.  A NaN LSE_p makes the row NaN, as
+ * ln sum_p exp(LSE_p) is NaN then.
  * Returns 0, -1 on bad arguments.
  */
 int attn_lse_merge_ref_f64(const double *o_part, const double *lse_part, int64_t rows,
@@ -102,9 +103,17 @@ int attn_lse_merge_ref_f64(const double *o_part, const double *lse_part, int64_t
     for (int64_t r = 0; r < rows; ++r) {
         const double *lp = lse_part + r * n_parts;
         double m = -INFINITY;
-        for (int p = 0; p < n_parts; ++p)
+        int nan_part = 0;
+        for (int p = 0; p < n_parts; ++p) {
+            if (isnan(lp[p])) nan_part = 1;
             if (lp[p] > m) m = lp[p];
+        }
         double *orow = o + r * D;
+        if (nan_part) {
+            for (int d = 0; d < D; ++d) orow[d] = NAN;
+            lse[r] = NAN;
+            continue;
+        }
         for (int d = 0; d < D; ++d) orow[d] = 0.0;
         if (m == -INFINITY) {
             lse[r] = -INFINITY;

@@ -112,7 +112,9 @@ def pin_merge_closed_forms(dref, mref):
     """Equal LSEs a: LSE = a + ln P and O = mean of the parts; LSE agrees with
     numpy's logaddexp; a part 1000 nats above the others is returned unchanged
     (no overflow); a single part is the identity; all-empty rows give O = 0,
-    LSE = -inf."""
+    LSE = -inf; a NaN LSE_p makes its row NaN, as numpy's logaddexp does, also
+    when every other part is empty, and an empty part beside a finite one is
+    left out."""
     rng = np.random.default_rng(7)
     op = rng.standard_normal((5, 3, 8))
     lp = np.full((5, 3), 1.5)
@@ -132,6 +134,15 @@ def pin_merge_closed_forms(dref, mref):
     assert np.array_equal(o4, op3[:, 0]) and np.array_equal(l4, lp3[:, 0]), "single part"
     o5, l5 = mref(np.zeros((2, 2, 8)), np.full((2, 2), -np.inf))
     assert np.all(o5 == 0) and np.all(l5 == -np.inf), "all-empty row"
+    lp6 = np.array([[np.nan, -np.inf], [0.5, np.nan], [-np.inf, 0.5]])
+    op6 = rng.standard_normal((3, 2, 8))
+    op6[2, 0] = 0.0
+    o6, l6 = mref(op6, lp6)
+    ref6 = np.logaddexp.reduce(lp6, axis=1)
+    assert np.array_equal(np.isnan(l6), np.isnan(ref6)) and np.isnan(l6[:2]).all(), "NaN part LSE"
+    assert np.isnan(o6[:2]).all() and np.isfinite(o6[2]).all(), "NaN part O"
+    close(o6[2], op6[2, 1], what="empty part beside a finite one")
+    close(l6[2:], [0.5], tol=1e-15, what="LSE beside an empty part")
 
 
 def pin_merge_permutation(dref, mref):

@@ -28,8 +28,9 @@ MUTATIONS = {
     "merge_lse_log2": ("const double L = m + log(total);", "const double L = m + log2(total);"),
     "merge_first_part_only": ("for (int p = 0; p < n_parts; ++p) {\n            const double w",
                               "for (int p = 0; p < 1; ++p) {\n            const double w"),
-    "merge_max_ignores_last": ("for (int p = 0; p < n_parts; ++p)\n            if (lp[p] > m) m = lp[p];",
-                               "for (int p = 0; p + 1 < n_parts; ++p)\n            if (lp[p] > m) m = lp[p];"),
+    "merge_max_ignores_last": ("for (int p = 0; p < n_parts; ++p) {\n            if (isnan(lp[p])) nan_part = 1;",
+                               "for (int p = 0; p + 1 < n_parts; ++p) {\n            if (isnan(lp[p])) nan_part = 1;"),
+    "merge_drops_nan_part": ("if (isnan(lp[p])) nan_part = 1;", "if (0) nan_part = 1;"),
 }
 
 
