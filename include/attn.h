@@ -309,6 +309,10 @@ size_t attn_bwd_workspace_bytes(int B, int H_q, int H_kv, int N, int D, int caus
  * Precision: scores and P V accumulate in fp32 on the matrix cores with P
  * rounded to bf16; each partial O is divided by the sum of the bf16 weights
  * it applied; partials and the merge are fp32; O is rounded to bf16 once.
+ * Non-finite inputs propagate as the formula does: a NaN or +inf score, or
+ * scores that are all -inf, make the row's O and LSE NaN; a non-finite V
+ * element reaches exactly the rows that see its key (keys a row does not see
+ * never enter its products).
  * Errors as for attn_fwd, plus ATTN_ERR_WORKSPACE.  q, k, v and workspace must
  * be 16-byte aligned, o and lse 4-byte aligned.
  */
@@ -350,9 +354,11 @@ attn_status attn_decode_noalloc(const void* q, const void* k, const void* v, voi
  *
  * o_part   device pointer, fp32 [B*H_q*M, n_splits, D], 16-byte aligned,
  *          written: each split's softmax-weighted mean of V over its allowed
- *          keys (0 where it has none).
+ *          keys (0 where it has none; where they all scored -inf, the sum of
+ *          0 * V over them: 0, or NaN where such a V element is not finite).
  * lse_part device pointer, fp32 [B*H_q*M, n_splits], written: each split's
- *          natural-log LSE (-inf where it has no allowed key).
+ *          natural-log LSE (-inf where it has no allowed key or they all
+ *          scored -inf; NaN where one scored NaN or +inf).
  * Other arguments as for attn_decode.
  */
 attn_status attn_decode_partial(const void* q, const void* k, const void* v, float* o_part,
@@ -375,11 +381,14 @@ size_t attn_decode_workspace_bytes(int B, int H_q, int H_kv, int M, int L, int D
  * also the step that merges per-GPU partials when keys are sharded.
  *
  * o_part   device pointer, fp32 [rows, n_parts, D], 16-byte aligned.
- * lse_part device pointer, fp32 [rows, n_parts]; -inf marks a part with no keys
- *          (its O_p must be finite; it gets weight 0).
+ * lse_part device pointer, fp32 [rows, n_parts]; -inf marks a part of weight
+ *          0 (no keys, or keys that all scored -inf): its O_p is multiplied
+ *          by that 0, so a NaN there reaches O.  A NaN or +inf LSE_p makes
+ *          the row's O and LSE NaN.
  * o        device pointer, bf16 [rows, D], written (round to nearest even).
  * lse      device pointer, fp32 [rows], written, or NULL.  A row whose parts
- *          are all empty gets O = 0 and LSE = -inf.
+ *          are all -inf gets O = 0 and LSE = -inf (attn_decode, whose rows
+ *          always have keys, makes such a row NaN instead).
  * D        128 in this build.
  */
 attn_status attn_lse_merge(const float* o_part, const float* lse_part, int rows, int n_parts,

@@ -75,10 +75,14 @@ struct DecParams {
     float lse_scale;   // |scale|
 };
 
-__device__ __forceinline__ float wave_max_all(float x) {
+// NaN-propagating maximum over the wave
+__device__ __forceinline__ float wave_maximum_all(float x) {
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+    for (int s = 32; s >= 1; s >>= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, s));
     return x;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 __device__ __forceinline__ float wave_sum_all(float x) {
 #pragma unroll
@@ -119,8 +123,18 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
     const int klim = !col_ok ? -1 : (p.causal ? L - M + i : L - 1);   // last key it sees
     const int lo = (int)((int64_t)split * p.n_blocks / p.n_splits) * KB;
     const int hi = min(L, (int)((int64_t)(split + 1) * p.n_blocks / p.n_splits) * KB);
-    // keys any column of the wave sees end at kmax; blocks past it are skipped
-    const int kmax = __builtin_amdgcn_readfirstlane((int)wave_max_all((float)klim));
+    // keys any column of the wave sees end at kmax; blocks past it are skipped.
+    // Keys up to kmin are seen by every column of the wave; a key past kmin is
+    // hidden from some column (bottom-right causal mask, or past the cache).
+    // The wave's columns c0..c1 hold rows col % M: one run of residues, all
+    // of them once it has M columns or wraps past a multiple of M.
+    int kmin = L - 1, kmax = L - 1;
+    if (p.causal) {
+        const int c0 = cb * 32, c1 = min(c0 + 31, p.gm - 1);
+        const bool all_rows = c1 - c0 + 1 >= M || c0 / M != c1 / M;
+        kmin = L - M + (all_rows ? 0 : c0 % M);
+        kmax = L - M + (all_rows ? M - 1 : c1 % M);
+    }
     const int last = min(hi - 1, kmax);
     const int nb = last >= lo ? (last - lo) / KB + 1 : 0;
 
@@ -144,7 +158,25 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
             qf[ks] = __builtin_bit_cast(bf16x8, (x & keep) ^ (flip & keep));
         }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // Q loads done: only DMA counts in vmcnt below
+    // Keys past kmin in the wave's blocks meet a 0 weight for some column, and
+    // the matrix core makes 0 * inf and 0 * NaN NaN, a product the formula
+    // never takes.  Their V rows (the last ones of a causal cache, or past
+    // the wave's last key) are checked here; only when one holds a non-finite
+    // element does the wave take them out of the product (exact).
+    bool exact = false;
+    {
+        const int j0 = max(lo, kmin + 1);
+        const int j1 = min(lo + nb * KB, L) - 1;
+        uint32_t bad = 0u;
+        for (int idx = lane; idx < (j1 - j0 + 1) * 16; idx += 64) {
+            const u32x4 x = *(const u32x4*)(vbase + (size_t)(j0 + (idx >> 4)) * HD + 8 * (idx & 15));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bad |= (uint32_t)((x[e] & 0x7F80u) == 0x7F80u) | (uint32_t)((x[e] & 0x7F800000u) == 0x7F800000u);
+        }
+        exact = __builtin_amdgcn_ballot_w64(bad != 0u) != 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // Q and check loads done: only DMA counts in vmcnt below
 
     uint32_t dsrc[8];
 #pragma unroll
@@ -199,7 +231,10 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
 #pragma unroll
     for (int g = 0; g < DC_RING; ++g)
         if (g < nb) issue(g);
-    for (int g = 0; g < nb; ++g) {
+    // One pass over block g.  EX: the exact form for a block with keys past
+    // kmin (a separate copy, so the common loop body stays one basic block).
+    auto block = [&](int g, auto ex_t) {
+        constexpr bool EX = decltype(ex_t)::value;
         // block g has landed once at most (blocks issued after it) * 16 DMAs are pending
         const int ahead = min(nb - 1 - g, DC_RING - 1);
         if (ahead >= 3) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
@@ -212,7 +247,8 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(lds, ks, kk), qf[kk], s, 0, 0, 0);
-        const int kb0 = lo + g * KB + 4 * hh;
+        const int kb = lo + g * KB;
+        const int kb0 = kb + 4 * hh;
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -244,6 +280,24 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        // exact: in a block with keys past kmin (rows r0.. of the block) their
+        // V rows are cleared in this wave's LDS before the product and their
+        // weights taken out of O's divisor; the epilogue adds their terms for
+        // the columns that see them.
+        if constexpr (EX) {
+            const int r0 = max(0, kmin + 1 - kb);
+            for (int idx = (r0 << 4) + lane; idx < KB * 16; idx += 64)
+                *(u32x4*)(lds + vs + 16 * idx) = u32x4{0u, 0u, 0u, 0u};
+            float hid = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                const uint32_t w2 = pw[r >> 3][(r & 7) >> 1];
+                const float w = bf16_bits_to_f32((uint16_t)((r & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)));
+                hid += kr >= r0 ? w : 0.f;
+            }
+            lb -= hid;
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -254,16 +308,69 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
         m = m_new;
         // the ring slot of block g is free once its MFMAs have their operands
         if (g + DC_RING < nb) issue(g + DC_RING);
+    };
+    // an exact wave runs the blocks from the first one with a key past kmin
+    // in the exact form (the blocks wholly at or below kmin come first)
+    const int n_common = exact ? min(nb, max(0, kmin + 1 - lo) / KB) : nb;
+    for (int g = 0; g < n_common; ++g) block(g, std::false_type{});
+    for (int g = n_common; g < nb; ++g) block(g, std::true_type{});
+
+    // exact: the terms of the keys past kmin that a column sees, against the
+    // final reference: the raw score again on the vector unit (this lane's 64
+    // head dims of q, the partner lane's other 64), its weight rounded to bf16
+    // as the product's weights are, counted in O's divisor.
+    const int j_end = min(hi - 1, kmax);
+    if (exact && nb > 0 && kmin < j_end) {   // wave-uniform
+        const float mbf = m == -INFINITY ? 0.f : m * c;
+        for (int j = max(lo, kmin + 1); j <= j_end; ++j) {
+            const uint16_t* krow = kbase + (size_t)j * HD;
+            float sd = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4 x = *(const u32x4*)(krow + 16 * ks + 8 * hh);
+                const u32x4 y = __builtin_bit_cast(u32x4, qf[ks]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sd = fmaf(bf16_bits_to_f32((uint16_t)(y[e] & 0xFFFFu)),
+                              bf16_bits_to_f32((uint16_t)(x[e] & 0xFFFFu)), sd);
+                    sd = fmaf(bf16_bits_to_f32((uint16_t)(y[e] >> 16)),
+                              bf16_bits_to_f32((uint16_t)(x[e] >> 16)), sd);
+                }
+            }
+            sd = wave_swap_sum(sd);
+            const bool sees = klim >= j;
+            const float pb = (float)(__bf16)__builtin_amdgcn_exp2f(fmaf(sd, c, -mbf));
+            if (sees && hh == 0) lb += pb;
+            const uint16_t* vrow = vbase + (size_t)j * HD + 4 * hh;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const uint2 x = *(const uint2*)(vrow + 32 * db + 8 * r4);
+                    const int r = 4 * r4;
+                    const float v0 = bf16_bits_to_f32((uint16_t)(x.x & 0xFFFFu));
+                    const float v1 = bf16_bits_to_f32((uint16_t)(x.x >> 16));
+                    const float v2 = bf16_bits_to_f32((uint16_t)(x.y & 0xFFFFu));
+                    const float v3 = bf16_bits_to_f32((uint16_t)(x.y >> 16));
+                    o[db][r + 0] = sees ? fmaf(pb, v0, o[db][r + 0]) : o[db][r + 0];
+                    o[db][r + 1] = sees ? fmaf(pb, v1, o[db][r + 1]) : o[db][r + 1];
+                    o[db][r + 2] = sees ? fmaf(pb, v2, o[db][r + 2]) : o[db][r + 2];
+                    o[db][r + 3] = sees ? fmaf(pb, v3, o[db][r + 3]) : o[db][r + 3];
+                }
+        }
     }
 
-    // partial O = O^T / sum bf16(p) and LSE = m*|scale| + ln(sum p); a column
-    // that saw no key of this split gets O = 0 and LSE = -inf
+    // partial O = O^T / sum bf16(p) and LSE = m*|scale| + ln(sum p).  A column
+    // with no key in this split gets O = 0 and LSE = -inf; one whose keys all
+    // scored -inf gets LSE = -inf and O = sum 0 * v (0, or NaN where such a
+    // key's V is not finite: the formula's terms); a NaN or +inf score makes
+    // the sum, so the LSE and O, NaN.
     const float l_tot = wave_swap_sum(l);
     const float lb_tot = wave_swap_sum(lb);
     if (col_ok) {
         const size_t row = ((size_t)b * p.Hq + h) * (size_t)M + i;
         const size_t part = row * p.n_splits + split;
-        const bool any = l_tot > 0.f;
+        const bool any = !(l_tot == 0.f);
         const float inv = any ? 1.0f / lb_tot : 0.f;
         float* orow = p.o_part + part * HD;
 #pragma unroll
@@ -286,33 +393,39 @@ __global__ __launch_bounds__(DC_THREADS, 1) void attn_decode_split_kernel(DecPar
 constexpr int MG_THREADS = 256;
 constexpr int MG_GROUPS = MG_THREADS / 32;
 
+// is_max: NaN-propagating maximum (a NaN LSE_p makes the row NaN)
 __device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
-    x = is_max ? wave_max_all(x) : wave_sum_all(x);
+    x = is_max ? wave_maximum_all(x) : wave_sum_all(x);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = x;
     __syncthreads();
     float r = red[0];
 #pragma unroll
-    for (int i = 1; i < MG_THREADS / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+    for (int i = 1; i < MG_THREADS / 64; ++i)
+        r = is_max ? __builtin_elementwise_maximum(r, red[i]) : r + red[i];
     __syncthreads();
     return r;
 }
 
+// keyed_rows: every row has at least one allowed key (decode), so parts that
+// all have LSE -inf mean keys that all scored -inf: the formula's NaN.
+// Without it such a row counts as having no keys: O = 0, LSE = -inf.
 __global__ __launch_bounds__(MG_THREADS) void attn_lse_merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, int n_parts,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int keyed_rows) {
     __shared__ float red[MG_THREADS / 64];
     __shared__ f32x4 part[MG_GROUPS][32];
     const int t = threadIdx.x;
     const size_t row = blockIdx.x;
     const float* lp = lse_part + row * n_parts;
     float mx = -INFINITY;
-    for (int s = t; s < n_parts; s += MG_THREADS) mx = fmaxf(mx, lp[s]);
+    for (int s = t; s < n_parts; s += MG_THREADS) mx = __builtin_elementwise_maximum(mx, lp[s]);
     mx = block_reduce(mx, red, true);
     uint16_t* orow = o + row * HD;
-    if (mx == -INFINITY) {   // no part has a key: O = 0, LSE = -inf
-        if (t < HD / 2) *(uint32_t*)(orow + 2 * t) = 0u;
-        if (t == 0 && lse) lse[row] = -INFINITY;
+    if (mx == -INFINITY) {
+        const uint32_t fill = keyed_rows ? 0x7FC07FC0u : 0u;   // bf16 NaN pairs, or zeros
+        if (t < HD / 2) *(uint32_t*)(orow + 2 * t) = fill;
+        if (t == 0 && lse) lse[row] = keyed_rows ? __builtin_nanf("") : -INFINITY;
         return;
     }
     float tot = 0.f;
@@ -392,10 +505,10 @@ attn_status check_decode_shape(int B, int H_q, int H_kv, int M, int L, int D, in
 }
 
 attn_status launch_merge(const float* o_part, const float* lse_part, int rows, int n_parts,
-                         void* o, float* lse, hipStream_t s) {
+                         void* o, float* lse, bool keyed_rows, hipStream_t s) {
     if (rows == 0) return ATTN_OK;
     hipLaunchKernelGGL(attn_lse_merge_kernel, dim3((unsigned)rows), dim3(MG_THREADS), 0, s,
-                       o_part, lse_part, n_parts, (uint16_t*)o, lse);
+                       o_part, lse_part, n_parts, (uint16_t*)o, lse, keyed_rows ? 1 : 0);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -504,7 +617,7 @@ extern "C" attn_status attn_decode(const void* q, const void* k, const void* v, 
     const hipStream_t s = (hipStream_t)stream;
     st = launch_split(p, s);
     if (st != ATTN_OK) return st;
-    return launch_merge(p.o_part, p.lse_part, (int)pl.rows, pl.n_splits, o, lse, s);
+    return launch_merge(p.o_part, p.lse_part, (int)pl.rows, pl.n_splits, o, lse, true, s);
 }
 
 extern "C" attn_status attn_decode_noalloc(const void* q, const void* k, const void* v, void* o,
@@ -531,7 +644,7 @@ extern "C" attn_status attn_decode_noalloc(const void* q, const void* k, const v
     const hipStream_t s = (hipStream_t)stream;
     st = launch_split(p, s);
     if (st != ATTN_OK) return st;
-    return launch_merge(p.o_part, p.lse_part, (int)pl.rows, pl.n_splits, o, lse, s);
+    return launch_merge(p.o_part, p.lse_part, (int)pl.rows, pl.n_splits, o, lse, true, s);
 }
 
 extern "C" attn_status attn_decode_partial(const void* q, const void* k, const void* v,
@@ -570,7 +683,7 @@ extern "C" attn_status attn_lse_merge(const float* o_part, const float* lse_part
         return ATTN_ERR_ALIAS;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
-    return launch_merge(o_part, lse_part, rows, n_parts, o, lse, (hipStream_t)stream);
+    return launch_merge(o_part, lse_part, rows, n_parts, o, lse, false, (hipStream_t)stream);
 }
 
 extern "C" double attn_decode_flops(int B, int H_q, int M, int L, int D, int causal) {

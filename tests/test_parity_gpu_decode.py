@@ -142,6 +142,34 @@ def test_lse_merge_kernel():
         assert np.all(og[~fin] == 0)
 
 
+def test_lse_merge_nonfinite_parts():
+    """A NaN LSE_p makes its row NaN, beside finite and beside empty parts (the
+    merge oracle's IEEE reading); an empty part (LSE -inf, O 0) beside finite
+    ones is left out; a row of empty parts is O = 0, LSE = -inf."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    rng = np.random.default_rng(6)
+    rows, P = 6, 5
+    op = rng.standard_normal((rows, P, 128)).astype(np.float32)
+    lp = (rng.standard_normal((rows, P)) * 4).astype(np.float32)
+    lp[0, 2] = np.nan                      # NaN beside finite parts
+    lp[1, :] = -np.inf; op[1] = 0; lp[1, 3] = np.nan   # NaN beside empty parts
+    lp[2, :] = -np.inf; op[2] = 0          # all empty
+    lp[3, 1:] = -np.inf; op[3, 1:] = 0     # one finite part, the rest empty
+    lp[4, 0] = np.inf                      # +inf: exp(inf - inf) is NaN
+    o, lse = sdpa.lse_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda())
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_lse_merge_ref(op.astype(np.float64), lp.astype(np.float64))
+    og = bf16_to_np(o).astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    for name, g, r in (("O", og, o_ref), ("LSE", lg, lse_ref)):
+        for kind, f in (("NaN", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+            assert np.array_equal(f(g), f(r)), f"merge {name} {kind} pattern {f(g)} vs {f(r)}"
+    assert np.isnan(lg[[0, 1, 4]]).all() and lg[2] == -np.inf and np.all(og[2] == 0)
+    fin = np.isfinite(o_ref)
+    assert np.all(np.abs(og[fin] - o_ref[fin]) <= 2.0 ** -8 * np.abs(o_ref[fin]) + 1e-5 * 4)
+
+
 def test_decode_partial_then_merge():
     """attn_decode_partial's splits match the oracle over their key ranges, and
     merging them with attn_lse_merge reproduces attn_decode bitwise."""
