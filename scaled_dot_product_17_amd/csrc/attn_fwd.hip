@@ -124,30 +124,15 @@ __device__ __forceinline__ uint32_t v_lds_off(int row, int chunk) {
     return (uint32_t)(row * ROW_BYTES + ((chunk ^ ((row & 3) << 2)) << 4));
 }
 
-// SAFE = false: the fast kernel.  SAFE = true: the exact kernel, which redoes
-// only the workgroups the fast kernel marked (see NF_MARK).
-template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW, bool SAFE>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
-    static_assert(NW == 8 || NW == 4, "workgroups of 4 or 8 waves");
-    constexpr int BRW = 32 * NW;                 // query rows of this workgroup
-    constexpr int NTH = NW * 64;
-    constexpr int DMA_PER_WAVE = 32 / (4 * NW);  // 4-row DMA instructions per wave per key block
-    constexpr int QB_WG = BRW / SP_BLOCK;        // SPARSE: query blocks per workgroup (1 or 2)
-    constexpr int SP_PER_T = SP_MAX / NTH;       // SPARSE: key blocks each thread compacts
-    constexpr int ZERO_OFF = LDS_BYTES + (SPARSE ? SP_BYTES : 0);   // exact kernel: a block of zeros
-    constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;                     // exact kernel: per-wave saved blocks
-    __shared__ __attribute__((aligned(1024))) char lds[ZERO_OFF + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;   // query column owned by this lane
-    const int hh = lane >> 5;    // which half of the wave
-
-    // ---- which (batch, head, query tile) this workgroup computes.  VARLEN: the
-    // batch index is the sequence of a packed batch (B = 1, N = all tokens).
-    const int logical = xcd_remap(blockIdx.x, p.total);
-    int bh, qt;
+// Which (batch, head, query tile) workgroup id bid computes, and the token
+// range [s0, s1) of its sequence (the whole panel when dense).  VARLEN: the
+// batch index is the sequence of a packed batch (B = 1, N = all tokens).
+// false: bid is padding of the grid or past its sequence's end.
+template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW>
+__device__ __forceinline__ bool tile_of(const Params& p, int bid, int& b, int& h, int& qt, int& s0, int& s1) {
+    constexpr int BRW = 32 * NW;
+    const int logical = xcd_remap(bid, p.total);
+    int bh;
     if (VARLEN && p.n_seq > 1 && p.dealt) {
         // several sequences of unequal lengths: groups of cgroup (sequence,
         // head)s, each group's tiles tile-major with the heaviest first, so a
@@ -157,12 +142,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         // heads and the XCDs finish together.
         const int per = p.B * p.Hq;
         const int G = p.cgroup > 1 ? p.cgroup : 1;
-        const int x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+        const int x = bid & 7, sx = bid >> 3;
         const int k = sx / (G * p.n_qtiles);
         const int r = sx - k * G * p.n_qtiles;
         const int grp = x + 8 * k;
         const int gh = min(G, per - grp * G);   // heads in this group (the last may be short)
-        if (gh <= 0 || r >= gh * p.n_qtiles) return;   // padding of the grid: no barrier yet
+        if (gh <= 0 || r >= gh * p.n_qtiles) return false;   // padding of the grid
         qt = p.n_qtiles - 1 - r / gh;
         bh = grp * G + r % gh;
     } else if (CAUSAL && !SPARSE) {
@@ -185,17 +170,45 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         qt = logical % p.n_qtiles;
         if (CAUSAL) qt = p.n_qtiles - 1 - qt;   // heaviest tiles of a head first
     }
-    const int b = bh / p.Hq;
-    const int h = bh % p.Hq;
+    b = bh / p.Hq;
+    h = bh % p.Hq;
+    // rows [s0, s1) of the panel form this tile's sequence (the whole panel when dense)
+    s0 = 0;
+    s1 = p.N;
+    if constexpr (VARLEN) {
+        s0 = min(max(p.cu[b], 0), p.N);
+        s1 = min(max(p.cu[b + 1], s0), p.N);
+        if (qt * BRW >= s1 - s0) return false;   // past this sequence's end
+    }
+    return true;
+}
+
+// One query tile (workgroup id bid).  SAFE = false: the fast kernel's body.
+// SAFE = true: the exact form, for the tiles the fast kernel marked (see
+// NF_MARK).
+template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW, bool SAFE>
+__device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
+    static_assert(NW == 8 || NW == 4, "workgroups of 4 or 8 waves");
+    constexpr int BRW = 32 * NW;                 // query rows of this workgroup
+    constexpr int NTH = NW * 64;
+    constexpr int DMA_PER_WAVE = 32 / (4 * NW);  // 4-row DMA instructions per wave per key block
+    constexpr int QB_WG = BRW / SP_BLOCK;        // SPARSE: query blocks per workgroup (1 or 2)
+    constexpr int SP_PER_T = SP_MAX / NTH;       // SPARSE: key blocks each thread compacts
+    constexpr int ZERO_OFF = LDS_BYTES + (SPARSE ? SP_BYTES : 0);   // exact kernel: a block of zeros
+    constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;                     // exact kernel: per-wave saved blocks
+    __shared__ __attribute__((aligned(1024))) char lds[ZERO_OFF + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;   // query column owned by this lane
+    const int hh = lane >> 5;    // which half of the wave
+
+    // ---- which (batch, head, query tile) this workgroup computes
+    int b, h, qt, s0, s1;
+    if (!tile_of<CAUSAL, VARLEN, SPARSE, NW>(p, bid, b, h, qt, s0, s1)) return;   // whole workgroup, no barrier yet
     const int kvh = h / p.group;
     const int N = p.N;
-    // rows [s0, s1) of the panel form this tile's sequence (the whole panel when dense)
-    int s0 = 0, s1 = N;
-    if constexpr (VARLEN) {
-        s0 = min(max(p.cu[b], 0), N);
-        s1 = min(max(p.cu[b + 1], s0), N);
-        if (qt * BRW >= s1 - s0) return;   // past this sequence's end: whole workgroup, no barrier yet
-    }
     const int q0 = s0 + qt * BRW;
     const int wq0 = q0 + wave * 32;       // first query row of this wave
     const int myq = wq0 + l32;            // query row of this lane
@@ -818,6 +831,42 @@ void set_scale(Params& p, float scale) {
     p.lse_scale = mag;
 }
 
+// SAFE = false: the fast kernel, one workgroup per tile.  SAFE = true: the
+// exact kernel on a small grid (at most EXACT_GRID workgroups): each thread
+// checks one tile's mark, and each workgroup redoes its marked tiles one after
+// another (most launches mark none, so most workgroups only read marks).
+constexpr int EXACT_GRID = 256;
+template <bool CAUSAL, bool VARLEN, bool SPARSE, int NW, bool SAFE>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
+    if constexpr (!SAFE) {
+        fwd_tile<CAUSAL, VARLEN, SPARSE, NW, false>(p, blockIdx.x);
+    } else {
+        constexpr int NTH = NW * 64;
+        __shared__ int marked[NTH];
+        __shared__ int n_marked;
+        const int t = threadIdx.x;
+        if (t == 0) n_marked = 0;
+        __syncthreads();
+        const int bid = blockIdx.x + t * gridDim.x;   // gridDim.x * NTH >= p.total
+        int b, h, qt, s0, s1;
+        if (bid < p.total && tile_of<CAUSAL, VARLEN, SPARSE, NW>(p, bid, b, h, qt, s0, s1)) {
+            const size_t qo_panel = ((size_t)(VARLEN ? 0 : b) * p.Hq + h) * (size_t)p.N * HD;
+            const u32x4 w = *(const u32x4*)(p.o + qo_panel + (size_t)(s0 + qt * 32 * NW) * HD);
+            if (w[0] == NF_MARK[0] && w[1] == NF_MARK[1] && w[2] == NF_MARK[2] && w[3] == NF_MARK[3])
+                marked[atomicAdd(&n_marked, 1)] = bid;
+        }
+        __syncthreads();
+        const int n = n_marked;
+        for (int i = 0; i < n; ++i) {
+            fwd_tile<CAUSAL, VARLEN, SPARSE, NW, true>(p, marked[i]);
+            // the next tile reuses the LDS: copies still in flight (the pipeline
+            // issues some past a tile's last block) land first
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    }
+}
+
 template <bool VARLEN, bool SPARSE, int NW = NWAVE>
 attn_status launch_fwd(const Params& p, bool causal, void* stream) {
     hipStream_t s = (hipStream_t)stream;
@@ -825,12 +874,13 @@ attn_status launch_fwd(const Params& p, bool causal, void* stream) {
     // workgroups the fast kernel marked (a NaN or infinity in the V rows of a
     // masked block) and every other workgroup of it exits at once
     const dim3 grid((unsigned)p.total), block(NW * 64);
+    const dim3 egrid((unsigned)std::max(std::min(p.total, EXACT_GRID), (p.total + NW * 64 - 1) / (NW * 64)));
     if (causal) {
         hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW, false>), grid, block, 0, s, p);
-        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<true, VARLEN, SPARSE, NW, true>), egrid, block, 0, s, p);
     } else {
         hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW, false>), grid, block, 0, s, p);
-        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<false, VARLEN, SPARSE, NW, true>), egrid, block, 0, s, p);
     }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
