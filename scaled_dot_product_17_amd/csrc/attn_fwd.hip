@@ -858,7 +858,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         __syncthreads();
         const int n = n_marked;
         for (int i = 0; i < n; ++i) {
-            fwd_tile<CAUSAL, VARLEN, SPARSE, NW, true>(p, marked[i]);
+            fwd_tile<CAUSAL, VARLEN, SPARSE, NW, true>(p, __builtin_amdgcn_readfirstlane(marked[i]));
             // the next tile reuses the LDS: copies still in flight (the pipeline
             // issues some past a tile's last block) land first
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

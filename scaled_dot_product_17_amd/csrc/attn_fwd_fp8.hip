@@ -132,27 +132,11 @@ __device__ __forceinline__ f32x16 mfma8_sb(const i32x8& a, const i32x8& b, const
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
-// NW waves per workgroup (8, or 4 for short sequences: twice the workgroups,
-// two per CU, not tied by one barrier).  SAFE = false: the fast kernel;
-// SAFE = true: the exact kernel, which redoes only the workgroups the fast
-// kernel marked (a NaN code in the V rows of a masked block; see NF_MARK).
-template <bool CAUSAL, int NW, bool SAFE>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p) {
-    constexpr int BRW = 32 * NW;      // query rows of this workgroup
-    constexpr int NTH = NW * 64;
-    constexpr int DPW = 8 / NW;       // 8-row DMA instructions per wave per key block
-    constexpr int ZERO_OFF = LDS_BYTES;                 // exact kernel: a block of zeros
-    constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;      // exact kernel: per-wave saved blocks
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;   // query column owned by this lane
-    const int hh = lane >> 5;    // which half of the wave
-
-    const int logical = xcd_remap(blockIdx.x, p.total);
-    int bh, qt;
+// Which (batch, head, query tile) workgroup id bid computes.
+template <bool CAUSAL, int NW>
+__device__ __forceinline__ void tile_of(const Params& p, int bid, int& b, int& h, int& qt) {
+    const int logical = xcd_remap(bid, p.total);
+    int bh;
     if (CAUSAL) {
         // groups of cgroup heads one after another (a group's tiles share K/V in
         // one XCD's L2), tile-major and heaviest tile first within a group; a
@@ -169,8 +153,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
         bh = logical / p.n_qtiles;
         qt = logical % p.n_qtiles;
     }
-    const int b = bh / p.Hq;
-    const int h = bh % p.Hq;
+    b = bh / p.Hq;
+    h = bh % p.Hq;
+}
+
+// One query tile (workgroup id bid).  NW waves per workgroup (8, or 4 for
+// short sequences: twice the workgroups, two per CU, not tied by one barrier).
+// SAFE = false: the fast kernel's body; SAFE = true: the exact form, for the
+// tiles the fast kernel marked (a NaN code in the V rows of a masked block;
+// see NF_MARK).
+template <bool CAUSAL, int NW, bool SAFE>
+__device__ __forceinline__ void fwd8_tile(const Params& p, const int bid) {
+    constexpr int BRW = 32 * NW;      // query rows of this workgroup
+    constexpr int NTH = NW * 64;
+    constexpr int DPW = 8 / NW;       // 8-row DMA instructions per wave per key block
+    constexpr int ZERO_OFF = LDS_BYTES;                 // exact kernel: a block of zeros
+    constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;      // exact kernel: per-wave saved blocks
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;   // query column owned by this lane
+    const int hh = lane >> 5;    // which half of the wave
+
+    int b, h, qt;
+    tile_of<CAUSAL, NW>(p, bid, b, h, qt);
+    // workgroup-uniform (said so, so the copy descriptors stay scalar)
+    b = __builtin_amdgcn_readfirstlane(b);
+    h = __builtin_amdgcn_readfirstlane(h);
+    qt = __builtin_amdgcn_readfirstlane(qt);
     const int kvh = h / p.group;
     const int N = p.N;
     const int q0 = qt * BRW;
@@ -487,11 +499,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
     // global memory for a NaN code (e4m3 has no infinity)
     uint32_t nf_bits = 0u;
     if (!SAFE && n_blk > 0) {
+        // one descriptor for the panel, the block in the offset: rows past N read as zeros
+        const __amdgpu_buffer_rsrc_t vpanel = make_rsrc(vbase, (uint32_t)N * ROW8);
         auto vcheck = [&](int g) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(vbase + (size_t)g * KB * HD, (uint32_t)(N - g * KB) * ROW8);
 #pragma unroll
             for (int i = 0; i < BLK_BYTES / 1024; ++i) {
-                const u32x4 x = buf_load16(r, (uint32_t)(16 * lane + 1024 * i));
+                const u32x4 x = buf_load16(vpanel, (uint32_t)(g * BLK_BYTES + 16 * lane + 1024 * i));
                 // a byte with all seven low bits set (0x7F, 0xFF) carries into its top bit
 #pragma unroll
                 for (int e = 0; e < 4; ++e) nf_bits |= (x[e] & 0x7F7F7F7Fu) + 0x01010101u;
@@ -624,6 +637,42 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
     }
 }
 
+// SAFE = false: the fast kernel, one workgroup per tile.  SAFE = true: the
+// exact kernel on a small grid (at most EXACT_GRID workgroups): each thread
+// checks one tile's mark, and each workgroup redoes its marked tiles one after
+// another (most launches mark none, so most workgroups only read marks).
+constexpr int EXACT_GRID = 256;
+template <bool CAUSAL, int NW, bool SAFE>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p) {
+    if constexpr (!SAFE) {
+        fwd8_tile<CAUSAL, NW, false>(p, blockIdx.x);
+    } else {
+        constexpr int NTH = NW * 64;
+        __shared__ int marked[NTH];
+        __shared__ int n_marked;
+        const int t = threadIdx.x;
+        if (t == 0) n_marked = 0;
+        __syncthreads();
+        const int bid = blockIdx.x + t * gridDim.x;   // gridDim.x * NTH >= p.total
+        if (bid < p.total) {
+            int b, h, qt;
+            tile_of<CAUSAL, NW>(p, bid, b, h, qt);
+            const size_t q_panel = ((size_t)b * p.Hq + h) * (size_t)p.N * HD;
+            const u32x4 w = *(const u32x4*)(p.o + q_panel + (size_t)(qt * 32 * NW) * HD);
+            if (w[0] == NF_MARK[0] && w[1] == NF_MARK[1] && w[2] == NF_MARK[2] && w[3] == NF_MARK[3])
+                marked[atomicAdd(&n_marked, 1)] = bid;
+        }
+        __syncthreads();
+        const int n = n_marked;
+        for (int i = 0; i < n; ++i) {
+            fwd8_tile<CAUSAL, NW, true>(p, __builtin_amdgcn_readfirstlane(marked[i]));
+            // the next tile reuses the LDS: copies still in flight land first
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o,
@@ -686,23 +735,25 @@ extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* 
     p.dv = descale_v;
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid((unsigned)total);
-    // the fast kernel, then the exact kernel over the same grid: it redoes the
-    // workgroups the fast kernel marked and every other workgroup exits at once
+    // the fast kernel, then the exact kernel on a small grid that redoes the
+    // tiles the fast kernel marked
+    const int nth = short_n ? 256 : 512;
+    const dim3 egrid((unsigned)std::max(std::min(p.total, EXACT_GRID), (p.total + nth - 1) / nth));
     if (short_n) {
         if (causal) {
             hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4, false>), grid, dim3(256), 0, s, p);
-            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4, true>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 4, true>), egrid, dim3(256), 0, s, p);
         } else {
             hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4, false>), grid, dim3(256), 0, s, p);
-            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4, true>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 4, true>), egrid, dim3(256), 0, s, p);
         }
     } else {
         if (causal) {
             hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8, false>), grid, dim3(512), 0, s, p);
-            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8, true>), grid, dim3(512), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, 8, true>), egrid, dim3(512), 0, s, p);
         } else {
             hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8, false>), grid, dim3(512), 0, s, p);
-            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8, true>), grid, dim3(512), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, 8, true>), egrid, dim3(512), 0, s, p);
         }
     }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
