@@ -241,3 +241,78 @@ def test_nonfinite_decode(shape, causal, n_splits):
     n = check_nonfinite(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref,
                         f"{shape} causal={causal} n_splits={n_splits}")
     assert n > 0
+
+
+def _tile_rows(B, H, N, rows_per_tile):
+    """Flat row ids ((b*H + h)*N + i) of rows 0, 31, 32, 63 and the last of
+    every query tile of rows_per_tile rows (wave boundaries of the tile)."""
+    out = []
+    for bh in range(B * H):
+        for t0 in range(0, N, rows_per_tile):
+            for r in sorted({0, 31, 32, 63, rows_per_tile - 1}):
+                if t0 + r < N:
+                    out.append(bh * N + t0 + r)
+    return np.array(out, np.int64)
+
+
+def test_nonfinite_every_tile_marked():
+    """A NaN in V at the last key of every 32-key block: every wave's causal
+    diagonal block holds a key hidden from its earlier rows, so the fast
+    kernel hands every tile (512 of them, more than the exact kernel's 256
+    workgroups) to the exact kernel, whose workgroups then redo several tiles
+    one after another.  Row i's column 7j % 128 is NaN exactly when i >= 32j + 31."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, H, N = 2, 16, 2048
+    say(f"[nonfinite every tile] B={B} H={H} N={N} causal")
+    q = synth.normal_bf16(24000, (B, H, N, 128))
+    k = synth.normal_bf16(24001, (B, H, N, 128))
+    v = synth.normal_bf16(24002, (B, H, N, 128))
+    for j in range(N // 32):
+        v[:, :, 32 * j + 31, (7 * j) % 128] = NAN
+    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = _tile_rows(B, H, N, 128)
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, True, SCALE, rows=rows)
+    og = bf16_to_np(o).reshape(-1, 128)[rows]
+    lg = lse.cpu().numpy().reshape(-1)[rows]
+    n = check_nonfinite(og, lg, o_ref, lse_ref, "every tile marked")
+    assert n > 0 and np.isfinite(o_ref).any()
+
+
+def test_nonfinite_every_tile_marked_fp8():
+    """The same for the FP8 forward: an e4m3 NaN code at the last key of every
+    64-key block, causal, 512 tiles of 128 rows."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    B, H, N = 1, 16, 4096
+    say(f"[nonfinite every tile fp8] B={B} H={H} N={N} causal")
+    d = synth.FP8_DESCALE
+    q8 = synth.normal_e4m3(25000, (B, H, N, 128), d)
+    k8 = synth.normal_e4m3(25001, (B, H, N, 128), d)
+    v8 = synth.normal_e4m3(25002, (B, H, N, 128), d)
+    for j in range(N // 64):
+        v8[:, :, 64 * j + 63, (5 * j) % 128] = 0x7F
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).cuda()
+
+    o, lse = sdpa.fwd_fp8(up(q8), up(k8), up(v8), d, d, d, causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = _tile_rows(B, H, N, 128)
+    og = bf16_to_np(o).reshape(-1, 128)[rows]
+    lg = lse.cpu().numpy().reshape(-1)[rows]
+    qv = oracle.e4m3_decode(q8.reshape(-1, 128))
+    kv = oracle.e4m3_decode(k8.reshape(-1, 128))
+    serr = parity.fp8_score_err(qv, kv, SCALE, d, d)
+    o_ref, lse_ref, mag, rms = oracle.attn_fp8_ref(q8, k8, v8, d, d, d, True, SCALE, rows=rows,
+                                                   mags=parity.fp8_mags(serr))
+    diff = np.argwhere(np.isnan(og.astype(np.float64)) != np.isnan(o_ref))
+    assert diff.size == 0, f"FP8 O NaN pattern differs at {diff[:6].tolist()}"
+    assert np.array_equal(np.isnan(lg), np.isnan(lse_ref))
+    fin = np.isfinite(o_ref)
+    assert (~fin).any() and fin.any()
+    # finite elements of rows with NaN columns still meet the element bound
+    err = np.abs(og.astype(np.float64)[fin] - o_ref[fin])
+    tol = 2.0 ** -8 * np.abs(o_ref[fin]) + parity.FP8_KAPPA * mag[fin]
+    assert np.all(err <= tol), f"FP8 finite elements beyond the bound: {int((err > tol).sum())}"
