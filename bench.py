@@ -1247,7 +1247,9 @@ def main():
             t0 = time.perf_counter()
             dst.copy_(src)
             torch.cuda.synchronize()
-            log(f"[copy] {args.calibrate_copy} MiB copy {i}: {(time.perf_counter() - t0) * 1e3:.3f} ms")
+            dt = time.perf_counter() - t0
+            log(f"[copy] {args.calibrate_copy} MiB copy {i}: {dt * 1e3:.3f} ms, "
+                f"{2 * n / dt / 1e9:.0f} GB/s read + write (wall time)")
         return
     sdpa.load()
 
