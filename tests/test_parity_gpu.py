@@ -204,3 +204,29 @@ def test_long_sequence_sampled():
     m = parity.compare(bf16_to_np(o.view(-1, 128)[sel]), lse.view(-1)[sel].cpu().numpy(), o_ref, lse_ref)
     say(f"  N={N}: {m}")
     parity.check(m, f"N={N}")
+
+
+def test_max_sequence_sampled():
+    """N = 2^23 - 1, the longest head panel the kernels' 32-bit byte offsets
+    allow (N * 256 bytes < 2^31; attn_fwd refuses 2^23), causal, one head.  Q,
+    K and V repeat a seeded pattern of 65521 rows: a prime period, so an
+    offset that wrapped at a power of two would read a different row.  Sampled
+    rows, the last of which see every key, against the oracle."""
+    import torch
+    import scaled_dot_product_17_amd as sdpa
+    N, P = (1 << 23) - 1, 65521
+    say(f"[max sequence] N={N}")
+    q = np.resize(synth.normal_bf16(18100, (P, 128)), (1, 1, N, 128))
+    k = np.resize(synth.normal_bf16(18101, (P, 128)), (1, 1, N, 128))
+    v = np.resize(synth.normal_bf16(18102, (P, 128)), (1, 1, N, 128))
+    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, P + 5, N // 2 + 7, N - 257, N - 33, N - 2, N - 1], np.int64)
+    sel = torch.from_numpy(rows).cuda()
+    og = bf16_to_np(o.view(-1, 128)[sel])
+    lg = lse.view(-1)[sel].cpu().numpy()
+    del o, lse
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, True, SCALE, rows=rows)
+    m = parity.compare(og, lg, o_ref, lse_ref)
+    say(f"  N={N}: {m}")
+    parity.check(m, f"N={N}")
