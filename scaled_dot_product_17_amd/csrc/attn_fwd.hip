@@ -99,7 +99,8 @@ struct Params {
     // packed variable-length batch (VARLEN kernels only): B = 1 and N = tokens
     const int* cu;    // n_seq + 1 token offsets
     int n_seq;
-    int dealt;        // several sequences of unequal lengths: head groups dealt to the XCDs in turn
+    int dealt;        // the dealt grid order (dealt_tile) instead of the plain one
+    Deal deal;        // its sizes
     int left, right;  // window: row i sees keys i-left .. i+right (< 0: unbounded)
     // block-sparse mask (SPARSE kernels only): lists of SP_BLOCK-key blocks per
     // (mask head, SP_BLOCK-row query block), block-compressed-row form
@@ -133,23 +134,13 @@ __device__ __forceinline__ bool tile_of(const Params& p, int bid, int& b, int& h
     constexpr int BRW = 32 * NW;
     const int logical = xcd_remap(bid, p.total);
     int bh;
-    if (VARLEN && p.n_seq > 1 && p.dealt) {
-        // several sequences of unequal lengths: groups of cgroup (sequence,
-        // head)s, each group's tiles tile-major with the heaviest first, so a
-        // group's K/V is read from HBM about once and then served by its XCD's
-        // L2.  Whole groups are dealt to the 8 XCDs in turn (workgroup i runs on
-        // XCD i % 8), so every XCD receives an even share of every sequence's
-        // heads and the XCDs finish together.
-        const int per = p.B * p.Hq;
-        const int G = p.cgroup > 1 ? p.cgroup : 1;
-        const int x = bid & 7, sx = bid >> 3;
-        const int k = sx / (G * p.n_qtiles);
-        const int r = sx - k * G * p.n_qtiles;
-        const int grp = x + 8 * k;
-        const int gh = min(G, per - grp * G);   // heads in this group (the last may be short)
-        if (gh <= 0 || r >= gh * p.n_qtiles) return false;   // padding of the grid
-        qt = p.n_qtiles - 1 - r / gh;
-        bh = grp * G + r % gh;
+    if ((VARLEN || (CAUSAL && !SPARSE)) && p.dealt) {
+        // varlen batches of unequal lengths, and causal grids whose head groups
+        // do not split evenly over the 8 XCDs: slices of groups dealt to the
+        // XCDs in turn, each a strided share of its group's heaviest-first
+        // list, so the XCDs receive equal work and finish together
+        if (!dealt_tile(bid, p.B * p.Hq, p.cgroup > 1 ? p.cgroup : 1, p.n_qtiles, p.deal, bh, qt))
+            return false;   // padding of the grid
     } else if (CAUSAL && !SPARSE) {
         // groups of cgroup (batch, head)s one after another, so the tiles of a
         // group share K/V in the L2 of one XCD; within a group tile-major,
@@ -936,6 +927,13 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     // slots (32 CUs x 2 four-wave or 1 eight-wave workgroups)
     const int64_t slots = short_n ? 64 : 32;
     p.cgroup = (int)std::min<int64_t>((int64_t)B * H_q, (slots + n_qtiles - 1) / n_qtiles);
+    int64_t grid = 0;
+    int64_t dg = p.cgroup;
+    if (causal && causal_deal((int64_t)B * H_q, dg, n_qtiles, slots, p.deal, grid) && grid <= INT32_MAX) {
+        p.dealt = 1;
+        p.cgroup = (int)dg;
+        p.total = (int)grid;
+    }
     set_scale(p, scale);
     return short_n ? launch_fwd<false, false, NWAVE / 2>(p, causal != 0, stream)
                    : launch_fwd<false, false, NWAVE>(p, causal != 0, stream);
@@ -959,13 +957,23 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     const int64_t n_qtiles = ((int64_t)max_seqlen + br - 1) / br;
     // Sequences of nearly equal length (the longest within 1.25x the mean)
     // take the dense order: a few heads at a time, whose K/V stays in one
-    // XCD's L2 (grouped as for dense causal grids).  Unequal lengths deal whole
-    // groups of heads to the XCDs in turn, which balances them.
+    // XCD's L2 (grouped as for dense causal grids).  Unequal lengths are dealt
+    // to the XCDs in turn (dealt_tile): with 32 groups of (sequence, head)
+    // pairs or more, whole groups, one after another on each XCD, which
+    // balances them on average; with fewer, 8 slices of every group, one per
+    // XCD and run row by row, so each XCD gets an eighth of every group's work
+    // whatever the lengths (whole groups would leave XCDs idle, or give one XCD
+    // a long sequence's every tile).
     const bool unequal = n_seq > 1 && (int64_t)max_seqlen * n_seq * 4 > (int64_t)total * 5;
     const int64_t pairs = (int64_t)n_seq * H_q;
     const int64_t cgroup = std::min<int64_t>(pairs, (64 + n_qtiles - 1) / n_qtiles);
     const int64_t n_groups = (pairs + cgroup - 1) / cgroup;
-    const int64_t grid = unequal ? 8 * ((n_groups + 7) / 8) * cgroup * n_qtiles : pairs * n_qtiles;
+    int64_t grid = pairs * n_qtiles;
+    Deal deal{};
+    if (unequal) {
+        deal = n_groups < 32 ? make_deal(pairs, cgroup, n_qtiles, 8, true, grid)
+                             : make_deal(pairs, cgroup, n_qtiles, 1, false, grid);
+    }
     if (grid > INT32_MAX || n_seq == INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
     if (mis != 0 || (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) != 0) return ATTN_ERR_ALIGN;
@@ -999,6 +1007,7 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.cu = cu_seqlens;
     p.n_seq = n_seq;
     p.dealt = unequal;
+    p.deal = deal;
     p.cgroup = (int)cgroup;
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;

@@ -100,6 +100,8 @@ struct Params {
     int total;        // B * Hq * n_qtiles workgroups
     int q_mode;       // 0: Q as given, 1: Q negated, 2: Q replaced by zeros
     int cgroup;       // causal: heads whose tiles are interleaved (<= 1: one head)
+    int dealt;        // causal: the dealt grid order (dealt_tile) instead of the plain one
+    Deal deal;        // its sizes
     float c;          // |scale*dq*dk| * log2(e), > 0
     float lse_scale;  // |scale*dq*dk|
     float dv;         // V descale, applied to O
@@ -132,12 +134,19 @@ __device__ __forceinline__ f32x16 mfma8_sb(const i32x8& a, const i32x8& b, const
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
-// Which (batch, head, query tile) workgroup id bid computes.
+// Which (batch, head, query tile) workgroup id bid computes; false: bid is
+// padding of the grid.
 template <bool CAUSAL, int NW>
-__device__ __forceinline__ void tile_of(const Params& p, int bid, int& b, int& h, int& qt) {
+__device__ __forceinline__ bool tile_of(const Params& p, int bid, int& b, int& h, int& qt) {
     const int logical = xcd_remap(bid, p.total);
     int bh;
-    if (CAUSAL) {
+    if (CAUSAL && p.dealt) {
+        // head groups that do not split evenly over the 8 XCDs: slices of
+        // groups dealt to the XCDs in turn, each a strided share of its
+        // group's heaviest-first list, so the XCDs receive equal work
+        if (!dealt_tile(bid, p.B * p.Hq, p.cgroup > 1 ? p.cgroup : 1, p.n_qtiles, p.deal, bh, qt))
+            return false;
+    } else if (CAUSAL) {
         // groups of cgroup heads one after another (a group's tiles share K/V in
         // one XCD's L2), tile-major and heaviest tile first within a group; a
         // group holds at least an XCD's worth of workgroup slots, so light tiles
@@ -155,6 +164,7 @@ __device__ __forceinline__ void tile_of(const Params& p, int bid, int& b, int& h
     }
     b = bh / p.Hq;
     h = bh % p.Hq;
+    return true;
 }
 
 // One query tile (workgroup id bid).  NW waves per workgroup (8, or 4 for
@@ -178,7 +188,7 @@ __device__ __forceinline__ void fwd8_tile(const Params& p, const int bid) {
     const int hh = lane >> 5;    // which half of the wave
 
     int b, h, qt;
-    tile_of<CAUSAL, NW>(p, bid, b, h, qt);
+    if (!tile_of<CAUSAL, NW>(p, bid, b, h, qt)) return;   // whole workgroup, no barrier yet
     // workgroup-uniform (said so, so the copy descriptors stay scalar)
     b = __builtin_amdgcn_readfirstlane(b);
     h = __builtin_amdgcn_readfirstlane(h);
@@ -654,9 +664,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_fp8_kernel(Params p)
         if (t == 0) n_marked = 0;
         __syncthreads();
         const int bid = blockIdx.x + t * gridDim.x;   // gridDim.x * NTH >= p.total
-        if (bid < p.total) {
-            int b, h, qt;
-            tile_of<CAUSAL, NW>(p, bid, b, h, qt);
+        int b, h, qt;
+        if (bid < p.total && tile_of<CAUSAL, NW>(p, bid, b, h, qt)) {
             const size_t q_panel = ((size_t)b * p.Hq + h) * (size_t)p.N * HD;
             const u32x4 w = *(const u32x4*)(p.o + q_panel + (size_t)(qt * 32 * NW) * HD);
             if (w[0] == NF_MARK[0] && w[1] == NF_MARK[1] && w[2] == NF_MARK[2] && w[3] == NF_MARK[3])
@@ -730,11 +739,18 @@ extern "C" attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* 
     // (32 CUs x 2 four-wave or 1 eight-wave workgroups)
     const int64_t slots = short_n ? 64 : 32;
     p.cgroup = (int)std::min<int64_t>((int64_t)B * H_q, (slots + n_qtiles - 1) / n_qtiles);
+    int64_t dgrid = 0;
+    int64_t dg = p.cgroup;
+    if (causal && causal_deal((int64_t)B * H_q, dg, n_qtiles, slots, p.deal, dgrid) && dgrid <= INT32_MAX) {
+        p.dealt = 1;
+        p.cgroup = (int)dg;
+        p.total = (int)dgrid;
+    }
     p.c = (float)((double)(mag > 0.f ? mag : 1.0f) * 1.4426950408889634);
     p.lse_scale = mag;
     p.dv = descale_v;
     hipStream_t s = (hipStream_t)stream;
-    const dim3 grid((unsigned)total);
+    const dim3 grid((unsigned)p.total);
     // the fast kernel, then the exact kernel on a small grid that redoes the
     // tiles the fast kernel marked
     const int nth = short_n ? 256 : 512;

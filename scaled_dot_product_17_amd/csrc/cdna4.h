@@ -5,9 +5,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <numeric>
 
 namespace cdna4 {
 
@@ -101,7 +103,85 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return start + s;
 }
 
+// Dealt grid order.  The query tiles of `per` heads (or (sequence, head)
+// pairs) form groups of G heads, each group's G * n tiles listed heaviest
+// first (tile-major: every head's last tile, then every head's second-to-last,
+// ...).  Each group is cut into S slices: slice s takes the list positions
+// S*j + s for even j and S*j + S-1-s for odd j, so the slices of a group carry
+// equal work.  Slices (group-major) are dealt to the 8 XCDs in turn (the
+// dispatcher sends workgroup i to XCD i mod 8), U slices to each XCD, len
+// positions per slice.  An XCD runs its slices one after another (inter = 0),
+// or row by row, the heaviest positions of all its slices first (inter = 1).
+struct Deal {
+    int S, U, len, inter;
+};
+// false: bid is padding of the grid.  (Host-callable too, for checks of the
+// order on the CPU.)
+__host__ __device__ __forceinline__ bool dealt_tile(int bid, int per, int G, int n, const Deal& d, int& bh,
+                                                    int& qt) {
+    const int x = bid & 7, sx = bid >> 3;
+    int k, j;
+    if (d.inter) {
+        k = sx % d.U;
+        j = sx / d.U;
+    } else {
+        k = sx / d.len;
+        j = sx - k * d.len;
+    }
+    const int u = x + 8 * k;
+    const int grp = u / d.S, s = u - grp * d.S;
+    const int gh = G < per - grp * G ? G : per - grp * G;   // heads in this group (the last may be short)
+    const int r = d.S * j + ((j & 1) ? d.S - 1 - s : s);
+    if (gh <= 0 || r >= gh * n) return false;
+    qt = n - 1 - r / gh;
+    bh = grp * G + r % gh;
+    return true;
+}
+
 // ---- host side
+// The dealt order's sizes for per heads in groups of G with n tiles each, S
+// slices per group; the grid is 8 * U * len workgroups.
+inline Deal make_deal(int64_t per, int64_t G, int64_t n, int S, bool inter, int64_t& grid) {
+    const int64_t n_groups = (per + G - 1) / G;
+    const int64_t U = (n_groups * S + 7) / 8;
+    const int64_t len = (G * n + S - 1) / S;
+    grid = 8 * U * len;
+    return Deal{S, (int)std::min<int64_t>(U, INT32_MAX), (int)std::min<int64_t>(len, INT32_MAX), inter ? 1 : 0};
+}
+
+// Causal dense grids.  The plain order hands each XCD a contiguous eighth of
+// the groups' heaviest-first lists, which balances the XCDs only when whole,
+// equal groups split evenly over them: with 1, 2 or 4 groups the first XCDs get
+// the heavy tiles of a group and the others its light ones (a simulated
+// makespan of 1.5-1.9x the ideal for one to four long heads), and a short last
+// group shifts every boundary.  So unless the groups are full and a multiple
+// of 8, or at least 32 (then the plain order is balanced to a few percent),
+// the grid is dealt instead, in groups of G' heads, G' the largest divisor of
+// per not above G (so every group is full): S = 8 / gcd(groups, 8) slices per
+// group make the slice count a multiple of 8, and an XCD with at most 16
+// slices runs them row by row (at most 16 heads in flight on it, so K/V is
+// still shared in its L2); with more, one after another when a slice holds at
+// least an XCD's workgroup slots.  false: keep the plain order.  true: G is
+// set to G'.
+inline bool causal_deal(int64_t per, int64_t& G, int64_t n, int64_t slots, Deal& d, int64_t& grid) {
+    const int64_t ng = (per + G - 1) / G;
+    if ((per % G == 0 && ng % 8 == 0) || ng >= 32) return false;
+    int64_t g = G;
+    while (per % g != 0) --g;
+    const int64_t ngd = per / g;
+    const int S = 8 / (int)std::gcd(ngd, (int64_t)8);
+    const int64_t U = ngd * S / 8;
+    if (U <= 16) {
+        d = make_deal(per, g, n, S, true, grid);
+    } else if (g * n / S >= slots) {
+        d = make_deal(per, g, n, S, false, grid);
+    } else {
+        return false;
+    }
+    G = g;
+    return true;
+}
+
 inline bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return na != 0 && nb != 0 && x < y + nb && y < x + na;

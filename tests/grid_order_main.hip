@@ -1,0 +1,111 @@
+// Host check of the dealt grid order (dealt_tile, causal_deal, make_deal in
+// cdna4.h): for the launch shapes of the dense bf16 and FP8 causal forwards
+// and of varlen batches of unequal lengths, every workgroup id of the grid
+// maps to padding or to one (head, query tile) in range, and every (head,
+// query tile) is reached exactly once, and the XCDs receive equal causal
+// work up to a few of a group's lightest tiles.  The tile-row and slot rules below are
+// the launches' own: 256-row tiles and 32 slots per XCD, or 128-row tiles and
+// 64 slots for short sequences (bf16 causal up to 8192 tokens, FP8 up to
+// 4096, varlen always).  Prints "ok ..." and exits 0, or names the first
+// failing shape and exits 1.
+#include "cdna4.h"
+
+#include <cstdio>
+#include <vector>
+
+using namespace cdna4;
+
+static long n_shapes = 0, n_dealt = 0;
+
+static int64_t worst_gap = 0;
+
+static bool covers(int64_t per, int64_t G, int64_t n, const Deal& d, int64_t grid, const char* what,
+                   long a, long b, long c) {
+    std::vector<uint8_t> seen((size_t)(per * n), 0);
+    int64_t hits = 0;
+    int64_t work[8] = {0};   // causal work per XCD: tile qt sees qt + 1 diagonal-width key blocks
+    for (int64_t bid = 0; bid < grid; ++bid) {
+        int bh = -1, qt = -1;
+        if (!dealt_tile((int)bid, (int)per, (int)G, (int)n, d, bh, qt)) continue;
+        work[bid & 7] += qt + 1;
+        if (bh < 0 || bh >= per || qt < 0 || qt >= n) {
+            printf("out of range: %s %ld %ld %ld: workgroup %ld -> head %d tile %d\n", what, a, b, c, (long)bid, bh, qt);
+            return false;
+        }
+        if (seen[(size_t)bh * n + qt]++) {
+            printf("twice: %s %ld %ld %ld: workgroup %ld -> head %d tile %d\n", what, a, b, c, (long)bid, bh, qt);
+            return false;
+        }
+        ++hits;
+    }
+    if (hits != per * n) {
+        printf("missed: %s %ld %ld %ld: %ld of %ld tiles\n", what, a, b, c, (long)hits, (long)(per * n));
+        return false;
+    }
+    // Balance.  Over two consecutive rows of S list positions every slice
+    // takes the same total weight, so slices of one group differ only by
+    // their last, odd row: at most S tiles of a group's lightest rows, whose
+    // weight is at most a few diagonal blocks each: bounded here by 2 * S * S
+    // blocks per slice, U slices per XCD (dense groups are all full).  Whole-
+    // group orders (S = 1, varlen) are balanced only on average and are not
+    // held to it.
+    if (d.S > 1) {
+        const int64_t mx = *std::max_element(work, work + 8), mn = *std::min_element(work, work + 8);
+        const int64_t bound = (int64_t)d.U * 2 * d.S * d.S;
+        worst_gap = std::max(worst_gap, mx - mn);
+        if (mx - mn > bound) {
+            printf("unbalanced: %s %ld %ld %ld: XCD work %ld .. %ld (bound %ld)\n", what, a, b, c, (long)mn,
+                   (long)mx, (long)bound);
+            return false;
+        }
+    }
+    return true;
+}
+
+static bool dense_causal(int B, int H, int N, bool fp8) {
+    const bool short_n = fp8 ? N <= 4096 : N <= 8192;
+    const int64_t br = short_n ? 128 : 256, slots = short_n ? 64 : 32;
+    const int64_t n = (N + br - 1) / br, per = (int64_t)B * H;
+    int64_t G = std::min<int64_t>(per, (slots + n - 1) / n);
+    Deal d{};
+    int64_t grid = 0;
+    ++n_shapes;
+    if (!causal_deal(per, G, n, slots, d, grid) || grid > INT32_MAX) return true;   // plain order
+    ++n_dealt;
+    return covers(per, G, n, d, grid, fp8 ? "fp8 B H N" : "bf16 B H N", B, H, N);
+}
+
+static bool varlen(int n_seq, int H, int max_seqlen) {
+    const int64_t n = (max_seqlen + 127) / 128, pairs = (int64_t)n_seq * H;
+    const int64_t G = std::min<int64_t>(pairs, (64 + n - 1) / n);
+    const int64_t ng = (pairs + G - 1) / G;
+    int64_t grid = 0;
+    const Deal d = ng < 32 ? make_deal(pairs, G, n, 8, true, grid) : make_deal(pairs, G, n, 1, false, grid);
+    ++n_shapes;
+    ++n_dealt;
+    return covers(pairs, G, n, d, grid, "varlen n_seq H max_seqlen", n_seq, H, max_seqlen);
+}
+
+int main() {
+    const int Ns[] = {1, 31, 100, 128, 129, 255, 256, 1000, 2048, 4095, 4096, 4097,
+                      8192, 8193, 12345, 16384, 65536, 131073};
+    for (int B = 1; B <= 9; ++B)
+        for (int H = 1; H <= 40; ++H)
+            for (int N : Ns)
+                for (int f = 0; f < 2; ++f)
+                    if (!dense_causal(B, H, N, f)) return 1;
+    const int longest[] = {1 << 20, 3000001, (1 << 23) - 1};
+    for (int H = 1; H <= 12; ++H)
+        for (int N : longest)
+            for (int f = 0; f < 2; ++f)
+                if (!dense_causal(1, H, N, f)) return 1;
+    const int Ls[] = {1, 100, 128, 129, 1000, 4096, 8192, 8193, 32768, 100000};
+    for (int s = 2; s <= 40; ++s)
+        for (int H = 1; H <= 16; ++H)
+            for (int L : Ls)
+                if (!varlen(s, H, L)) return 1;
+    if (!varlen(2, 1, (1 << 23) - 1001) || !varlen(2, 2, (1 << 23) - 1001)) return 1;
+    printf("ok: %ld launch shapes, %ld with a dealt grid, largest XCD work gap %ld blocks\n", n_shapes, n_dealt,
+           (long)worst_gap);
+    return 0;
+}
