@@ -99,6 +99,8 @@ struct BwdParams {
     int kgroup;             // attn_bwd_dkdv, causal: (batch, K/V head, part)s interleaved
     int n_ktiles, total_k;  // attn_bwd_dkdv grid: B * Hkv * ceil(N / 128) * n_split
     int n_split;            // dK/dV: parts of each group's query heads (1: write dk, dv)
+    int dealt_q, dealt_k;   // causal: the dealt grid order (dealt_tile) instead of the plain one
+    Deal deal_q, deal_k;    // its sizes for the dQ and dK/dV grids
     float* ws;              // n_split > 1: fp32 partials [n_split][dV, dK][B * Hkv * N][D]
     float c;                // scale * log2(e)
     float scale;
@@ -152,7 +154,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
     // of one group, not heavy tiles of the next, end each XCD's share
     const int logical = xcd_remap(blockIdx.x, p.total_q);
     int bh, qt;
-    if (CAUSAL) {
+    if (CAUSAL && p.dealt_q) {
+        // head groups that do not split evenly over the 8 XCDs: slices of
+        // groups dealt to the XCDs in turn, each a strided share of its
+        // group's heaviest-first list (whole workgroup, no barrier yet)
+        if (!dealt_tile(blockIdx.x, p.B * p.Hq, p.cgroup > 1 ? p.cgroup : 1, p.n_qtiles, p.deal_q, bh, qt))
+            return;   // padding of the grid
+    } else if (CAUSAL) {
         const int per = p.B * p.Hq;
         const int G = p.cgroup > 1 ? p.cgroup : 1;
         const int grp = logical / (G * p.n_qtiles);
@@ -351,7 +359,14 @@ __global__ __launch_bounds__(KV_THREADS, 2) void attn_bwd_dkdv_kernel(BwdParams 
     const int ns = p.n_split > 1 ? p.n_split : 1;
     const int logical = xcd_remap(blockIdx.x, p.total_k);
     int bks, kt;
-    if (CAUSAL) {
+    if (CAUSAL && p.dealt_k) {
+        // units that do not split evenly over the 8 XCDs: dealt slices, as
+        // for dQ; the heaviest key tile is the first
+        int t;
+        if (!dealt_tile(blockIdx.x, p.B * p.Hkv * ns, p.kgroup > 1 ? p.kgroup : 1, p.n_ktiles, p.deal_k, bks, t))
+            return;   // padding of the grid (whole workgroup, no barrier yet)
+        kt = p.n_ktiles - 1 - t;
+    } else if (CAUSAL) {
         const int per = p.B * p.Hkv * ns;
         const int G = p.kgroup > 1 ? p.kgroup : 1;
         const int grp = logical / (G * p.n_ktiles);
@@ -691,7 +706,29 @@ size_t q_bytes(int B, int H_q, int N) { return (size_t)B * H_q * N * HD * 2; }
 size_t kv_bytes(int B, int H_kv, int N) { return (size_t)B * H_kv * N * HD * 2; }
 size_t row_bytes(int B, int H_q, int N) { return (size_t)B * H_q * N * 4; }
 
-void launch_dq(const BwdParams& p, bool causal, hipStream_t s) {
+// Causal grids whose groups do not split evenly over the 8 XCDs take the
+// dealt order (causal_deal); the launch grid is then its padded size.
+void deal_dq(BwdParams& p) {
+    int64_t G = p.cgroup > 1 ? p.cgroup : 1, grid = 0;
+    const int64_t slots = p.dq_waves == 4 ? 64 : 32;
+    if (causal_deal((int64_t)p.B * p.Hq, G, p.n_qtiles, slots, p.deal_q, grid) && grid <= INT32_MAX) {
+        p.dealt_q = 1;
+        p.cgroup = (int)G;
+        p.total_q = (int)grid;
+    }
+}
+void deal_dkdv(BwdParams& p) {
+    const int64_t ns = p.n_split > 1 ? p.n_split : 1;
+    int64_t G = p.kgroup > 1 ? p.kgroup : 1, grid = 0;
+    if (causal_deal((int64_t)p.B * p.Hkv * ns, G, p.n_ktiles, 32, p.deal_k, grid) && grid <= INT32_MAX) {
+        p.dealt_k = 1;
+        p.kgroup = (int)G;
+        p.total_k = (int)grid;
+    }
+}
+
+void launch_dq(BwdParams p, bool causal, hipStream_t s) {
+    if (causal) deal_dq(p);
     if (p.dq_waves == 4) {
         if (causal)
             hipLaunchKernelGGL((attn_bwd_dq_kernel<true, 4>), dim3((unsigned)p.total_q), dim3(256), 0, s, p);
@@ -704,7 +741,8 @@ void launch_dq(const BwdParams& p, bool causal, hipStream_t s) {
             hipLaunchKernelGGL((attn_bwd_dq_kernel<false, 8>), dim3((unsigned)p.total_q), dim3(512), 0, s, p);
     }
 }
-void launch_dkdv(const BwdParams& p, bool causal, hipStream_t s) {
+void launch_dkdv(BwdParams p, bool causal, hipStream_t s) {
+    if (causal) deal_dkdv(p);
     if (causal)
         hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)p.total_k), dim3(KV_THREADS), 0, s, p);
     else

@@ -1,6 +1,7 @@
 // Host check of the dealt grid order (dealt_tile, causal_deal, make_deal in
-// cdna4.h): for the launch shapes of the dense bf16 and FP8 causal forwards
-// and of varlen batches of unequal lengths, every workgroup id of the grid
+// cdna4.h): for the launch shapes of the dense bf16 and FP8 causal forwards,
+// the causal backward's dQ and dK/dV grids and varlen batches of unequal
+// lengths, every workgroup id of the grid
 // maps to padding or to one (head, query tile) in range, and every (head,
 // query tile) is reached exactly once, and the XCDs receive equal causal
 // work up to a few of a group's lightest tiles.  The tile-row and slot rules below are
@@ -75,6 +76,20 @@ static bool dense_causal(int B, int H, int N, bool fp8) {
     return covers(per, G, n, d, grid, fp8 ? "fp8 B H N" : "bf16 B H N", B, H, N);
 }
 
+// The backward's dK/dV grid: 128-key tiles, one workgroup per CU (32 slots
+// per XCD), units of (batch, K/V head, part).  (Its dQ grid follows the bf16
+// forward's rule above.)
+static bool dkdv_causal(int units, int N) {
+    const int64_t n = (N + 127) / 128, slots = 32;
+    int64_t G = std::min<int64_t>(units, (slots + n - 1) / n);
+    Deal d{};
+    int64_t grid = 0;
+    ++n_shapes;
+    if (!causal_deal(units, G, n, slots, d, grid) || grid > INT32_MAX) return true;
+    ++n_dealt;
+    return covers(units, G, n, d, grid, "dkdv units N", units, N, 0);
+}
+
 static bool varlen(int n_seq, int H, int max_seqlen) {
     const int64_t n = (max_seqlen + 127) / 128, pairs = (int64_t)n_seq * H;
     const int64_t G = std::min<int64_t>(pairs, (64 + n - 1) / n);
@@ -99,6 +114,9 @@ int main() {
         for (int N : longest)
             for (int f = 0; f < 2; ++f)
                 if (!dense_causal(1, H, N, f)) return 1;
+    for (int u = 1; u <= 72; ++u)
+        for (int N : Ns)
+            if (!dkdv_causal(u, N)) return 1;
     const int Ls[] = {1, 100, 128, 129, 1000, 4096, 8192, 8193, 32768, 100000};
     for (int s = 2; s <= 40; ++s)
         for (int H = 1; H <= 16; ++H)
