@@ -84,36 +84,47 @@ def test_varlen_small_full(case, causal):
     parity.check(m, f"{case} causal={causal}")
 
 
+@pytest.mark.parametrize("heads", [(16, 2), (32, 4)], ids=["16groups_sliced", "32groups_whole"])
 @pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (200, 0)),
                                            (False, (64, 64))])
-def test_varlen_dealt_groups_full(causal, window):
-    """Sequences of unequal lengths deal whole groups of (sequence, head)
-    pairs to the 8 XCDs in turn.  Eight sequences of 16 query heads make 128
-    pairs; with 128-row tiles the longest (1000 tokens) has 8 tiles, so groups
-    hold 8 pairs and there are 16 of them: every XCD slot gets a group in both
-    rounds of the deal.  Every row is compared with the oracle, and the outputs
-    start as NaN bytes, so every element must be written."""
+def test_varlen_dealt_groups_full(causal, window, heads):
+    """Sequences of unequal lengths are dealt to the 8 XCDs in groups of
+    (sequence, head) pairs: with fewer than 32 groups each group is cut into 8
+    slices, one per XCD, run row by row; with 32 or more, whole groups go to
+    the XCDs in turn.  Eight sequences (the longest, 1000 tokens, has 8 tiles
+    of 128 rows, so groups hold 8 pairs) of 16 query heads make 16 groups (the
+    sliced form: every XCD holds a slice of every group), of 32 query heads 32
+    groups (the whole-group form, four rounds over the XCDs).  Every row is
+    compared with the oracle, and the outputs start as NaN bytes, so every
+    element must be written."""
     import torch
     import scaled_dot_product_17_amd as sdpa
     lens = [1000, 40, 300, 7, 650, 129, 2, 900]
-    Hq, Hkv = 16, 2
+    Hq, Hkv = heads
     n_qtiles = -(-max(lens) // 128)
     pairs = len(lens) * Hq
     group = min(pairs, -(-64 // n_qtiles))
     assert max(lens) * len(lens) * 4 > sum(lens) * 5            # unequal: dealt order
-    assert -(-pairs // group) == 16                             # two rounds over 8 XCDs
-    say(f"[varlen dealt] causal={causal} window={window}")
-    q, k, v, cu = packed(14900, Hq, Hkv, lens)
+    assert -(-pairs // group) == Hq                             # 16: sliced, 32: whole groups
+    say(f"[varlen dealt] heads={heads} causal={causal} window={window}")
+    q, k, v, cu = packed(14900 + Hq, Hq, Hkv, lens)
     total = int(cu[-1])
     out = torch.full((Hq, total, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse_t = torch.full((Hq, total), float("nan"), dtype=torch.float32, device="cuda")
     o, lse = sdpa.fwd_varlen(to_gpu(q), to_gpu(k), to_gpu(v), torch.from_numpy(cu).cuda(),
                              max(lens), causal=causal, scale=SCALE, window=window, out=out, lse=lse_t)
     torch.cuda.synchronize()
-    o_ref, lse_ref = oracle.attn_varlen_ref(q, k, v, cu, causal, SCALE, *window)
+    # the oracle per K/V head (its query heads), on host threads
+    from concurrent.futures import ThreadPoolExecutor
+    gs = Hq // Hkv
+    with ThreadPoolExecutor(max_workers=Hkv) as ex:
+        parts = list(ex.map(lambda g: oracle.attn_varlen_ref(q[g * gs:(g + 1) * gs], k[g:g + 1], v[g:g + 1], cu,
+                                                             causal, SCALE, *window), range(Hkv)))
+    o_ref = np.concatenate([x[0] for x in parts])
+    lse_ref = np.concatenate([x[1] for x in parts])
     m = parity.compare(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref)
     say(f"  {m}")
-    parity.check(m, f"dealt causal={causal} window={window}")
+    parity.check(m, f"dealt heads={heads} causal={causal} window={window}")
 
 
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.5])
