@@ -970,9 +970,19 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     const int64_t n_groups = (pairs + cgroup - 1) / cgroup;
     int64_t grid = pairs * n_qtiles;
     Deal deal{};
+    int64_t dg = cgroup;
+    bool dealt = unequal;
     if (unequal) {
         deal = n_groups < 32 ? make_deal(pairs, cgroup, n_qtiles, 8, true, grid)
                              : make_deal(pairs, cgroup, n_qtiles, 1, false, grid);
+    } else if (causal) {
+        // nearly equal lengths, causal: the dense causal rule (64 slots of
+        // 4-wave workgroups per XCD)
+        int64_t g = 0;
+        if (causal_deal(pairs, dg, n_qtiles, 64, deal, g) && g <= INT32_MAX) {
+            dealt = true;
+            grid = g;
+        }
     }
     if (grid > INT32_MAX || n_seq == INT32_MAX) return ATTN_ERR_SHAPE;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15;
@@ -1006,9 +1016,9 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.total = (int)grid;
     p.cu = cu_seqlens;
     p.n_seq = n_seq;
-    p.dealt = unequal;
+    p.dealt = dealt;
     p.deal = deal;
-    p.cgroup = (int)cgroup;
+    p.cgroup = (int)dg;
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;
     set_scale(p, scale);

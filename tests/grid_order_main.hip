@@ -1,7 +1,7 @@
 // Host check of the dealt grid order (dealt_tile, causal_deal, make_deal in
 // cdna4.h): for the launch shapes of the dense bf16 and FP8 causal forwards,
-// the causal backward's dQ and dK/dV grids and varlen batches of unequal
-// lengths, every workgroup id of the grid
+// the causal backward's dQ and dK/dV grids and varlen batches (unequal
+// lengths, and causal ones of nearly equal lengths), every workgroup id of the grid
 // maps to padding or to one (head, query tile) in range, and every (head,
 // query tile) is reached exactly once, and the XCDs receive equal causal
 // work up to a few of a group's lightest tiles.  The tile-row and slot rules below are
@@ -90,6 +90,19 @@ static bool dkdv_causal(int units, int N) {
     return covers(units, G, n, d, grid, "dkdv units N", units, N, 0);
 }
 
+// Causal varlen batches of nearly equal lengths: the dense causal rule with
+// 128-row tiles and 64 slots at every length.
+static bool varlen_equal_causal(int pairs, int max_seqlen) {
+    const int64_t n = (max_seqlen + 127) / 128;
+    int64_t G = std::min<int64_t>(pairs, (64 + n - 1) / n);
+    Deal d{};
+    int64_t grid = 0;
+    ++n_shapes;
+    if (!causal_deal(pairs, G, n, 64, d, grid) || grid > INT32_MAX) return true;
+    ++n_dealt;
+    return covers(pairs, G, n, d, grid, "varlen equal pairs max_seqlen", pairs, max_seqlen, 0);
+}
+
 static bool varlen(int n_seq, int H, int max_seqlen) {
     const int64_t n = (max_seqlen + 127) / 128, pairs = (int64_t)n_seq * H;
     const int64_t G = std::min<int64_t>(pairs, (64 + n - 1) / n);
@@ -123,6 +136,10 @@ int main() {
             for (int L : Ls)
                 if (!varlen(s, H, L)) return 1;
     if (!varlen(2, 1, (1 << 23) - 1001) || !varlen(2, 2, (1 << 23) - 1001)) return 1;
+    for (int pr = 1; pr <= 72; ++pr)
+        for (int L : Ls)
+            if (!varlen_equal_causal(pr, L)) return 1;
+    if (!varlen_equal_causal(1, (1 << 23) - 1)) return 1;
     printf("ok: %ld launch shapes, %ld with a dealt grid, largest XCD work gap %ld blocks\n", n_shapes, n_dealt,
            (long)worst_gap);
     return 0;
