@@ -227,36 +227,60 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     // built in LDS (the rings serve as scratch before the first copy); stream
     // block g is 32-key part g % 4 of union entry g / 4
     const uint16_t* sp = (const uint16_t*)(lds + LDS_BYTES);
+    // Q rows into VGPRs, the B operand of S^T = K Q^T in k-steps of 16 head
+    // dims.  SPARSE loads them first: they do not depend on the key-block
+    // lists, so their latency hides behind the list reads below.
+    bf16x8 qf[8];
+    auto load_q = [&]() {
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + qo_panel, (uint32_t)N * ROW_BYTES);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, (uint32_t)myq * ROW_BYTES + (16 * ks + 8 * hh) * 2));
+    };
     if constexpr (SPARSE) {
+        load_q();
+        const int nsb = p.n_sblk;
+        const size_t mh = p.mask_heads == 1 ? 0 : (size_t)h;
+        // the lists' bounds, read before the flags are cleared (offsets
+        // clamped to [0, nnz]: a malformed list cannot read out of range)
+        int la[QB_WG], le[QB_WG];
+#pragma unroll
+        for (int half = 0; half < QB_WG; ++half) {
+            const int qb = QB_WG * qt + half;
+            la[half] = 0;
+            le[half] = 0;
+            if (qb < nsb) {
+                la[half] = min(max(p.kb_ptr[mh * nsb + qb], 0), p.nnz);
+                le[half] = min(max(p.kb_ptr[mh * nsb + qb + 1], la[half]), p.nnz);
+            }
+        }
         uint8_t* f0 = (uint8_t*)lds;             // key blocks listed by query block QB_WG*qt
         uint8_t* f1 = (uint8_t*)lds + SP_MAX;    // ... and by query block 2qt+1 (8 waves)
         int* wsum = (int*)(lds + LDS_BYTES + 2 * SP_MAX);
         for (int i = tid; i < 2 * SP_MAX / 4; i += NTH) ((uint32_t*)lds)[i] = 0u;
         __syncthreads();
-        const int nsb = p.n_sblk;
-        const size_t mh = p.mask_heads == 1 ? 0 : (size_t)h;
 #pragma unroll
         for (int half = 0; half < QB_WG; ++half) {
             const int qb = QB_WG * qt + half;
-            if (qb < nsb) {
-                // offsets clamped to [0, nnz]: a malformed list cannot read out of range
-                const int a = min(max(p.kb_ptr[mh * nsb + qb], 0), p.nnz);
-                const int e = min(max(p.kb_ptr[mh * nsb + qb + 1], a), p.nnz);
-                uint8_t* f = half ? f1 : f0;
-                for (int x = a + tid; x < e; x += NTH) {
-                    const int kb = p.kb_idx[x];
-                    // causal: key blocks after the query block hold no visible key
-                    if (kb >= 0 && kb < nsb && (!CAUSAL || kb <= qb)) f[kb] = 1;
-                }
+            uint8_t* f = half ? f1 : f0;
+            for (int x = la[half] + tid; x < le[half]; x += NTH) {
+                const int kb = p.kb_idx[x];
+                // causal: key blocks after the query block hold no visible key
+                if (kb >= 0 && kb < nsb && (!CAUSAL || kb <= qb)) f[kb] = 1;
             }
         }
         __syncthreads();
-        // compaction in key-block order: thread t owns SP_PER_T consecutive key blocks
+        // compaction in key-block order: thread t owns SP_PER_T consecutive key
+        // blocks, whose flags it reads as one word per query block
+        static_assert(SP_PER_T == 8 || SP_PER_T == 4, "flag words of 8 or 4 bytes");
+        using FlagWord = std::conditional_t<SP_PER_T == 8, uint64_t, uint32_t>;
+        const FlagWord w0 = *(const FlagWord*)(f0 + SP_PER_T * tid);
+        const FlagWord w1 = *(const FlagWord*)(f1 + SP_PER_T * tid);
         int bits[SP_PER_T], cnt = 0;
 #pragma unroll
         for (int j = 0; j < SP_PER_T; ++j) {
             const int kb = SP_PER_T * tid + j;
-            bits[j] = kb < nsb ? (f0[kb] | (f1[kb] << 1)) : 0;
+            bits[j] = kb < nsb ? (int)(((w0 >> (8 * j)) & 1u) | (((w1 >> (8 * j)) & 1u) << 1)) : 0;
             cnt += bits[j] != 0;
         }
         int incl = cnt;
@@ -398,13 +422,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     dma_block(R_K{}, S1{}, k_desc, k_dma, 1);
     dma_block(R_K{}, S2{}, k_desc, k_dma, 2);
 
-    bf16x8 qf[8];   // B operand of S^T = K Q^T, k-steps of 16 head dims
-    {
-        const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + qo_panel, (uint32_t)N * ROW_BYTES);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, (uint32_t)myq * ROW_BYTES + (16 * ks + 8 * hh) * 2));
-    }
+    if constexpr (!SPARSE) load_q();
     // A negative scale is applied as |scale| on -Q (a sign flip is exact in
     // bf16) and a zero scale as zero scores, so the exp2 argument below always
     // multiplies by a positive constant and masked -inf scores stay -inf.
