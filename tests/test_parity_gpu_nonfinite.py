@@ -255,15 +255,22 @@ def _tile_rows(B, H, N, rows_per_tile):
     return np.array(out, np.int64)
 
 
-def test_nonfinite_every_tile_marked():
+# (2, 16, 2048): 512 tiles in the plain grid order, more than the exact
+# kernel's 256 workgroups.  (1, 3, 2900): 69 tiles of one head group dealt as
+# 8 slices of 9 list positions, a grid of 72 with 3 padding workgroups.
+EVERY_TILE_SHAPES = [(2, 16, 2048), (1, 3, 2900)]
+EVERY_TILE_IDS = ["plain_512_tiles", "dealt_69_tiles"]
+
+
+@pytest.mark.parametrize("B,H,N", EVERY_TILE_SHAPES, ids=EVERY_TILE_IDS)
+def test_nonfinite_every_tile_marked(B, H, N):
     """A NaN in V at the last key of every 32-key block: every wave's causal
     diagonal block holds a key hidden from its earlier rows, so the fast
-    kernel hands every tile (512 of them, more than the exact kernel's 256
-    workgroups) to the exact kernel, whose workgroups then redo several tiles
-    one after another.  Row i's column 7j % 128 is NaN exactly when i >= 32j + 31."""
+    kernel hands every tile to the exact kernel (whose workgroups redo several
+    tiles one after another when there are more tiles than workgroups).  Row
+    i's column 7j % 128 is NaN exactly when i >= 32j + 31."""
     import torch
     import scaled_dot_product_17_amd as sdpa
-    B, H, N = 2, 16, 2048
     say(f"[nonfinite every tile] B={B} H={H} N={N} causal")
     q = synth.normal_bf16(24000, (B, H, N, 128))
     k = synth.normal_bf16(24001, (B, H, N, 128))
@@ -280,12 +287,13 @@ def test_nonfinite_every_tile_marked():
     assert n > 0 and np.isfinite(o_ref).any()
 
 
-def test_nonfinite_every_tile_marked_fp8():
+@pytest.mark.parametrize("B,H,N", [(1, 16, 4096), (1, 3, 2900)], ids=["plain_512_tiles", "dealt_69_tiles"])
+def test_nonfinite_every_tile_marked_fp8(B, H, N):
     """The same for the FP8 forward: an e4m3 NaN code at the last key of every
-    64-key block, causal, 512 tiles of 128 rows."""
+    64-key block, causal, tiles of 128 rows (512 in the plain order; 69 in a
+    dealt grid of 72)."""
     import torch
     import scaled_dot_product_17_amd as sdpa
-    B, H, N = 1, 16, 4096
     say(f"[nonfinite every tile fp8] B={B} H={H} N={N} causal")
     d = synth.FP8_DESCALE
     q8 = synth.normal_e4m3(25000, (B, H, N, 128), d)
