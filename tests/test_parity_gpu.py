@@ -81,13 +81,17 @@ def test_workload_sampled(name):
     parity.check(m, name)
 
 
-@pytest.mark.parametrize("shape", [(1, 5, 5, 3000), (3, 5, 1, 1000)],
+@pytest.mark.parametrize("shape", [(1, 5, 5, 3000), (3, 5, 1, 1000), (1, 3, 3, 9000)],
                          ids=lambda s: "b%d_hq%d_hkv%d_n%d" % s)
 def test_causal_head_groups_full(shape):
     """Causal grids interleave the tiles of groups of heads (enough tiles to fill
-    one XCD's workgroup slots: 3 heads of 24 tiles, 8 heads of 8 tiles here),
-    and the last group is short (2 and 7 heads).  Every row of every head must
-    still be computed once and match the oracle."""
+    one XCD's workgroup slots).  Groups that would not split evenly over the 8
+    XCDs (here: groups of 3 heads of 24 tiles leaving a short last one; 15
+    heads in groups of 8; 3 heads of 36 eight-wave tiles) are full-sized
+    instead (1, 5 and 1 heads) and dealt to the XCDs in strided slices, over a
+    grid with padding workgroups for the last shape (120 for 108 tiles).
+    Every row of every head must still be computed once and match the
+    oracle."""
     B, Hq, Hkv, N = shape
     say(f"[causal groups] {shape}")
     q, k, v = inputs(B, Hq, Hkv, N, seed=7500 + N)
