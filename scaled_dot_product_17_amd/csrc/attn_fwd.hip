@@ -812,17 +812,33 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     bool empty = false;
     if constexpr (SPARSE) empty = n_blk_wg == 0 || (CAUSAL && sp_key(0) > myq);
     const float inv = empty ? 0.f : 1.0f / lb_tot;
+    // O leaves through LDS.  A lane holds its row's values in 8-byte pieces of
+    // 4 head dims, so direct stores would touch 32 rows per instruction; staged
+    // row-major in the wave's 8 KiB of the K/V rings (16-byte chunk c of row r
+    // at chunk c ^ (r mod 16), so the 16 rows a write phase touches fall in
+    // distinct banks), they leave as 4 whole rows (1 KiB) per store.  The
+    // rings are free once every wave's copies, including the drain step's
+    // past-the-end ones, have landed and no wave reads them.
+    wait_dma();
+    __syncthreads();
+    char* const stage = lds + K_RING + wave * (32 * ROW_BYTES);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[db][4 * r4 + i] * inv);
+            const int ch = 4 * db + r4;   // head dims 8*ch .. 8*ch+7; this lane's half at 4*hh
+            *(bf16x4*)(stage + l32 * ROW_BYTES + ((ch ^ (l32 & 15)) << 4) + 8 * hh) = ov;
+        }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int r = 4 * t + (lane >> 4), ch = lane & 15;
+        const u32x4 x = *(const u32x4*)(stage + r * ROW_BYTES + ((ch ^ (r & 15)) << 4));
+        if (wq0 + r < s1) *(u32x4*)(p.o + qo_panel + (size_t)(wq0 + r) * HD + 8 * ch) = x;
+    }
     if (myq < s1) {
-        uint16_t* orow = p.o + qo_panel + (size_t)myq * HD;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x4 ov;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[db][4 * r4 + i] * inv);
-                *(bf16x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = ov;
-            }
         if (p.lse != nullptr && hh == 0) {
             const size_t li = ((size_t)pbat * p.Hq + h) * (size_t)N + myq;
             p.lse[li] = empty ? -INFINITY : m == -INFINITY ? __builtin_nanf("") : m * p.lse_scale + logf(l_tot);
