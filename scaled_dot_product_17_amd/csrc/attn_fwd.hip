@@ -187,7 +187,14 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     constexpr int SP_PER_T = SP_MAX / NTH;       // SPARSE: key blocks each thread compacts
     constexpr int ZERO_OFF = LDS_BYTES + (SPARSE ? SP_BYTES : 0);   // exact kernel: a block of zeros
     constexpr int SAVE_OFF = ZERO_OFF + BLK_BYTES;                     // exact kernel: per-wave saved blocks
-    __shared__ __attribute__((aligned(1024))) char lds[ZERO_OFF + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0)];
+    // Fast dense and varlen kernels copy each wave's 32 Q rows into LDS: 8-wave
+    // workgroups (one per CU) into 64 KiB past the rings, 4-wave ones into the
+    // ring slots the prologue leaves free (K slot 3, V slots 1-3); their
+    // waves' non-finite answers then move past the rings
+    constexpr bool Q_STAGED = !SAFE && !SPARSE;
+    constexpr int Q_EXTRA = !Q_STAGED ? 0 : NW == 8 ? NW * 32 * ROW_BYTES : 64;
+    constexpr int NF_OFF = (Q_STAGED && NW == 4) ? LDS_BYTES : V_RING + 3 * BLK_BYTES;
+    __shared__ __attribute__((aligned(1024))) char lds[ZERO_OFF + (SAFE ? BLK_BYTES + NW * SAVE_WAVE_BYTES : 0) + Q_EXTRA];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -422,17 +429,56 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     dma_block(R_K{}, S1{}, k_desc, k_dma, 1);
     dma_block(R_K{}, S2{}, k_desc, k_dma, 2);
 
-    if constexpr (!SPARSE) load_q();
+    // Staged Q: the wave's 32 rows copied by LDS DMA, 4 whole rows (1 KiB) per
+    // instruction instead of 32 rows per load, with the K tiles' bank swizzle
+    // applied on the global side (16-byte chunk c of row r at chunk
+    // c ^ (r mod 16)); rows at or past N arrive as zeros (range-checked
+    // voffset).  Each wave reads back only its own rows, after its own copies
+    // have landed.
+    const uint32_t q_lds = NW == 8 ? (uint32_t)(LDS_BYTES + wave * (32 * ROW_BYTES))
+                                   : (uint32_t)(wave == 0 ? K_RING + 3 * BLK_BYTES : V_RING + wave * BLK_BYTES);
+    auto stage_q = [&]() {
+        const u32x4 qd = sgpr_rsrc(p.q + qo_panel, (uint32_t)N * ROW_BYTES);
+        const uint32_t qbase = lds_base + q_lds;
+        auto one = [&](auto i_t) {
+            constexpr int i = decltype(i_t)::value;
+            const int row = 4 * i + (lane >> 4);
+            const uint32_t voff = (uint32_t)((wq0 + row) * ROW_BYTES + (((lane & 15) ^ (row & 15)) << 4));
+            lds_dma16_at<(uint32_t)(i * 4 * ROW_BYTES)>(qd, qbase, voff, 0u);
+        };
+        one(std::integral_constant<int, 0>{});
+        one(std::integral_constant<int, 1>{});
+        one(std::integral_constant<int, 2>{});
+        one(std::integral_constant<int, 3>{});
+        one(std::integral_constant<int, 4>{});
+        one(std::integral_constant<int, 5>{});
+        one(std::integral_constant<int, 6>{});
+        one(std::integral_constant<int, 7>{});
+    };
+    auto read_q = [&]() {
+        const char* qs = lds + q_lds;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qf[ks] = *(const bf16x8*)(qs + l32 * ROW_BYTES + (((2 * ks + hh) ^ (l32 & 15)) << 4));
+    };
     // A negative scale is applied as |scale| on -Q (a sign flip is exact in
     // bf16) and a zero scale as zero scores, so the exp2 argument below always
     // multiplies by a positive constant and masked -inf scores stay -inf.
-    if (p.q_mode != 0) {
-        const u32x4 flip = p.q_mode == 1 ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
-                                         : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 keep = p.q_mode == 1 ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
+    auto q_sign = [&]() {
+        if (p.q_mode != 0) {
+            const u32x4 flip = p.q_mode == 1 ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
+                                             : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 keep = p.q_mode == 1 ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, qf[ks]) & keep) ^ flip);
+            for (int ks = 0; ks < 8; ++ks)
+                qf[ks] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, qf[ks]) & keep) ^ flip);
+        }
+    };
+    if constexpr (Q_STAGED) {
+        stage_q();
+    } else {
+        if constexpr (!SPARSE) load_q();
+        q_sign();
     }
     const float c = p.c;
 
@@ -689,10 +735,15 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     // vmcnt(0) through the builtin, so the compiler also knows the Q loads are
     // complete and never waits on vmcnt (which counts the DMA) inside the loop
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (Q_STAGED) {
+        read_q();
+        q_sign();
+    }
     // fast kernel: the waves' answers meet in V slot 3 (not refilled before
-    // tile 1); a workgroup with a non-finite V value in a masked block marks its
-    // first output row and leaves the rows to the exact kernel
-    uint32_t* const nf_wave = (uint32_t*)(lds + V_RING + 3 * BLK_BYTES);
+    // tile 1), or past the rings where staged Q uses that slot; a workgroup
+    // with a non-finite V value in a masked block marks its first output row
+    // and leaves the rows to the exact kernel
+    uint32_t* const nf_wave = (uint32_t*)(lds + NF_OFF);
     if constexpr (!SAFE) {
         const bool nf = __builtin_amdgcn_ballot_w64((nf_bits & 0x80008000u) != 0u) != 0;
         if (lane == 0) nf_wave[wave] = nf ? 1u : 0u;
