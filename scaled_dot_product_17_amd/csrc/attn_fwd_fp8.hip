@@ -629,17 +629,44 @@ __device__ __forceinline__ void fwd8_tile(const Params& p, const int bid) {
     // all -inf (or NaN) gets NaN, as the formula gives
     const float l_tot = wave_swap_sum(l);
     const float inv = p.dv / ol[0];
-    if (myq < N) {
-        uint16_t* orow = p.o + q_panel + (size_t)myq * HD;
+    // Fast kernel: O leaves through LDS as whole rows, as in the bf16 kernel:
+    // staged row-major in the wave's 8 KiB of the K/V rings (bf16 rows of 256
+    // bytes, 16-byte chunk c of row r at chunk c ^ (r mod 16)) once every
+    // wave's copies have landed and no wave reads the rings, then stored 4
+    // rows (1 KiB) per instruction.  The exact kernel, short of registers,
+    // stores its rows directly.
+    auto o_piece = [&](int db, int r4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[db][4 * r4 + i] * inv);
+        return ov;
+    };
+    if constexpr (!SAFE) {
+        wait_dma();
+        __syncthreads();
+        constexpr int OROW = HD * 2;   // bytes per bf16 O row
+        char* const stage = lds + K_RING + wave * (32 * OROW);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x4 ov;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[db][4 * r4 + i] * inv);
-                *(bf16x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = ov;
+                const int ch = 4 * db + r4;   // head dims 8*ch .. 8*ch+7; this lane's half at 4*hh
+                *(bf16x4*)(stage + l32 * OROW + ((ch ^ (l32 & 15)) << 4) + 8 * hh) = o_piece(db, r4);
             }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int r = 4 * t + (lane >> 4), ch = lane & 15;
+            const u32x4 x = *(const u32x4*)(stage + r * OROW + ((ch ^ (r & 15)) << 4));
+            if (wq0 + r < N) *(u32x4*)(p.o + q_panel + (size_t)(wq0 + r) * HD + 8 * ch) = x;
+        }
+    } else if (myq < N) {
+        uint16_t* orow = p.o + q_panel + (size_t)myq * HD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) *(bf16x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = o_piece(db, r4);
+    }
+    if (myq < N) {
         if (p.lse != nullptr && hh == 0) {
             const size_t li = ((size_t)b * p.Hq + h) * (size_t)N + myq;
             p.lse[li] = m == -INFINITY ? __builtin_nanf("") : m * p.lse_scale + logf(l_tot);
