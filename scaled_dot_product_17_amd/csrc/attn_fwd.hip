@@ -504,11 +504,23 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
     } else if constexpr (CAUSAL && !SPARSE) {
         g_hi = min(g_hi, wq0 / KB);
     }
+    // SPARSE with one query block per workgroup (the 4-wave kernels): every
+    // union entry is listed by that block, and only the last entry can hold a
+    // masked key (the diagonal block when causal, since a causal list holds no
+    // block past it; the panel's ragged last block), so the steps before it
+    // read no list entry from LDS to decide
+    constexpr bool SP_ONE = SPARSE && QB_WG == 1;
+    const int g_tail = SPARSE ? n_blk_wg - 4 : 0;   // first stream block of the last union entry
+    auto member = [&](int g) {
+        if constexpr (SP_ONE) return true;
+        else return sp_member(g);
+    };
     // key >= N (ragged tail) or key > query (causal) -> -inf
     auto needs_mask = [&](int g) {
         if constexpr (SPARSE) {
+            if (SP_ONE && g < g_tail) return false;
             const int kb = sp_key(g);
-            return !sp_member(g) || (CAUSAL && kb + KB - 1 > wq0) || (kb + KB > N);
+            return !member(g) || (CAUSAL && kb + KB - 1 > wq0) || (kb + KB > N);
         }
         if constexpr (VARLEN) return g < g_lo || g >= g_hi;
         return g >= g_hi;
@@ -635,9 +647,9 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
         const bool valid = g < n_blk;
         // SPARSE: a wave skips the work of blocks its own query block does not
         // list (wave-uniform): the scores of g+1, the softmax of g, the PV of g-1
-        const bool use_n = !SPARSE || (g + 1 < n_blk_wg && sp_member(g + 1));
-        const bool use_g = !SPARSE || (valid && sp_member(g));
-        const bool use_p = !SPARSE || (g >= 1 && sp_member(g - 1));
+        const bool use_n = !SPARSE || (g + 1 < n_blk_wg && member(g + 1));
+        const bool use_g = !SPARSE || (valid && member(g));
+        const bool use_p = !SPARSE || (g >= 1 && member(g - 1));
         const bool mask_g = needs_mask(g);
         if (!FIRST && use_g && mask_g) apply_mask(s, g);
         if constexpr (SAFE) {
