@@ -361,14 +361,17 @@ __device__ __forceinline__ void fwd_tile(const Params& p, const int bid) {
         v_dma[i] = (uint32_t)(row * ROW_BYTES + ((pc ^ ((row & 3) << 2)) << 4));
     }
     // first key of stream block g, and whether this wave's query block lists it (SPARSE)
-    auto sp_key = [&](int g) {
-        const int ent = __builtin_amdgcn_readfirstlane((int)sp[g >> 2]);
-        return (ent & 0x3FFF) * SP_BLOCK + (g & 3) * KB;
+    // SPARSE: the union list's first 64 entries are also held in one VGPR
+    // (entry i in lane i) and read back with readlane, off the LDS latency;
+    // later entries come from LDS
+    int sp_reg = 0;
+    if constexpr (SPARSE) sp_reg = lane < n_blk_wg / 4 ? (int)sp[lane] : 0;
+    auto sp_ent = [&](int g) {
+        const int e = g >> 2;
+        return e < 64 ? __builtin_amdgcn_readlane(sp_reg, e) : __builtin_amdgcn_readfirstlane((int)sp[e]);
     };
-    auto sp_member = [&](int g) {
-        const int ent = __builtin_amdgcn_readfirstlane((int)sp[g >> 2]);
-        return ((ent >> (14 + (wave >> 2))) & 1) != 0;
-    };
+    auto sp_key = [&](int g) { return (sp_ent(g) & 0x3FFF) * SP_BLOCK + (g & 3) * KB; };
+    auto sp_member = [&](int g) { return ((sp_ent(g) >> (14 + (wave >> 2))) & 1) != 0; };
     // One descriptor per panel serves every copy, with the block's offset in
     // soffset.  Its range ends at the last key any block of this workgroup
     // needs (the sequence's or the panel's end, or the end of the workgroup's
