@@ -50,12 +50,14 @@ namespace {
 using namespace cdna4;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
-// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for short dense
-// sequences and packed batches, where twice as many workgroups balance the
-// grid better and the two workgroups sharing a CU are not tied by one barrier).
+// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for dense grids
+// too small to fill the chip with 8-wave workgroups, short sequences and packed
+// batches, where twice as many workgroups balance the grid better and the two
+// workgroups sharing a CU are not tied by one barrier).
 constexpr int BR = 256;                    // query rows per 8-wave workgroup
 constexpr int NWAVE = 8;
-constexpr int SHORT_N = 4096;              // dense sequences up to this length use 4 waves
+constexpr int N_CU = 256;                  // compute units of the chip (8 XCDs x 32)
+constexpr int MIN_N_8W = 1024;             // shorter dense sequences use 4 waves
 constexpr int ROW_BYTES = HD * 2;          // 256 B per K/V/Q/O row
 constexpr int KB = 32;                     // keys per pipeline step (one MFMA M block)
 constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB per K or V block
@@ -988,9 +990,13 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     // one head panel is addressed with 32-bit byte offsets
     if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    // measured: 4 waves win up to 4096 tokens, and causal up to 8192 (a causal
-    // tile sees half the keys on average)
-    const bool short_n = N <= SHORT_N || (causal && N <= 2 * SHORT_N);
+    // measured (same-process sweeps, 256-20480 tokens, 1-128 heads): 8-wave
+    // workgroups win once their grid fills the chip, a causal tile counting as
+    // half a tile (it sees half the keys on average), for sequences of at
+    // least 1024 tokens; 4-wave workgroups (two per CU) win on smaller grids
+    // and shorter sequences
+    const int64_t tiles8 = (int64_t)B * H_q * (((int64_t)N + BR - 1) / BR);
+    const bool short_n = N < MIN_N_8W || tiles8 < (causal ? 2 : 1) * (int64_t)N_CU;
     const int br = short_n ? BR / 2 : BR;
     const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
     const int64_t total = (int64_t)B * H_q * n_qtiles;

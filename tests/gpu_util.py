@@ -34,9 +34,9 @@ def poison_lds():
     cleared between launches, so the workgroups of the next launch inherit it."""
     import torch
     import scaled_dot_product_17_amd as sdpa
-    for n in (8192, 4096):
-        q = torch.randn(1, 16, n, 128, device="cuda").to(torch.bfloat16)
-        kv = torch.full((1, 16, n, 128), float("nan"), device="cuda", dtype=torch.bfloat16)
+    for b, n in ((1, 8192), (8, 512)):
+        q = torch.randn(b, 16, n, 128, device="cuda").to(torch.bfloat16)
+        kv = torch.full((b, 16, n, 128), float("nan"), device="cuda", dtype=torch.bfloat16)
         sdpa.fwd(q, kv, kv)
     n = 4096
     q = torch.randn(1, 16, n, 128, device="cuda").to(torch.bfloat16)

@@ -1,14 +1,14 @@
 // Host check of the dealt grid order (dealt_tile, causal_deal, make_deal in
-// cdna4.h): for the launch shapes of the dense bf16 and FP8 causal forwards,
+// cdna4.h): for the launch shapes of the dense causal forwards,
 // the causal backward's dQ and dK/dV grids and varlen batches (unequal
 // lengths, and causal ones of nearly equal lengths), every workgroup id of the grid
 // maps to padding or to one (head, query tile) in range, and every (head,
 // query tile) is reached exactly once, and the XCDs receive equal causal
-// work up to a few of a group's lightest tiles.  The tile-row and slot rules below are
-// the launches' own: 256-row tiles and 32 slots per XCD, or 128-row tiles and
-// 64 slots for short sequences (bf16 causal up to 8192 tokens, FP8 up to
-// 4096, varlen always).  Prints "ok ..." and exits 0, or names the first
-// failing shape and exits 1.
+// work up to a few of a group's lightest tiles.  The launches use two tile
+// forms: 256-row tiles and 32 slots per XCD (8-wave workgroups), or 128-row
+// tiles and 64 slots (4-wave workgroups: bf16 grids too small for the 8-wave
+// form, FP8 and varlen always); every dense shape is checked in both forms.
+// Prints "ok ..." and exits 0, or names the first failing shape and exits 1.
 #include "cdna4.h"
 
 #include <cstdio>
@@ -63,9 +63,8 @@ static bool covers(int64_t per, int64_t G, int64_t n, const Deal& d, int64_t gri
     return true;
 }
 
-static bool dense_causal(int B, int H, int N, bool fp8) {
-    const bool short_n = fp8 ? N <= 4096 : N <= 8192;
-    const int64_t br = short_n ? 128 : 256, slots = short_n ? 64 : 32;
+static bool dense_causal(int B, int H, int N, bool four_wave) {
+    const int64_t br = four_wave ? 128 : 256, slots = four_wave ? 64 : 32;
     const int64_t n = (N + br - 1) / br, per = (int64_t)B * H;
     int64_t G = std::min<int64_t>(per, (slots + n - 1) / n);
     Deal d{};
@@ -73,12 +72,12 @@ static bool dense_causal(int B, int H, int N, bool fp8) {
     ++n_shapes;
     if (!causal_deal(per, G, n, slots, d, grid) || grid > INT32_MAX) return true;   // plain order
     ++n_dealt;
-    return covers(per, G, n, d, grid, fp8 ? "fp8 B H N" : "bf16 B H N", B, H, N);
+    return covers(per, G, n, d, grid, four_wave ? "128-row tiles B H N" : "256-row tiles B H N", B, H, N);
 }
 
 // The backward's dK/dV grid: 128-key tiles, one workgroup per CU (32 slots
-// per XCD), units of (batch, K/V head, part).  (Its dQ grid follows the bf16
-// forward's rule above.)
+// per XCD), units of (batch, K/V head, part).  (Its dQ grid takes one of
+// the two dense forms above.)
 static bool dkdv_causal(int units, int N) {
     const int64_t n = (N + 127) / 128, slots = 32;
     int64_t G = std::min<int64_t>(units, (slots + n - 1) / n);

@@ -105,18 +105,30 @@ def test_nonfinite_dense(shape, causal):
     assert n > 0
 
 
-def test_nonfinite_causal_8wave():
-    """A causal length that takes the 8-wave kernel (N > 8192)."""
+@pytest.mark.parametrize("causal,shape", [(False, (1, 16, 2, 4200)), (True, (1, 16, 2, 8300))],
+                         ids=["noncausal_b1_hq16_hkv2_n4200", "causal_b1_hq16_hkv2_n8300"])
+def test_nonfinite_8wave(causal, shape):
+    """Grids large enough for the 8-wave kernel (256 or more 256-row tiles,
+    512 or more causal): the planted heads' rows near the planted positions,
+    block edges and the tail, against the oracle row by row."""
     import torch
     import scaled_dot_product_17_amd as sdpa
-    B, Hq, Hkv, N = 1, 2, 1, 8300
-    say(f"[nonfinite dense] causal N={N}")
-    q, k, v = dense_case(B, Hq, Hkv, N, seed=21900)
-    v[0, 0, 8192 + 40, 100] = PINF
-    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=True, scale=SCALE)
+    B, Hq, Hkv, N = shape
+    say(f"[nonfinite dense] {shape} causal={causal}")
+    q, k, v = dense_case(B, Hq, Hkv, N, seed=21900 + N)
+    v[0, 0, 8192 % N + 40, 100] = PINF
+    o, lse = sdpa.fwd(to_gpu(q), to_gpu(k), to_gpu(v), causal=causal, scale=SCALE)
     torch.cuda.synchronize()
-    o_ref, lse_ref = oracle.attn_ref(q, k, v, True, SCALE)
-    check_nonfinite(bf16_to_np(o), lse.cpu().numpy(), o_ref, lse_ref, f"causal N={N}")
+    near = np.r_[0:48, 48:53, 68:73, 110:118, 148:153, 254:258, 1000:1003, 4160:4200,
+                 8230:8236, N - 33:N]
+    near = np.unique(near[near < N])
+    heads = [0, 1, Hq // Hkv, Hq - 1]
+    rows = np.concatenate([h * N + near for h in heads]).astype(np.int64)
+    o_ref, lse_ref = oracle.attn_ref(q, k, v, causal, SCALE, rows=rows)
+    og = bf16_to_np(o).reshape(-1, 128)[rows]
+    lg = lse.cpu().numpy().reshape(-1)[rows]
+    n = check_nonfinite(og, lg, o_ref, lse_ref, f"{shape} causal={causal}")
+    assert n > 0
 
 
 VARLEN = [([100, 130, 70], (-1, -1)), ([100, 130, 70], (16, 0)), ([33, 64, 300], (40, 40)),

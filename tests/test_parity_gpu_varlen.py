@@ -234,11 +234,12 @@ def test_nearly_equal_lengths_full():
 @pytest.mark.parametrize("causal,n", [(False, 8192), (True, 9000), (False, 5000)])
 def test_four_and_eight_wave_workgroups_agree(causal, n):
     """A single sequence through the packed entry point (4-wave workgroups) equals
-    the dense kernel at lengths where the dense path uses 8-wave workgroups,
-    bitwise: each row's arithmetic does not depend on the workgroup size."""
+    the dense kernel on grids where the dense path uses 8-wave workgroups (16
+    heads: 256 or more 256-row tiles, 512 or more causal), bitwise: each row's
+    arithmetic does not depend on the workgroup size."""
     import torch
     import scaled_dot_product_17_amd as sdpa
-    q, k, v, cu = packed(14800 + n, 4, 2, [n])
+    q, k, v, cu = packed(14800 + n, 16, 2, [n])
     o, lse = run_varlen(q, k, v, cu, causal, SCALE, (-1, -1))
     od, ld = sdpa.fwd(to_gpu(q)[None], to_gpu(k)[None], to_gpu(v)[None], causal=causal, scale=SCALE)
     torch.cuda.synchronize()
