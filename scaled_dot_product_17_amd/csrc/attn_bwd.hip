@@ -62,7 +62,7 @@ using TileReads = tile::Reads;
 constexpr float LOG2E = 1.4426950408889634f;
 
 // attn_bwd_dq: 8 waves, rings of 4 K blocks and 4 V blocks
-constexpr int DQ_WAVES = 8;                // 8-wave dQ workgroups (4 for short sequences)
+constexpr int DQ_WAVES = 8;                // 8-wave dQ workgroups (4 for short sequences and small grids)
 constexpr int DQ_K_RING = 0;
 constexpr int DQ_V_RING = 4 * BLK_BYTES;
 constexpr int DQ_LDS = 8 * BLK_BYTES;      // 64 KiB
@@ -653,11 +653,14 @@ attn_status prepare(const Buf* ins, int n_in, const Buf* outs, int n_out, int B,
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     // one head panel is addressed with 32-bit byte offsets
     if ((int64_t)N * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    // 4-wave dQ workgroups (128 rows, two per CU) for short sequences, as in
-    // the forward: twice the workgroups balance the grid better.  Measured
-    // (whole backward): causal N = 2048 +4%, 4096 +1%, 8192 +1.4%;
-    // non-causal N = 2048 +0-1.5%, 4096 -1.5%.
-    const bool dq_short = causal ? N <= 8192 : N <= 2048;
+    // 4-wave dQ workgroups (128 rows, two per CU) for short sequences and for
+    // grids of 256-row tiles that do not fill the chip (a causal tile counting
+    // as half), as in the forward: twice the workgroups balance the grid
+    // better.  Measured (whole backward): causal N = 2048 +4%, 4096 +1%,
+    // 8192 +1.4%; non-causal N = 2048 +0-1.5%, 4096 -1.5%; one head N = 32768
+    // +8.6%, causal two heads N = 32768 +4.5%.
+    const int64_t dq_tiles8 = (int64_t)B * H_q * (((int64_t)N + 255) / 256);
+    const bool dq_short = (causal ? N <= 8192 : N <= 2048) || dq_tiles8 < (causal ? 512 : 256);
     const int dq_rows = (dq_short ? 4 : DQ_WAVES) * 32;
     const int64_t n_qtiles = ((int64_t)N + dq_rows - 1) / dq_rows;
     const int64_t n_ktiles = ((int64_t)N + KV_KEYS - 1) / KV_KEYS;
