@@ -50,14 +50,14 @@ namespace {
 using namespace cdna4;
 
 constexpr int HD = 128;                    // head dimension handled by this kernel
-// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for dense grids
-// too small to fill the chip with 8-wave workgroups, short sequences and packed
-// batches, where twice as many workgroups balance the grid better and the two
+// A workgroup is NW waves = 32*NW query rows (NW = 8, or 4 for grids too small
+// to fill the chip with 8-wave workgroups, short sequences and narrow windows,
+// where twice as many workgroups balance the grid better and the two
 // workgroups sharing a CU are not tied by one barrier).
 constexpr int BR = 256;                    // query rows per 8-wave workgroup
 constexpr int NWAVE = 8;
 constexpr int N_CU = 256;                  // compute units of the chip (8 XCDs x 32)
-constexpr int MIN_N_8W = 1024;             // shorter dense sequences use 4 waves
+constexpr int MIN_N_8W = 1024;             // shorter sequences use 4 waves
 constexpr int ROW_BYTES = HD * 2;          // 256 B per K/V/Q/O row
 constexpr int KB = 32;                     // keys per pipeline step (one MFMA M block)
 constexpr int BLK_BYTES = KB * ROW_BYTES;  // 8 KiB per K or V block
@@ -1057,9 +1057,22 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     if (D != HD) return ATTN_ERR_HEAD_DIM;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if ((int64_t)total * ROW_BYTES >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-    // 4-wave workgroups: a packed or windowed tile sees few keys, and twice the
-    // workgroups balance better (as for short dense sequences)
-    const int br = BR / 2;
+    // 8-wave workgroups (256-row tiles) by the dense rule: when the mean
+    // sequence holds at least MIN_N_8W tokens and the batch's 256-row tiles
+    // fill the chip (a causal tile counting as half), unless a window
+    // narrower than 8192 keys bounds the rows (a windowed tile's masked edge
+    // blocks grow with its rows).  4-wave ones otherwise: twice the
+    // workgroups balance short and windowed tiles better.  Measured (same
+    // process, bitwise equal): causal mix of 8 sequences +3.1%, 8 equal causal
+    // sequences +2.9%, 4096-key causal window +0.1%, 2049-key window -9%.
+    const bool windowed = window_left >= 0 || (!causal && window_right >= 0);
+    const int64_t width = (window_left < 0 ? (int64_t)max_seqlen : window_left) +
+                          (causal ? 0 : (window_right < 0 ? (int64_t)max_seqlen : window_right)) + 1;
+    const int64_t tiles8 = (int64_t)H_q * (((int64_t)total + BR - 1) / BR);
+    const bool eight = !(windowed && width < 8192) && (int64_t)total >= (int64_t)MIN_N_8W * n_seq &&
+                       tiles8 >= (causal ? 2 : 1) * (int64_t)N_CU;
+    const int br = eight ? BR : BR / 2;
+    const int64_t slots = eight ? 32 : 64;   // an XCD's workgroup slots: 32 CUs x 1 or 2
     const int64_t n_qtiles = ((int64_t)max_seqlen + br - 1) / br;
     // Sequences of nearly equal length (the longest within 1.25x the mean)
     // take the dense order: a few heads at a time, whose K/V stays in one
@@ -1072,7 +1085,7 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     // a long sequence's every tile).
     const bool unequal = n_seq > 1 && (int64_t)max_seqlen * n_seq * 4 > (int64_t)total * 5;
     const int64_t pairs = (int64_t)n_seq * H_q;
-    const int64_t cgroup = std::min<int64_t>(pairs, (64 + n_qtiles - 1) / n_qtiles);
+    const int64_t cgroup = std::min<int64_t>(pairs, (slots + n_qtiles - 1) / n_qtiles);
     const int64_t n_groups = (pairs + cgroup - 1) / cgroup;
     int64_t grid = pairs * n_qtiles;
     Deal deal{};
@@ -1082,10 +1095,9 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
         deal = n_groups < 32 ? make_deal(pairs, cgroup, n_qtiles, 8, true, grid)
                              : make_deal(pairs, cgroup, n_qtiles, 1, false, grid);
     } else if (causal) {
-        // nearly equal lengths, causal: the dense causal rule (64 slots of
-        // 4-wave workgroups per XCD)
+        // nearly equal lengths, causal: the dense causal rule
         int64_t g = 0;
-        if (causal_deal(pairs, dg, n_qtiles, 64, deal, g) && g <= INT32_MAX) {
+        if (causal_deal(pairs, dg, n_qtiles, slots, deal, g) && g <= INT32_MAX) {
             dealt = true;
             grid = g;
         }
@@ -1128,7 +1140,8 @@ extern "C" attn_status attn_fwd_varlen(const void* q, const void* k, const void*
     p.left = window_left < 0 ? -1 : window_left;
     p.right = window_right < 0 ? -1 : window_right;
     set_scale(p, scale);
-    return launch_fwd<true, false, NWAVE / 2>(p, causal != 0, stream);
+    return eight ? launch_fwd<true, false, NWAVE>(p, causal != 0, stream)
+                 : launch_fwd<true, false, NWAVE / 2>(p, causal != 0, stream);
 }
 
 extern "C" attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,

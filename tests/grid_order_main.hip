@@ -7,7 +7,8 @@
 // work up to a few of a group's lightest tiles.  The launches use two tile
 // forms: 256-row tiles and 32 slots per XCD (8-wave workgroups), or 128-row
 // tiles and 64 slots (4-wave workgroups: bf16 grids too small for the 8-wave
-// form, FP8 and varlen always); every dense shape is checked in both forms.
+// form, short sequences, narrow windows, and FP8 always); every shape is
+// checked in both forms.
 // Prints "ok ..." and exits 0, or names the first failing shape and exits 1.
 #include "cdna4.h"
 
@@ -89,28 +90,31 @@ static bool dkdv_causal(int units, int N) {
     return covers(units, G, n, d, grid, "dkdv units N", units, N, 0);
 }
 
-// Causal varlen batches of nearly equal lengths: the dense causal rule with
-// 128-row tiles and 64 slots at every length.
-static bool varlen_equal_causal(int pairs, int max_seqlen) {
-    const int64_t n = (max_seqlen + 127) / 128;
-    int64_t G = std::min<int64_t>(pairs, (64 + n - 1) / n);
+// Causal varlen batches of nearly equal lengths: the dense causal rule, in
+// either tile form.
+static bool varlen_equal_causal(int pairs, int max_seqlen, bool four_wave) {
+    const int64_t br = four_wave ? 128 : 256, slots = four_wave ? 64 : 32;
+    const int64_t n = (max_seqlen + br - 1) / br;
+    int64_t G = std::min<int64_t>(pairs, (slots + n - 1) / n);
     Deal d{};
     int64_t grid = 0;
     ++n_shapes;
-    if (!causal_deal(pairs, G, n, 64, d, grid) || grid > INT32_MAX) return true;
+    if (!causal_deal(pairs, G, n, slots, d, grid) || grid > INT32_MAX) return true;
     ++n_dealt;
-    return covers(pairs, G, n, d, grid, "varlen equal pairs max_seqlen", pairs, max_seqlen, 0);
+    return covers(pairs, G, n, d, grid, "varlen equal pairs max_seqlen", pairs, max_seqlen, four_wave);
 }
 
-static bool varlen(int n_seq, int H, int max_seqlen) {
-    const int64_t n = (max_seqlen + 127) / 128, pairs = (int64_t)n_seq * H;
-    const int64_t G = std::min<int64_t>(pairs, (64 + n - 1) / n);
+static bool varlen(int n_seq, int H, int max_seqlen, bool four_wave) {
+    const int64_t br = four_wave ? 128 : 256, slots = four_wave ? 64 : 32;
+    const int64_t n = (max_seqlen + br - 1) / br, pairs = (int64_t)n_seq * H;
+    const int64_t G = std::min<int64_t>(pairs, (slots + n - 1) / n);
     const int64_t ng = (pairs + G - 1) / G;
     int64_t grid = 0;
     const Deal d = ng < 32 ? make_deal(pairs, G, n, 8, true, grid) : make_deal(pairs, G, n, 1, false, grid);
     ++n_shapes;
     ++n_dealt;
-    return covers(pairs, G, n, d, grid, "varlen n_seq H max_seqlen", n_seq, H, max_seqlen);
+    return covers(pairs, G, n, d, grid, four_wave ? "varlen 128-row n_seq H max_seqlen" : "varlen 256-row n_seq H max_seqlen",
+                  n_seq, H, max_seqlen);
 }
 
 int main() {
@@ -133,12 +137,16 @@ int main() {
     for (int s = 2; s <= 40; ++s)
         for (int H = 1; H <= 16; ++H)
             for (int L : Ls)
-                if (!varlen(s, H, L)) return 1;
-    if (!varlen(2, 1, (1 << 23) - 1001) || !varlen(2, 2, (1 << 23) - 1001)) return 1;
+                for (int f = 0; f < 2; ++f)
+                    if (!varlen(s, H, L, f)) return 1;
+    for (int f = 0; f < 2; ++f)
+        if (!varlen(2, 1, (1 << 23) - 1001, f) || !varlen(2, 2, (1 << 23) - 1001, f)) return 1;
     for (int pr = 1; pr <= 72; ++pr)
         for (int L : Ls)
-            if (!varlen_equal_causal(pr, L)) return 1;
-    if (!varlen_equal_causal(1, (1 << 23) - 1)) return 1;
+            for (int f = 0; f < 2; ++f)
+                if (!varlen_equal_causal(pr, L, f)) return 1;
+    for (int f = 0; f < 2; ++f)
+        if (!varlen_equal_causal(1, (1 << 23) - 1, f)) return 1;
     printf("ok: %ld launch shapes, %ld with a dealt grid, largest XCD work gap %ld blocks\n", n_shapes, n_dealt,
            (long)worst_gap);
     return 0;

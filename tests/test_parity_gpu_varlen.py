@@ -231,16 +231,20 @@ def test_nearly_equal_lengths_full():
         parity.check(m, f"nearly equal lengths causal={causal}")
 
 
-@pytest.mark.parametrize("causal,n", [(False, 8192), (True, 9000), (False, 5000)])
-def test_four_and_eight_wave_workgroups_agree(causal, n):
-    """A single sequence through the packed entry point (4-wave workgroups) equals
-    the dense kernel on grids where the dense path uses 8-wave workgroups (16
-    heads: 256 or more 256-row tiles, 512 or more causal), bitwise: each row's
-    arithmetic does not depend on the workgroup size."""
+@pytest.mark.parametrize("causal,n,heads,window", [(False, 8192, 16, (-1, -1)), (True, 9000, 16, (-1, -1)),
+                                                   (False, 5000, 16, (-1, -1)), (False, 4000, 16, (3999, 3999)),
+                                                   (True, 4000, 32, (3999, -1))])
+def test_four_and_eight_wave_workgroups_agree(causal, n, heads, window):
+    """A single sequence through the packed entry point equals the dense kernel
+    on grids where the dense path uses 8-wave workgroups (256 or more 256-row
+    tiles, 512 or more causal), bitwise: each row's arithmetic does not depend
+    on the workgroup size.  Without a window the packed launch takes 8-wave
+    workgroups as well; with a window wide enough to change no row (N - 1
+    keys) but narrower than 8192 keys it takes 4-wave ones."""
     import torch
     import scaled_dot_product_17_amd as sdpa
-    q, k, v, cu = packed(14800 + n, 16, 2, [n])
-    o, lse = run_varlen(q, k, v, cu, causal, SCALE, (-1, -1))
+    q, k, v, cu = packed(14800 + n + heads, heads, 2, [n])
+    o, lse = run_varlen(q, k, v, cu, causal, SCALE, window)
     od, ld = sdpa.fwd(to_gpu(q)[None], to_gpu(k)[None], to_gpu(v)[None], causal=causal, scale=SCALE)
     torch.cuda.synchronize()
     assert np.array_equal(o, bf16_to_np(od)[0]) and np.array_equal(lse, ld.cpu().numpy()[0])
