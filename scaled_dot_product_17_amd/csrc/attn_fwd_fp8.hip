@@ -16,7 +16,8 @@
 // neutral exponent (2^0), i.e. a plain e4m3 x e4m3 product with fp32
 // accumulation, 64 contraction values per lane pair.
 //
-// Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
+// Work decomposition (one workgroup = NW waves = 32 NW query rows of one head;
+// launched with 4 waves, two workgroups per CU):
 //   * each wave owns 32 query rows; its Q rows (128 bytes each) stay in VGPRs as
 //     the B operand of S^T = K Q^T;
 //   * key blocks of 64 rows of K and V (8 KiB each) are copied HBM -> LDS by the
